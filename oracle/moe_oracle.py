@@ -1,0 +1,253 @@
+"""fp64 CPU oracle of the gpt-oss MoE feed-forward layer with MXFP4 experts.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+``cpu_baseline`` leg of the benchmark may import this module.  The GPU
+library never calls it, and it shares no code, table or helper with the GPU
+path: it has its own MXFP4 decoder, its own bf16 rounding and its own
+routing.  Everything is computed in float64, step by step, in the order the
+pages describe the layer:
+
+  1. router: a small network scores every expert for every token
+     [gpt-oss architecture walk-through (ewbang.com), section "Mixture of
+     Experts": the router picks several experts and weights them];
+  2. top-k: gpt-oss keeps the 4 best experts of 32 (20b) or 128 (120b)
+     [same section; GPT-OSS 20B model card (llm-atlas), "feed-forward / MoE"];
+  3. gates: softmax over the selected logits, so the weights sum to 1 as in
+     the page's example A = 0.7 * NN2 + 0.3 * NN4 [same MoE section];
+  4. experts: a SwiGLU feed-forward block (three linear maps, Swish = x *
+     sigmoid(x) on the gate) [From GPT-2 to gpt-oss (qypowez.cn), section 3
+     "Swish/SwiGLU", Fig. 6-7], width 2880 [model card config table], clamp
+     limit swiglu_limit = 7 [model card raw config];
+  5. expert weights in MXFP4: 4-bit values, one 8-bit scale per 32 values,
+     4.25 bits per parameter [ewbang.com walk-through, "Quantization"];
+     element and scale formats E2M1 / E8M0 per the OCP Microscaling v1.0
+     specification;
+  6. combine: the weighted sum of the selected experts' outputs.
+
+Readings where the pages are silent (each one is listed in the design notes):
+router = linear map with bias; softmax over the k selected logits; exact
+ties go to the lower expert id; the k slots of a token are stored in
+ascending expert id; the permutation is stable by token within an expert;
+the clamp applies to both gate and up pre-activations before silu(g) * u;
+h is rounded to bf16 (round to nearest even) before the down projection.
+
+Parity status: every function here is pinned by the CPU tests
+(exhaustive decode table, closed forms, the 0.7/0.3 example, brute force
+on tiny inputs, permutation invariants).  The layer output values
+themselves are not printed by the pages; they are pinned only through the
+dense brute-force evaluation.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# E2M1 magnitudes for codes 0..7 (OCP MX v1.0, FP4 E2M1): bit 3 is the sign.
+E2M1_MAGNITUDE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+NEAR_TIE = 1e-6      # logit gap below which a token's selection is flagged
+
+
+# ----------------------------------------------------------------------------
+# Formats
+# ----------------------------------------------------------------------------
+def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Decode MXFP4 rows: codes uint8 [R][K/2], scales uint8 [R][K/32] -> f64 [R][K].
+
+    value = E2M1(code) * 2^(s - 127); the low nibble holds the even K index;
+    scale byte 255 is NaN (OCP MX v1.0 E8M0).  Exact in float64.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    R, half = codes.shape
+    K = half * 2
+    c = np.empty((R, K), dtype=np.uint8)
+    c[:, 0::2] = codes & 0x0F
+    c[:, 1::2] = codes >> 4
+    mag = E2M1_MAGNITUDE[c & 7]
+    val = np.where(c & 8, -mag, mag)
+    s = scales.astype(np.int64)
+    blk = np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+    return val * np.repeat(blk, 32, axis=1)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (8 significant bits), ties to even.
+
+    Works on the float64 value directly (no intermediate fp32 rounding).
+    Normal bf16 range only, which is all the layer produces (|h| <= 49).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                     # v = m * 2^e, |m| in [0.5, 1)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+# ----------------------------------------------------------------------------
+# Router, top-k and gates
+# ----------------------------------------------------------------------------
+def router_logits(x: np.ndarray, w_router: np.ndarray, b_router: np.ndarray) -> np.ndarray:
+    """l[t, e] = sum_d x[t, d] * Wr[e, d] + br[e], float64 (bf16 x fp32 products are exact)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x @ np.asarray(w_router, dtype=np.float64).T + np.asarray(b_router, dtype=np.float64)
+
+
+def select_experts(logits: np.ndarray, k: int):
+    """Top-k experts per token.
+
+    Experts are ranked by (logit descending, id ascending) and the first k
+    kept; the k ids are returned in ascending order.  A token is flagged as a
+    near tie when the k-th and (k+1)-th largest logits differ by less than
+    1e-6.  Returns (idx int32 [T][k], flagged bool [T], gap float64 [T]).
+    """
+    T, E = logits.shape
+    order = np.argsort(-logits, axis=1, kind="stable")      # stable: ties keep ascending id
+    idx = np.sort(order[:, :k], axis=1).astype(np.int32)
+    srt = np.take_along_axis(logits, order, axis=1)
+    gap = srt[:, k - 1] - srt[:, k] if k < E else np.full(T, np.inf)
+    return idx, gap < NEAR_TIE, gap
+
+
+def gate_weights(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Softmax over the selected logits of each token (slot order = idx order)."""
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------
+# Grouping of assignments by expert
+# ----------------------------------------------------------------------------
+def build_permutation(idx: np.ndarray, E: int):
+    """Group the T*k assignments a = t*k + j by expert, stable by token.
+
+    counts[e] = number of tokens routed to e; offsets = exclusive prefix sum
+    (length E+1); perm[p] = assignment id at position p; inv[perm[p]] = p.
+    """
+    flat = idx.reshape(-1).astype(np.int64)
+    n = flat.size
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.lexsort((np.arange(n), flat)).astype(np.int32)   # key: expert, then assignment id
+    inv = np.empty(n, dtype=np.int32)
+    inv[perm] = np.arange(n, dtype=np.int32)
+    return counts, offsets, perm, inv
+
+
+# ----------------------------------------------------------------------------
+# SwiGLU expert
+# ----------------------------------------------------------------------------
+def silu(v: np.ndarray) -> np.ndarray:
+    """Swish / SiLU: v * sigmoid(v)."""
+    return v / (1.0 + np.exp(-v))
+
+
+def swiglu(g: np.ndarray, u: np.ndarray, limit: float) -> np.ndarray:
+    """silu(clamp(g)) * clamp(u), both clamped to [-limit, limit]; float64, unrounded."""
+    g = np.clip(g, -limit, limit)
+    u = np.clip(u, -limit, limit)
+    return silu(g) * u
+
+
+def expert_ffn(xr: np.ndarray, gu_codes, gu_scales, dn_codes, dn_scales, limit: float):
+    """One expert on rows xr [M][D]: returns (h [M][I] bf16-rounded f64, z [M][D] f64)."""
+    w_gu = mxfp4_decode(gu_codes, gu_scales)        # [2I][D]
+    I = w_gu.shape[0] // 2
+    g = xr @ w_gu[:I].T
+    u = xr @ w_gu[I:].T
+    del w_gu
+    h = round_to_bf16(swiglu(g, u, limit))
+    w_dn = mxfp4_decode(dn_codes, dn_scales)        # [D][I]
+    z = h @ w_dn.T
+    return h, z
+
+
+# ----------------------------------------------------------------------------
+# Whole layer
+# ----------------------------------------------------------------------------
+def combine(w: np.ndarray, z_perm: np.ndarray, inv: np.ndarray, tokens: np.ndarray, k: int) -> np.ndarray:
+    """y[t] = sum_j w[t, j] * z[inv[t*k + j]], summed in slot (ascending expert id) order."""
+    y = np.zeros((len(tokens), z_perm.shape[1]), dtype=np.float64)
+    for j in range(k):
+        y += w[tokens, j][:, None] * z_perm[inv[tokens * k + j]]
+    return y
+
+
+def forward(inp, tokens=None, override_idx: dict | None = None) -> dict:
+    """Evaluate the layer.
+
+    inp: object with T, D, E, k, I, swiglu_limit, x_bf16, w_router, b_router,
+    gu_codes, gu_scales, dn_codes, dn_scales (canonical MXFP4 layout).
+    tokens: optional array of token indices; routing and the permutation are
+    always computed for all tokens, the experts and the combine only for
+    these tokens (all tokens when None).
+    override_idx: {token: k expert ids} replacing the oracle's own selection
+    for those tokens (used for near-tie tokens only).
+
+    Returns a dict with logits, idx, flagged, gap, w, counts, offsets, perm,
+    inv, tokens, and for the evaluated tokens: h (by position p), z (by
+    position p) and y [len(tokens)][D], all float64.
+    """
+    T, E, k = inp.T, inp.E, inp.k
+    x = bf16_to_f64(inp.x_bf16)
+    logits = router_logits(x, inp.w_router, inp.b_router)
+    idx, flagged, gap = select_experts(logits, k)
+    if override_idx:
+        for t, ids in override_idx.items():
+            idx[t] = np.sort(np.asarray(ids, dtype=np.int32))
+    w = gate_weights(logits, idx)
+    counts, offsets, perm, inv = build_permutation(idx, E)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+
+    want = np.zeros(T, dtype=bool)
+    want[tokens] = True
+    h_all, z_all = {}, {}
+    for e in range(E):
+        seg = np.arange(offsets[e], offsets[e + 1])
+        seg = seg[want[perm[seg] // k]]
+        if seg.size == 0:
+            continue
+        rows = x[perm[seg] // k]
+        h, z = expert_ffn(rows, inp.gu_codes[e], inp.gu_scales[e], inp.dn_codes[e],
+                          inp.dn_scales[e], inp.swiglu_limit)
+        for i, p in enumerate(seg):
+            h_all[int(p)] = h[i]
+            z_all[int(p)] = z[i]
+    z_perm = np.zeros((T * k, inp.D), dtype=np.float64)
+    for p, zz in z_all.items():
+        z_perm[p] = zz
+    y = combine(w, z_perm, inv, tokens, k)
+    return dict(logits=logits, idx=idx, flagged=flagged, gap=gap, w=w, counts=counts,
+                offsets=offsets, perm=perm, inv=inv, tokens=tokens, h=h_all, z=z_all, y=y)
+
+
+# ----------------------------------------------------------------------------
+# Closed forms printed by the pages
+# ----------------------------------------------------------------------------
+def mxfp4_bits_per_param(n_params: int, code_bytes: int, scale_bytes: int) -> float:
+    """Storage bits per parameter of an MXFP4 tensor (4.25 on the pages)."""
+    return 8.0 * (code_bytes + scale_bytes) / n_params
+
+
+def gpt_oss_param_counts(n_layers: int, n_experts: int, top_k: int, d_model: int = 2880,
+                         d_ff: int = 2880, n_q_heads: int = 64, n_kv_heads: int = 8,
+                         head_dim: int = 64, vocab: int = 201088) -> dict:
+    """Weight-matrix parameter counts of a gpt-oss model (biases and norms omitted).
+
+    Per layer: experts 3 * d_model * d_ff each, router d_model * E, attention
+    q/o d_model x (64*64) and k/v d_model x (8*64); untied embedding and
+    unembedding vocab x d_model.  'active' counts the top_k experts, the
+    attention, the router and the unembedding (the embedding is a lookup).
+    """
+    expert = 3 * d_model * d_ff
+    attn = 2 * d_model * n_q_heads * head_dim + 2 * d_model * n_kv_heads * head_dim
+    router = d_model * n_experts
+    emb = vocab * d_model
+    total = n_layers * (n_experts * expert + attn + router) + 2 * emb
+    active = n_layers * (top_k * expert + attn + router) + emb
+    return dict(total=total, active=active, expert=expert, attention=attn, router=router,
+                embedding=emb, experts_all_layers=n_layers * n_experts * expert)
