@@ -1,0 +1,208 @@
+/*
+ * moe_mxfp4.h — C ABI of the gpt-oss MoE feed-forward layer with MXFP4 experts
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources: "gpt-oss architecture walk-through" (ewbang.com), sections
+ * "Mixture of Experts" and "Quantization"; "From GPT-2 to gpt-oss" (qypowez.cn),
+ * section 3 "Swish/SwiGLU" and section 4 "Mixture of Experts"; "GPT-OSS 20B"
+ * model card (llm-atlas), config tables):
+ *
+ *   logits[t,e] = x[t,:] . Wr[e,:] + br[e]                        (router)
+ *   S_t         = the top_k experts of token t                    (top-k)
+ *   w[t,j]      = softmax over the selected logits                (gates, sum to 1)
+ *   g, u        = x[t] W_gate[e]^T, x[t] W_up[e]^T                 (MXFP4 weights)
+ *   h           = bf16( silu(clamp(g)) * clamp(u) ), clamp to +-swiglu_limit
+ *   z           = h W_down[e]^T
+ *   y[t]        = sum_j w[t,j] * z_{t, S_t[j]}                     (combine)
+ *
+ * Expert weights are MXFP4: E2M1 4-bit values with one E8M0 scale byte per 32
+ * consecutive values along the reduction axis (4.25 bits per parameter).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All device pointers are caller-owned device memory; the library never
+ *    allocates, frees or keeps them.  Host pointers are named so.
+ *  - Every call validates its arguments on the host before any HIP call and
+ *    returns MOE_EINVAL / MOE_EUNSUPPORTED without launching anything.  A
+ *    launch failure returns MOE_EHIP.  Device faults appear at the caller's
+ *    next synchronisation.  T == 0 is a no-op that returns MOE_OK.
+ *  - Work is enqueued on `stream` (0 = the null stream); no call synchronises.
+ *  - Supported shapes: d_model % 64 == 0, d_ff % 64 == 0, 1 <= top_k <= n_experts
+ *    <= 256, 0 <= T, T * top_k < 2^24.  Inputs must be finite.
+ *  - Index order: a token's k slots hold its experts in ascending id; an
+ *    assignment id is a = t * top_k + j; the permutation lists assignment ids
+ *    grouped by expert (ascending) and, within an expert, by token.
+ *  - Calls that share no buffers may run concurrently on different streams.
+ *
+ * Activation pack format ("split MX6")
+ * ------------------------------------
+ * The expert GEMMs consume activations that are already split into two MX
+ * terms, hi + lo, each stored as FP6 E2M3 codes with one E8M0 scale per 32
+ * values; hi + lo reproduces a bf16 row to about 2^-9 of its block maximum.
+ * One packed row of K values (K % 64 == 0) is moe_act_pack_bytes(K, 1) bytes:
+ *     [hi codes : K/32 blocks x 24 B][lo codes : K/32 blocks x 24 B]
+ *     [hi scales: 2 x KTp B][lo scales: 2 x KTp B]        KTp = roundup(K/64, 4)
+ * Block b's 32 codes are 6-bit fields packed little-endian (element i at bits
+ * 6i..6i+5); E2M3 = sign | 2 exponent bits (bias 1) | 3 mantissa bits.  The
+ * scale of block b sits at index [b % 2][b / 2] of its 2 x KTp array.
+ *
+ * Prepacked weight format
+ * -----------------------
+ * moe_mxfp4_prepack reorders canonical MXFP4 bytes (codes [E][N][K/2], even K
+ * in the low nibble; scales [E][N][K/32]; gate/up rows 0..I-1 gate and I..2I-1
+ * up) into tiles of 32 output rows x 64 K values laid out in the order the
+ * gfx950 scaled MFMA reads them, so each wavefront load is one contiguous
+ * 1 KiB.  Sizes: moe_prepacked_codes_bytes / moe_prepacked_scales_bytes.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,          /* null pointer, negative size, misaligned pointer, bad enum */
+  MOE_EUNSUPPORTED = 2,    /* shape outside the supported set above */
+  MOE_EWORKSPACE = 3,      /* workspace smaller than moe_workspace_bytes */
+  MOE_EHIP = 4             /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_FP32 = 1 } moe_dtype;
+
+typedef enum { MOE_STAGE_GATE_UP = 0, MOE_STAGE_DOWN = 1 } moe_stage;
+
+/* MoE-relevant model configuration (model card fields hidden_size,
+ * intermediate_size, num_local_experts, num_experts_per_tok, swiglu_limit). */
+typedef struct {
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t n_experts;
+  int32_t top_k;
+  float swiglu_limit;
+} moe_dims;
+
+/* Prepacked expert weights of one layer (device pointers, 16-byte aligned). */
+typedef struct {
+  const uint8_t* gu_codes;
+  const uint8_t* gu_scales;
+  const uint8_t* dn_codes;
+  const uint8_t* dn_scales;
+} moe_weights;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(moe_status s);
+
+/* Bytes of `rows` packed activation rows of length K (0 if K % 64 != 0). */
+size_t moe_act_pack_bytes(int32_t K, int32_t rows);
+
+/* Bytes of the prepacked codes / scales of all experts for one stage. */
+size_t moe_prepacked_codes_bytes(const moe_dims* dims, moe_stage stage);
+size_t moe_prepacked_scales_bytes(const moe_dims* dims, moe_stage stage);
+
+/* Workspace bytes moe_forward needs for T tokens (0 on invalid dims). */
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t T);
+
+/*
+ * Router, top-k and softmax gating ("Mixture of Experts" section of the
+ * ewbang.com walk-through: the router scores experts, keeps several and weights
+ * them; gpt-oss keeps 4).
+ *   x_bf16    [T][d_model] bf16, row-major, 16-byte aligned
+ *   w_router  [n_experts][d_model] fp32, 16-byte aligned;  b_router [n_experts] fp32
+ *   topk_idx  out [T][top_k] int32: selected expert ids, ascending per token
+ *   topk_w    out [T][top_k] fp32: softmax of the selected logits (same order)
+ *   logits    out [T][n_experts] fp32 or NULL: router logits (fp32 accumulation)
+ * Selection is decided in float64: logits are accumulated in fp32 on the
+ * matrix cores, and every expert within 1e-4 of the k-th largest is re-scored
+ * in float64 before the final choice; exact ties go to the lower id.  Gates are
+ * computed from float64 logits.
+ */
+moe_status moe_route(const moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                     const float* b_router, int32_t* topk_idx, float* topk_w, float* logits,
+                     hipStream_t stream);
+
+/*
+ * Group the T*top_k assignments by expert (deterministic, no atomics on order).
+ *   topk_idx  [T][top_k] int32, every entry in [0, n_experts)
+ *   counts    out [n_experts]; offsets out [n_experts + 1] (exclusive prefix sum)
+ *   perm      out [T*top_k]: assignment id at each grouped position
+ *   inv       out [T*top_k]: inv[perm[p]] = p
+ */
+moe_status moe_permute(const moe_dims* dims, int32_t T, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t stream);
+
+/*
+ * Split bf16 rows into the packed hi/lo MX6 activation format above.
+ *   a_bf16   [rows][K] bf16 row-major, 16-byte aligned;  K % 64 == 0
+ *   a_packed out, moe_act_pack_bytes(K, rows) bytes, 16-byte aligned
+ */
+moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_packed, hipStream_t stream);
+
+/*
+ * Grouped expert GEMM on MXFP4 weights with the CDNA4 scaled FP4 matrix cores.
+ *  MOE_STAGE_GATE_UP:
+ *    a_packed  packed x, T rows of d_model (moe_pack_act output); row of
+ *              grouped position p is token perm[p] / top_k
+ *    codes/scales  prepacked gate/up weights (moe_mxfp4_prepack, stage GATE_UP)
+ *    out       packed h, T*top_k rows of d_ff, row p = grouped position p, with
+ *              h = bf16(silu(clamp(g)) * clamp(u)) split into hi/lo MX6
+ *    topk_w    unused (may be NULL)
+ *  MOE_STAGE_DOWN:
+ *    a_packed  packed h from the GATE_UP stage
+ *    codes/scales  prepacked down weights (stage DOWN)
+ *    topk_w    [T][top_k] fp32 gates; row p is scaled by topk_w[perm[p]]
+ *    out       y_perm [T*top_k][d_model] fp32, row p = gate-weighted expert output
+ *  perm/offsets are moe_permute's outputs.  Experts with no token are skipped
+ *  (their weights are not read).
+ */
+moe_status moe_expert_gemm_mxfp4(const moe_dims* dims, int32_t T, moe_stage stage, const void* a_packed,
+                                 const int32_t* perm, const int32_t* offsets, const uint8_t* codes,
+                                 const uint8_t* scales, const float* topk_w, void* out, hipStream_t stream);
+
+/*
+ * Weighted combine: y[t] = sum over the token's slots j (ascending expert id)
+ * of y_perm[inv[t*top_k + j]], summed in fp32.
+ *   y_perm [T*top_k][d_model] fp32 (gate already applied);  inv from moe_permute
+ *   y      out [T][d_model], fp32 (MOE_FP32) or bf16 round-to-nearest-even (MOE_BF16)
+ */
+moe_status moe_combine(const moe_dims* dims, int32_t T, const float* y_perm, const int32_t* inv, void* y,
+                       moe_dtype y_dtype, hipStream_t stream);
+
+/*
+ * The whole layer: route -> permute -> pack x -> gate/up + SwiGLU -> down ->
+ * combine, six launches on `stream`, no host synchronisation.
+ *   ws / ws_bytes: device scratch of at least moe_workspace_bytes(dims, T)
+ *   bytes, 256-byte aligned; its contents are undefined after the call.
+ */
+moe_status moe_forward(const moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                       const float* b_router, const moe_weights* weights, void* y, moe_dtype y_dtype,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- host-only helpers (off the hot path; no HIP calls) ---------------- */
+
+/*
+ * Quantize fp32 rows [rows][K] (host memory, K % 32 == 0) to canonical MXFP4
+ * with the OCP Microscaling v1.0 rule: scale exponent floor(log2(amax)) - 2,
+ * elements rounded to nearest even on the E2M1 grid, saturating at +-6; an
+ * all-zero block gets scale byte 0.  codes [rows][K/2], scales [rows][K/32].
+ */
+moe_status moe_mxfp4_quantize(const float* w, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales);
+
+/*
+ * Reorder canonical MXFP4 bytes of all n_experts experts (host memory) into
+ * the device tile layout.  stage GATE_UP: N = 2*d_ff rows of K = d_model;
+ * stage DOWN: N = d_model rows of K = d_ff.
+ */
+moe_status moe_mxfp4_prepack(const moe_dims* dims, moe_stage stage, const uint8_t* codes,
+                             const uint8_t* scales, uint8_t* codes_out, uint8_t* scales_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

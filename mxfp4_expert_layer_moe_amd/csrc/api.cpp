@@ -1,0 +1,276 @@
+// C ABI of the MoE layer: argument validation, workspace layout, launch order,
+// and the host-side MXFP4 quantizer and weight prepack.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe_mxfp4.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlignWs = 256;
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+moe_status check_dims(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->d_model <= 0 || d->d_ff <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
+  if (!(d->swiglu_limit > 0.0f) || !isfinite(d->swiglu_limit)) return MOE_EINVAL;
+  if (d->d_model % kKTile || d->d_ff % kKTile) return MOE_EUNSUPPORTED;
+  if (d->top_k > d->n_experts || d->n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_T(const moe_dims* d, int32_t T) {
+  if (T < 0) return MOE_EINVAL;
+  if ((int64_t)T * d->top_k >= (1 << 24)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+struct WsLayout {
+  size_t idx, w, counts, offsets, perm, inv, xpack, hpack, yperm, total;
+};
+
+WsLayout ws_layout(const moe_dims* d, int32_t T) {
+  WsLayout L;
+  const size_t n = (size_t)T * d->top_k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = round_up(o + bytes, kAlignWs); return at; };
+  L.idx = take(n * 4);
+  L.w = take(n * 4);
+  L.counts = take((size_t)d->n_experts * 4);
+  L.offsets = take(((size_t)d->n_experts + 1) * 4);
+  L.perm = take(n * 4);
+  L.inv = take(n * 4);
+  L.xpack = take((size_t)T * act_row_bytes(d->d_model));
+  L.hpack = take(n * act_row_bytes(d->d_ff));
+  L.yperm = take(n * (size_t)d->d_model * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported shape";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch or runtime error";
+  }
+  return "unknown moe_status";
+}
+
+size_t moe_act_pack_bytes(int32_t K, int32_t rows) {
+  if (K <= 0 || K % kKTile || rows < 0) return 0;
+  return (size_t)rows * act_row_bytes(K);
+}
+
+size_t moe_prepacked_codes_bytes(const moe_dims* d, moe_stage stage) {
+  if (check_dims(d) != MOE_OK) return 0;
+  const int N = stage == MOE_STAGE_GATE_UP ? 2 * d->d_ff : d->d_model;
+  const int K = stage == MOE_STAGE_GATE_UP ? d->d_model : d->d_ff;
+  return (size_t)d->n_experts * w_codes_per_expert(N, K);
+}
+
+size_t moe_prepacked_scales_bytes(const moe_dims* d, moe_stage stage) {
+  if (check_dims(d) != MOE_OK) return 0;
+  const int N = stage == MOE_STAGE_GATE_UP ? 2 * d->d_ff : d->d_model;
+  const int K = stage == MOE_STAGE_GATE_UP ? d->d_model : d->d_ff;
+  return (size_t)d->n_experts * w_scales_per_expert(N, K);
+}
+
+size_t moe_workspace_bytes(const moe_dims* d, int32_t T) {
+  if (check_dims(d) != MOE_OK || check_T(d, T) != MOE_OK) return 0;
+  return ws_layout(d, T).total;
+}
+
+moe_status moe_route(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                     const float* b_router, int32_t* topk_idx, float* topk_w, float* logits,
+                     hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (!x_bf16 || !w_router || !b_router || !topk_idx || !topk_w) return MOE_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(b_router, 4) || !aligned(topk_idx, 4) ||
+      !aligned(topk_w, 4) || (logits && !aligned(logits, 4)))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_route(T, d->d_model, d->n_experts, d->top_k, (const uint16_t*)x_bf16, w_router,
+                                 b_router, topk_idx, topk_w, logits, stream));
+}
+
+moe_status moe_permute(const moe_dims* d, int32_t T, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* inv, hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (!topk_idx || !counts || !offsets || !perm || !inv) return MOE_EINVAL;
+  if (!aligned(topk_idx, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) ||
+      !aligned(inv, 4))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_permute(T, d->n_experts, d->top_k, topk_idx, counts, offsets, perm, inv, stream));
+}
+
+moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_packed, hipStream_t stream) {
+  if (K <= 0 || rows < 0) return MOE_EINVAL;
+  if (K % kKTile) return MOE_EUNSUPPORTED;
+  if (!a_bf16 || !a_packed || !aligned(a_bf16, 16) || !aligned(a_packed, 16)) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  return hip_status(launch_pack(K, rows, (const uint16_t*)a_bf16, (uint8_t*)a_packed, stream));
+}
+
+moe_status moe_expert_gemm_mxfp4(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed,
+                                 const int32_t* perm, const int32_t* offsets, const uint8_t* codes,
+                                 const uint8_t* scales, const float* topk_w, void* out, hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN) return MOE_EINVAL;
+  if (!a_packed || !perm || !offsets || !codes || !scales || !out) return MOE_EINVAL;
+  if (stage == MOE_STAGE_DOWN && !topk_w) return MOE_EINVAL;
+  if (!aligned(a_packed, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(out, 16) ||
+      !aligned(perm, 4) || !aligned(offsets, 4) || (topk_w && !aligned(topk_w, 4)))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_gemm(stage == MOE_STAGE_GATE_UP ? 0 : 1, T, d->d_model, d->d_ff, d->n_experts,
+                                d->top_k, d->swiglu_limit, (const uint8_t*)a_packed, perm, offsets, codes, scales,
+                                topk_w, out, stream));
+}
+
+moe_status moe_combine(const moe_dims* d, int32_t T, const float* y_perm, const int32_t* inv, void* y,
+                       moe_dtype y_dtype, hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (y_dtype != MOE_BF16 && y_dtype != MOE_FP32) return MOE_EINVAL;
+  if (!y_perm || !inv || !y || !aligned(y_perm, 16) || !aligned(inv, 4) || !aligned(y, 16)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_combine(T, d->d_model, d->top_k, y_perm, inv, y, y_dtype == MOE_BF16, stream));
+}
+
+moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                       const float* b_router, const moe_weights* wts, void* y, moe_dtype y_dtype, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (y_dtype != MOE_BF16 && y_dtype != MOE_FP32) return MOE_EINVAL;
+  if (!x_bf16 || !w_router || !b_router || !wts || !y || !ws) return MOE_EINVAL;
+  if (!wts->gu_codes || !wts->gu_scales || !wts->dn_codes || !wts->dn_scales) return MOE_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(b_router, 4) || !aligned(y, 16) ||
+      !aligned(ws, kAlignWs) || !aligned(wts->gu_codes, 16) || !aligned(wts->dn_codes, 16) ||
+      !aligned(wts->gu_scales, 4) || !aligned(wts->dn_scales, 4))
+    return MOE_EINVAL;
+  const WsLayout L = ws_layout(d, T);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  uint8_t* base = (uint8_t*)ws;
+  int32_t* idx = (int32_t*)(base + L.idx);
+  float* w = (float*)(base + L.w);
+  int32_t* counts = (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* perm = (int32_t*)(base + L.perm);
+  int32_t* inv = (int32_t*)(base + L.inv);
+  uint8_t* xpack = base + L.xpack;
+  uint8_t* hpack = base + L.hpack;
+  float* yperm = (float*)(base + L.yperm);
+  const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
+  hipError_t e;
+  if ((e = launch_route(T, D, E, k, (const uint16_t*)x_bf16, w_router, b_router, idx, w, nullptr, stream)))
+    return MOE_EHIP;
+  if ((e = launch_permute(T, E, k, idx, counts, offsets, perm, inv, stream))) return MOE_EHIP;
+  if ((e = launch_pack(D, T, (const uint16_t*)x_bf16, xpack, stream))) return MOE_EHIP;
+  if ((e = launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, perm, offsets, wts->gu_codes, wts->gu_scales,
+                       nullptr, hpack, stream)))
+    return MOE_EHIP;
+  if ((e = launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, perm, offsets, wts->dn_codes, wts->dn_scales, w,
+                       yperm, stream)))
+    return MOE_EHIP;
+  if ((e = launch_combine(T, D, k, yperm, inv, y, y_dtype == MOE_BF16, stream))) return MOE_EHIP;
+  return MOE_OK;
+}
+
+// ---- host-only ---------------------------------------------------------------
+
+moe_status moe_mxfp4_quantize(const float* w, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales) {
+  if (!w || !codes || !scales || rows < 0 || K <= 0) return MOE_EINVAL;
+  if (K % kBlock) return MOE_EUNSUPPORTED;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int b = 0; b < K / kBlock; ++b) {
+      const float* v = w + r * K + (int64_t)b * kBlock;
+      float amax = 0.0f;
+      for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      int sbyte = 0;
+      if (amax > 0.0f) {
+        int ex;
+        frexpf(amax, &ex);                      // amax = m * 2^ex, m in [0.5, 1)
+        sbyte = ex - 1 - 2 + 127;
+        sbyte = sbyte < 0 ? 0 : (sbyte > 254 ? 254 : sbyte);
+      }
+      scales[r * (K / kBlock) + b] = (uint8_t)sbyte;
+      const float inv = ldexpf(1.0f, 127 - sbyte);
+      for (int i = 0; i < kBlock; ++i) {
+        const float q = fabsf(v[i]) * inv;
+        float c;
+        if (q < 2.0f) c = rintf(q * 2.0f);
+        else if (q < 4.0f) c = 4.0f + rintf(q - 2.0f);
+        else c = 6.0f + rintf(fminf(q, 6.0f) * 0.5f - 2.0f);
+        uint8_t code = (uint8_t)(c > 7.0f ? 7.0f : c);
+        if (v[i] < 0.0f) code |= 8;
+        const int64_t kk = (int64_t)b * kBlock + i;
+        uint8_t* dst = codes + r * (K / 2) + kk / 2;
+        if (kk % 2 == 0) *dst = code;
+        else *dst = (uint8_t)(*dst | (code << 4));
+      }
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status moe_mxfp4_prepack(const moe_dims* d, moe_stage stage, const uint8_t* codes, const uint8_t* scales,
+                             uint8_t* codes_out, uint8_t* scales_out) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN) return MOE_EINVAL;
+  if (!codes || !scales || !codes_out || !scales_out) return MOE_EINVAL;
+  const bool gu = stage == MOE_STAGE_GATE_UP;
+  const int N = gu ? 2 * d->d_ff : d->d_model;
+  const int K = gu ? d->d_model : d->d_ff;
+  const int KT = K / kKTile, KG = w_kgroups(K), NQ = N / kNTile;
+  const size_t cpe = w_codes_per_expert(N, K), spe = w_scales_per_expert(N, K);
+  const size_t crow = K / 2, srow = K / kBlock;
+  for (int e = 0; e < d->n_experts; ++e) {
+    const uint8_t* ce = codes + (size_t)e * N * crow;
+    const uint8_t* se = scales + (size_t)e * N * srow;
+    uint8_t* co = codes_out + (size_t)e * cpe;
+    uint8_t* so = scales_out + (size_t)e * spe;
+    for (int q = 0; q < NQ; ++q) {
+      const int base = gu ? ((q & 1) ? d->d_ff : 0) + 32 * (q >> 1) : 32 * q;
+      for (int kt = 0; kt < KT; ++kt)
+        for (int l = 0; l < 64; ++l) {
+          const int row = base + (l & 31), blk = 2 * kt + (l >> 5);
+          memcpy(co + (((size_t)q * KT + kt) * 64 + l) * 16, ce + (size_t)row * crow + (size_t)blk * 16, 16);
+        }
+      for (int g = 0; g < KG; ++g)
+        for (int l = 0; l < 64; ++l)
+          for (int j = 0; j < 4; ++j) {
+            const int kt = 4 * g + j, row = base + (l & 31);
+            const uint8_t v = kt < KT ? se[(size_t)row * srow + 2 * kt + (l >> 5)] : 0;
+            so[(((size_t)q * KG + g) * 64 + l) * 4 + j] = v;
+          }
+    }
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// Grouping of the T*k (token, expert) assignments by expert.
+//
+// Only a subset of experts runs per token ("From GPT-2 to gpt-oss", section 4,
+// Mixture of Experts: the MoE block is sparse), so the expert GEMMs work on the
+// rows each expert received.  This kernel builds that grouping:
+//   counts[e], offsets = exclusive prefix sum, perm (assignment ids grouped by
+//   expert, ascending token within an expert) and its inverse.
+// The result is unique and deterministic: positions come from counts and
+// in-order ranks, never from the order in which atomics land.
+//
+// One workgroup of 1024 threads walks the assignments in chunks of 1024 (each
+// thread keeps its assignments in registers).  Within a wavefront, a thread's
+// rank among equal experts comes from a ballot-based match (one ballot per
+// expert-id bit); across wavefronts, per-(wave, expert) counts in LDS give the
+// offsets.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / 64;
+constexpr int kPermRegs = 32;          // assignments held per thread per pass
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, const int32_t* __restrict__ idx,
+                                                               int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ perm,
+                                                               int32_t* __restrict__ inv) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int wcnt[kPermWaves][kMaxExperts];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+  for (int e = tid; e < E; e += kPermThreads) cnt[e] = 0;
+  __syncthreads();
+
+  // ---- histogram (integer LDS atomics: the totals do not depend on order) ----
+  for (int a = tid; a < n; a += kPermThreads) {
+    const int e = idx[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // ---- exclusive scan by wave 0 --------------------------------------------
+  if (wave == 0) {
+    int carry = 0;
+    for (int c = 0; c < E; c += 64) {
+      const int e = c + lane;
+      const int v = e < E ? cnt[e] : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      if (e < E) {
+        base[e] = carry + incl - v;
+        counts[e] = v;
+        offsets[e] = carry + incl - v;
+      }
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+
+  // ---- stable scatter, chunk by chunk --------------------------------------
+  const int nchunks = (n + kPermThreads - 1) / kPermThreads;
+  for (int c0 = 0; c0 < nchunks; c0 += kPermRegs) {
+    int ev[kPermRegs];
+#pragma unroll
+    for (int r = 0; r < kPermRegs; ++r) {
+      const int a = (c0 + r) * kPermThreads + tid;
+      ev[r] = (c0 + r < nchunks && a < n) ? idx[a] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kPermRegs; ++r) {
+      if (c0 + r >= nchunks) break;                      // uniform
+      const int a = (c0 + r) * kPermThreads + tid;
+      const int e = ev[r];
+      const bool valid = (unsigned)e < (unsigned)E;
+      // lanes holding the same expert: intersect ballots over the id bits
+      uint64_t same = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const uint64_t b = __ballot(valid && ((e >> bit) & 1));
+        same &= ((e >> bit) & 1) ? b : ~b;
+      }
+      const int rank = __popcll(same & lt_mask);
+      for (int e2 = tid; e2 < kPermWaves * kMaxExperts; e2 += kPermThreads) (&wcnt[0][0])[e2] = 0;
+      __syncthreads();
+      if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
+      __syncthreads();
+      if (valid) {
+        int pos = base[e] + rank;
+        for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+        perm[pos] = a;
+        inv[a] = pos;
+      }
+      __syncthreads();
+      for (int e2 = tid; e2 < E; e2 += kPermThreads) {
+        int s = 0;
+        for (int w = 0; w < kPermWaves; ++w) s += wcnt[w][e2];
+        base[e2] += s;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, hipStream_t s) {
+  const int n = T * k;
+  permute_kernel<<<dim3(1), dim3(kPermThreads), 0, s>>>(n, E, idx, counts, offsets, perm, inv);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,113 @@
+"""Device-side buffers of one MoE layer (torch for memory and streams only).
+
+``DeviceLayer`` uploads a layer's inputs (bf16 x, fp32 router, MXFP4 experts
+prepacked by the C library) to the GPU, owns the workspace and output buffers,
+and calls the C entry points, either one step at a time or as ``moe_forward``.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (MOE_BF16, MOE_FP32, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, dims, moe_act_pack_bytes, moe_combine,
+               moe_expert_gemm_mxfp4, moe_forward, moe_mxfp4_prepack, moe_pack_act, moe_permute, moe_route,
+               moe_weights, moe_workspace_bytes)
+
+
+def _u8(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).to(device)
+
+
+class DeviceWeights:
+    """Prepacked MXFP4 expert weights of one layer on the device."""
+
+    def __init__(self, d, gu_codes, gu_scales, dn_codes, dn_scales, device="cuda"):
+        gc, gs = moe_mxfp4_prepack(d, MOE_STAGE_GATE_UP, gu_codes, gu_scales)
+        dc, ds = moe_mxfp4_prepack(d, MOE_STAGE_DOWN, dn_codes, dn_scales)
+        self.gu_codes, self.gu_scales = _u8(gc, device), _u8(gs, device)
+        self.dn_codes, self.dn_scales = _u8(dc, device), _u8(ds, device)
+
+    @classmethod
+    def from_prepacked(cls, tensors):
+        obj = cls.__new__(cls)
+        obj.gu_codes, obj.gu_scales, obj.dn_codes, obj.dn_scales = tensors
+        return obj
+
+    def clone(self):
+        return DeviceWeights.from_prepacked([t.clone() for t in
+                                             (self.gu_codes, self.gu_scales, self.dn_codes, self.dn_scales)])
+
+    def struct(self) -> moe_weights:
+        return moe_weights(self.gu_codes.data_ptr(), self.gu_scales.data_ptr(), self.dn_codes.data_ptr(),
+                           self.dn_scales.data_ptr())
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in (self.gu_codes, self.gu_scales, self.dn_codes, self.dn_scales))
+
+
+class DeviceLayer:
+    def __init__(self, inp, device="cuda", weights: DeviceWeights | None = None):
+        self.T, self.D, self.E, self.k, self.I = inp.T, inp.D, inp.E, inp.k, inp.I
+        self.dims = dims(inp.D, inp.I, inp.E, inp.k, inp.swiglu_limit)
+        self.device = device
+        self.x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(device).view(torch.bfloat16)
+        self.w_router = torch.from_numpy(np.ascontiguousarray(inp.w_router)).to(device)
+        self.b_router = torch.from_numpy(np.ascontiguousarray(inp.b_router)).to(device)
+        self.weights = weights or DeviceWeights(self.dims, inp.gu_codes, inp.gu_scales, inp.dn_codes,
+                                                inp.dn_scales, device)
+        T, k, D, I, E = self.T, self.k, self.D, self.I, self.E
+        n = T * k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty((T, k), **i32)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.perm = torch.empty(n, **i32)
+        self.inv = torch.empty(n, **i32)
+        self.x_packed = torch.empty(max(moe_act_pack_bytes(D, T), 16), dtype=torch.uint8, device=device)
+        self.h_packed = torch.empty(max(moe_act_pack_bytes(I, n), 16), dtype=torch.uint8, device=device)
+        self.y_perm = torch.empty((n, D), dtype=torch.float32, device=device)
+        self.y32 = torch.empty((T, D), dtype=torch.float32, device=device)
+        self.y16 = torch.empty((T, D), dtype=torch.bfloat16, device=device)
+        self.ws = torch.empty(max(moe_workspace_bytes(self.dims, T), 256), dtype=torch.uint8, device=device)
+
+    # ---- step by step (the C entry points in order) ---------------------------
+    def route(self, logits=True, stream=None):
+        moe_route(self.dims, self.T, self.x, self.w_router, self.b_router, self.topk_idx, self.topk_w,
+                  self.logits if logits else None, stream)
+
+    def permute(self, stream=None):
+        moe_permute(self.dims, self.T, self.topk_idx, self.counts, self.offsets, self.perm, self.inv, stream)
+
+    def pack_x(self, stream=None):
+        moe_pack_act(self.D, self.T, self.x, self.x_packed, stream)
+
+    def gate_up(self, weights: DeviceWeights | None = None, stream=None):
+        w = weights or self.weights
+        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_GATE_UP, self.x_packed, self.perm, self.offsets,
+                              w.gu_codes, w.gu_scales, None, self.h_packed, stream)
+
+    def down(self, weights: DeviceWeights | None = None, stream=None):
+        w = weights or self.weights
+        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_DOWN, self.h_packed, self.perm, self.offsets,
+                              w.dn_codes, w.dn_scales, self.topk_w, self.y_perm, stream)
+
+    def combine(self, bf16=False, stream=None):
+        moe_combine(self.dims, self.T, self.y_perm, self.inv, self.y16 if bf16 else self.y32,
+                    MOE_BF16 if bf16 else MOE_FP32, stream)
+
+    def steps(self, bf16=False, stream=None):
+        self.route(stream=stream)
+        self.permute(stream)
+        self.pack_x(stream)
+        self.gate_up(stream=stream)
+        self.down(stream=stream)
+        self.combine(bf16, stream)
+
+    def forward(self, bf16=False, weights: DeviceWeights | None = None, stream=None):
+        w = weights or self.weights
+        moe_forward(self.dims, self.T, self.x, self.w_router, self.b_router, w.struct(),
+                    self.y16 if bf16 else self.y32, MOE_BF16 if bf16 else MOE_FP32, self.ws, None, stream)
+        return self.y16 if bf16 else self.y32

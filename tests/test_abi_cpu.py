@@ -1,0 +1,148 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares,
+rejects bad arguments before any HIP call, and its host-side helpers (MXFP4
+quantizer, prepack, size functions) are right.  No GPU needed: no call here
+reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mxfp4_expert_layer_moe_amd as M
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return M.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe_mxfp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_header_symbol(L):
+    names = header_functions()
+    assert len(names) >= 12
+    assert sorted(M.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert M.moe_status_str(s).startswith("MOE_")
+
+
+D = M.dims(2880, 2880, 32, 4)
+
+
+def test_size_functions_closed_forms():
+    assert M.moe_act_pack_bytes(2880, 1) == 90 * 48 + 4 * 48
+    assert M.moe_act_pack_bytes(64, 3) == 3 * (2 * 48 + 16)
+    assert M.moe_act_pack_bytes(96, 1) == 0                    # K % 64 != 0
+    # prepacked codes are exactly the MXFP4 code bytes: 4 bits per weight
+    assert M.moe_prepacked_codes_bytes(D, M.MOE_STAGE_GATE_UP) == 32 * 5760 * 2880 // 2
+    assert M.moe_prepacked_codes_bytes(D, M.MOE_STAGE_DOWN) == 32 * 2880 * 2880 // 2
+    # scales: 45 k-tiles padded to 48 per 32-row tile
+    assert M.moe_prepacked_scales_bytes(D, M.MOE_STAGE_GATE_UP) == 32 * (5760 // 32) * 12 * 256
+    ws = M.moe_workspace_bytes(D, 4096)
+    assert ws >= 4096 * 4 * (2880 * 4 + M.moe_act_pack_bytes(2880, 1)) + 4096 * M.moe_act_pack_bytes(2880, 1)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(d_model=2880 + 32), M.MOE_EUNSUPPORTED),
+    (dict(d_ff=100), M.MOE_EUNSUPPORTED),
+    (dict(top_k=0), M.MOE_EINVAL),
+    (dict(top_k=33), M.MOE_EUNSUPPORTED),
+    (dict(n_experts=257, top_k=4), M.MOE_EUNSUPPORTED),
+    (dict(swiglu_limit=0.0), M.MOE_EINVAL),
+    (dict(swiglu_limit=float("inf")), M.MOE_EINVAL),
+])
+def test_bad_dims_rejected(L, bad, status):
+    args = dict(d_model=2880, d_ff=2880, n_experts=32, top_k=4, swiglu_limit=7.0)
+    args.update(bad)
+    d = M.moe_dims(**args)
+    st = L.moe_route(ctypes.byref(d), 4, 16, 16, 16, 16, 16, None, None)
+    assert st == status
+    assert L.moe_workspace_bytes(ctypes.byref(d), 4) == 0
+
+
+def test_bad_arguments_rejected_before_launch(L):
+    d = ctypes.byref(D)
+    A = 1 << 20                                   # fake, aligned, never dereferenced
+    assert L.moe_route(None, 4, A, A, A, A, A, None, None) == M.MOE_EINVAL
+    assert L.moe_route(d, -1, A, A, A, A, A, None, None) == M.MOE_EINVAL
+    assert L.moe_route(d, 1 << 22, A, A, A, A, A, None, None) == M.MOE_EUNSUPPORTED   # T*k >= 2^24
+    assert L.moe_route(d, 4, None, A, A, A, A, None, None) == M.MOE_EINVAL
+    assert L.moe_route(d, 4, A + 2, A, A, A, A, None, None) == M.MOE_EINVAL          # misaligned x
+    assert L.moe_route(d, 0, A, A, A, A, A, None, None) == M.MOE_OK                  # T = 0: no-op
+    assert L.moe_permute(d, 4, A, A, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_permute(d, 0, A, A, A, A, A, None) == M.MOE_OK
+    assert L.moe_pack_act(96, 4, A, A, None) == M.MOE_EUNSUPPORTED
+    assert L.moe_pack_act(64, 4, A, A + 8, None) == M.MOE_EINVAL
+    assert L.moe_pack_act(64, 0, A, A, None) == M.MOE_OK
+    assert L.moe_expert_gemm_mxfp4(d, 4, 7, A, A, A, A, A, A, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_GATE_UP, A, A, A, A + 4, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4(d, 0, M.MOE_STAGE_GATE_UP, A, A, A, A, A, None, A, None) == M.MOE_OK
+    assert L.moe_combine(d, 4, A, A, A, 5, None) == M.MOE_EINVAL
+    assert L.moe_combine(d, 4, A, A, A + 4, M.MOE_FP32, None) == M.MOE_EINVAL
+    w = M.moe_weights(A, A, A, A)
+    need = L.moe_workspace_bytes(d, 4)
+    assert L.moe_forward(d, 4, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need - 1, None) == M.MOE_EWORKSPACE
+    assert L.moe_forward(d, 4, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A + 16, need, None) == M.MOE_EINVAL
+    w0 = M.moe_weights(A, None, A, A)
+    assert L.moe_forward(d, 4, A, A, A, ctypes.byref(w0), A, M.MOE_FP32, A, need, None) == M.MOE_EINVAL
+    assert L.moe_forward(d, 0, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need, None) == M.MOE_OK
+
+
+def test_host_quantizer_matches_generator_encoder():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    w[3, :32] = 0.0                                   # zero block
+    w[5, 40] = 1e3                                    # wide block
+    w[7, :32] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0] * 4, np.float32)   # ties
+    c1, s1 = M.moe_mxfp4_quantize(w)
+    c2, s2 = synth.mxfp4_encode(w)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    # decodes within the quantizer bound: half a step, or up to 2X when amax/X in (6, 8) saturates
+    dec = oracle.mxfp4_decode(c1, s1)
+    X = np.repeat(np.ldexp(1.0, s1.astype(int) - 127), 32, axis=1)
+    assert np.all(np.abs(dec - w) <= 2.0 * X)
+
+
+def prepack_reference(codes, scales, N, K, I, gate_up):
+    """Independent statement of the device tile layout (see include/moe_mxfp4.h)."""
+    E = codes.shape[0]
+    KT, KG, NQ = K // 64, (K // 64 + 3) // 4, N // 32
+    co = np.zeros((E, NQ, KT, 64, 16), np.uint8)
+    so = np.zeros((E, NQ, KG, 64, 4), np.uint8)
+    for q in range(NQ):
+        base = ((I if q % 2 else 0) + 32 * (q // 2)) if gate_up else 32 * q
+        rows = base + np.arange(64) % 32
+        for kt in range(KT):
+            blk = 2 * kt + np.arange(64) // 32
+            for l in range(64):
+                co[:, q, kt, l] = codes[:, rows[l], blk[l] * 16:(blk[l] + 1) * 16]
+                so[:, q, kt // 4, l, kt % 4] = scales[:, rows[l], blk[l]]
+    return co.reshape(-1), so.reshape(-1)
+
+
+@pytest.mark.parametrize("D_,I_", [(64, 64), (128, 192)])
+def test_prepack_layout(D_, I_):
+    inp = synth.make_inputs(dict(T=4, D=D_, E=3, k=2, I=I_, seed=8))
+    d = M.dims(D_, I_, 3, 2)
+    co, so = M.moe_mxfp4_prepack(d, M.MOE_STAGE_GATE_UP, inp.gu_codes, inp.gu_scales)
+    rc, rs = prepack_reference(inp.gu_codes, inp.gu_scales, 2 * I_, D_, I_, True)
+    assert np.array_equal(co, rc) and np.array_equal(so, rs)
+    co, so = M.moe_mxfp4_prepack(d, M.MOE_STAGE_DOWN, inp.dn_codes, inp.dn_scales)
+    rc, rs = prepack_reference(inp.dn_codes, inp.dn_scales, D_, I_, I_, False)
+    assert np.array_equal(co, rc) and np.array_equal(so, rs)
