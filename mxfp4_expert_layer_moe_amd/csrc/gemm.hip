@@ -39,9 +39,9 @@ struct GemmArgs {
   size_t codes_per_expert, scales_per_expert;
 };
 
-// Locate row tile `mt` among all experts' 32-row tiles.  Every lane gets the
-// expert, the first grouped position and the number of valid rows (<= 32).
-__device__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mt, int& e_out, int& p0,
+// Locate row tile `mt` among all experts' tiles of bm rows.  Every lane gets the
+// expert, the first grouped position and the number of valid rows (<= bm).
+__device__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int bm, int mt, int& e_out, int& p0,
                               int& nrows) {
   const int lane = threadIdx.x & 63;
   int before = 0;
@@ -49,7 +49,7 @@ __device__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mt
     const int e = c + lane;
     int off = 0, cnt = 0;
     if (e < E) { off = offsets[e]; cnt = offsets[e + 1] - off; }
-    const int tiles = (cnt + kMTile - 1) / kMTile;
+    const int tiles = (cnt + bm - 1) / bm;
     int incl = tiles;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -63,8 +63,8 @@ __device__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mt
       const int src = __ffsll((long long)m) - 1;
       e_out = c + src;
       const int lt = mt - before - __shfl(excl, src);
-      p0 = __shfl(off, src) + lt * kMTile;
-      nrows = min(kMTile, __shfl(cnt, src) - lt * kMTile);
+      p0 = __shfl(off, src) + lt * bm;
+      nrows = min(bm, __shfl(cnt, src) - lt * bm);
       return true;
     }
     before += __shfl(incl, 63);
@@ -72,76 +72,68 @@ __device__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mt
   return false;
 }
 
-__device__ inline v8i load_a24(const uint8_t* p) {
+constexpr int kAStageBytes = 36 * 1024;     // LDS for staged activation rows: 8 rows of K = 2880 fit whole
+
+__device__ inline v8i b_operand(const uint4 b) {
+  v8i v = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return v;
+}
+
+// scaled MFMA, A = FP6 E2M3 (scale byte 0 of sa), B = FP4 E2M1 (scale byte `ob` of sb)
+template <int OB>
+__device__ inline v16f mma_fp6_fp4(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 4, 0, sa, OB, sb);
+}
+
+// ob is a compile-time constant after unrolling, so the switch folds away
+__device__ inline v16f mma_sel(int ob, v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  switch (ob) {
+    case 0: return mma_fp6_fp4<0>(a, b, c, sa, sb);
+    case 1: return mma_fp6_fp4<1>(a, b, c, sa, sb);
+    case 2: return mma_fp6_fp4<2>(a, b, c, sa, sb);
+    default: return mma_fp6_fp4<3>(a, b, c, sa, sb);
+  }
+}
+
+__device__ inline v8i a_operand_lds(const uint8_t* p) {      // 24 bytes, 8-byte aligned
   const uint2* q = reinterpret_cast<const uint2*>(p);
   const uint2 a = q[0], b = q[1], c = q[2];
   v8i v = {(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
   return v;
 }
 
-__device__ inline v8i load_b16(const uint8_t* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  v8i v = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-  return v;
-}
+// Staged row layout in LDS (per tile row, stride rs = roundup(100 * KC, 16) bytes):
+//   [hi codes KC x 48][lo codes KC x 48][hi scales: half 0 KC, half 1 KC][lo scales: 2 x KC]
+__host__ __device__ inline int stage_stride(int KC) { return (KC * 100 + 15) & ~15; }
 
-template <int NB>
-struct KStep {
-  v8i ahi, alo;
-  v8i b[NB];
-};
-
-template <int NB>
-__device__ inline void load_step(KStep<NB>& s, bool valid, const uint8_t* arow, size_t lo_off, int blk,
-                                 const uint8_t* const* bptr, int kt) {
-  if (valid) {
-    s.ahi = load_a24(arow + (size_t)blk * 24);
-    s.alo = load_a24(arow + lo_off + (size_t)blk * 24);
-  } else {
-    s.ahi = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    s.alo = s.ahi;
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) s.b[nb] = load_b16(bptr[nb] + (size_t)kt * 1024);
-}
-
-template <int J, int NB>
-__device__ inline void mma_step(v16f* acc, const KStep<NB>& s, uint32_t sah, uint32_t sal, const uint32_t* sb) {
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(s.ahi, s.b[nb], acc[nb], 2, 4, J, sah, J, sb[nb]);
-    acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(s.alo, s.b[nb], acc[nb], 2, 4, J, sal, J, sb[nb]);
-  }
-}
-
-__device__ inline float half_max(float v) {
-#pragma unroll
-  for (int d = 1; d < 32; d <<= 1) v = fmaxf(v, __shfl_xor(v, d));
-  return v;
-}
-
-template <int STAGE>
+template <int STAGE, int P, int BM>
 __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   constexpr int NB = STAGE == 0 ? 2 : 1;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  static_assert(P % 4 == 0, "prefetch depth must cover whole scale groups");
+  static_assert(BM <= kMTile && BM * 100 * P <= kAStageBytes, "a chunk of P k-tiles must fit for BM rows");
+  __shared__ __attribute__((aligned(16))) uint8_t sA[kAStageBytes];
+  __shared__ int srow[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int u = blockIdx.x * 4 + wave;                  // output unit of this wavefront
-  if (u >= g.units) return;
+  const bool active = u < g.units;                      // inactive waves still join the barriers
   int e, p0, nrows;
-  if (!find_row_tile(g.offsets, g.E, blockIdx.y, e, p0, nrows)) return;
+  if (!find_row_tile(g.offsets, g.E, BM, blockIdx.y, e, p0, nrows)) return;   // uniform per workgroup
 
   const int i = lane & 31;
   const int half = lane >> 5;
   const bool valid = i < nrows;
+  if (tid < nrows) srow[tid] = STAGE == 0 ? g.perm[p0 + tid] / g.k : p0 + tid;
+
+  // K chunk staged at once: everything if it fits, else a multiple of the prefetch depth
+  int KC = g.KT;
+  if (nrows * stage_stride(KC) > kAStageBytes) KC = (kAStageBytes / (nrows * 100)) / P * P;
+  const int rs = stage_stride(KC);
   const size_t arb = act_row_bytes(g.K);
-  const uint8_t* arow = g.a_packed;
-  if (valid) {
-    const size_t src = STAGE == 0 ? (size_t)(g.perm[p0 + i] / g.k) : (size_t)(p0 + i);
-    arow = g.a_packed + src * arb;
-  }
   const size_t lo_off = act_lo_codes_off(g.K);
-  const size_t hs_off = act_hi_scales_off(g.K) + (size_t)half * act_ktp(g.K);
-  const size_t ls_off = act_lo_scales_off(g.K) + (size_t)half * act_ktp(g.K);
+  const int ktp = act_ktp(g.K);
 
   const uint8_t* bptr[NB];
   const uint8_t* sptr[NB];
@@ -152,50 +144,93 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     sptr[nb] = g.scales + (size_t)e * g.scales_per_expert + (size_t)q * g.KG * 256 + (size_t)lane * 4;
   }
 
+  // weight ring: slot j holds k-tile kt with kt % P == j; scale slot s holds group (kt / 4) with (kt/4) % (P/4) == s
+  uint4 bq[P][NB];
+  uint32_t sbq[P / 4][NB];
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+      if (j < g.KT) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bq[j][nb] = *reinterpret_cast<const uint4*>(bptr[nb] + (size_t)j * 1024);
+      }
+#pragma unroll
+    for (int s = 0; s < P / 4; ++s)
+      if (s < g.KG) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sbq[s][nb] = *reinterpret_cast<const uint32_t*>(sptr[nb] + (size_t)s * 256);
+      }
+  }
+
   v16f acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = v16f{};
 
-  for (int kg = 0; kg < g.KG; ++kg) {
-    uint32_t sah = 0x7f7f7f7fu, sal = 0x7f7f7f7fu;
-    if (valid) {
-      sah = *reinterpret_cast<const uint32_t*>(arow + hs_off + 4 * kg);
-      sal = *reinterpret_cast<const uint32_t*>(arow + ls_off + 4 * kg);
+  for (int c0 = 0; c0 < g.KT; c0 += KC) {
+    const int kcn = min(KC, g.KT - c0);
+    __syncthreads();                                    // previous chunk consumed; srow visible
+    // stage rows [0, nrows) x k-tiles [c0, c0 + kcn): codes as 16-byte words, scales as bytes
+    const int n16 = kcn * 3;                            // 16-byte words per term per row
+    for (int w = tid; w < nrows * 2 * n16; w += 256) {
+      const int r = w / (2 * n16), rem = w - r * 2 * n16, term = rem / n16, o = rem - term * n16;
+      const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + term * lo_off + (size_t)c0 * 48 + (size_t)o * 16;
+      *reinterpret_cast<uint4*>(sA + r * rs + term * KC * 48 + o * 16) = *reinterpret_cast<const uint4*>(src);
     }
-    uint32_t sb[NB];
+    for (int w = tid; w < nrows * 4 * kcn; w += 256) {
+      const int r = w / (4 * kcn), rem = w - r * 4 * kcn, arr = rem / kcn, j = rem - arr * kcn;
+      // arr: 0 = hi half 0, 1 = hi half 1, 2 = lo half 0, 3 = lo half 1
+      const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + act_hi_scales_off(g.K) + (size_t)arr * ktp + c0 + j;
+      sA[r * rs + KC * 96 + arr * KC + j] = *src;
+    }
+    __syncthreads();
+    if (active) {
+      const uint8_t* arow = sA + i * rs;
+      // one k-tile: A from LDS (every lane reads; rows past nrows are masked to zero), two MFMAs
+      // per weight tile, then refill slot j with k-tile kt + P.  The refill address is clamped
+      // to the last k-tile so the loop body has no branches (a clamped reload hits the cache).
+      auto step = [&](const int j, const int kt) {
+        const int kl = kt - c0;
+        v8i ahi = a_operand_lds(arow + kl * 48 + half * 24);
+        v8i alo = a_operand_lds(arow + KC * 48 + kl * 48 + half * 24);
+        uint32_t sah = arow[KC * 96 + half * KC + kl];
+        uint32_t sal = arow[KC * 96 + (2 + half) * KC + kl];
+        const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+        ahi = valid ? ahi : z;
+        alo = valid ? alo : z;
+        sah = valid ? sah : 127u;
+        sal = valid ? sal : 127u;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) sb[nb] = *reinterpret_cast<const uint32_t*>(sptr[nb] + (size_t)kg * 256);
-    const int kt0 = 4 * kg;
-    if (kt0 + 3 < g.KT) {
-      KStep<NB> s0, s1, s2, s3;
-      load_step<NB>(s0, valid, arow, lo_off, 2 * (kt0 + 0) + half, bptr, kt0 + 0);
-      load_step<NB>(s1, valid, arow, lo_off, 2 * (kt0 + 1) + half, bptr, kt0 + 1);
-      load_step<NB>(s2, valid, arow, lo_off, 2 * (kt0 + 2) + half, bptr, kt0 + 2);
-      load_step<NB>(s3, valid, arow, lo_off, 2 * (kt0 + 3) + half, bptr, kt0 + 3);
-      mma_step<0, NB>(acc, s0, sah, sal, sb);
-      mma_step<1, NB>(acc, s1, sah, sal, sb);
-      mma_step<2, NB>(acc, s2, sah, sal, sb);
-      mma_step<3, NB>(acc, s3, sah, sal, sb);
-    } else {
-      KStep<NB> s;
-      load_step<NB>(s, valid, arow, lo_off, 2 * kt0 + half, bptr, kt0);
-      mma_step<0, NB>(acc, s, sah, sal, sb);
-      if (kt0 + 1 < g.KT) {
-        load_step<NB>(s, valid, arow, lo_off, 2 * (kt0 + 1) + half, bptr, kt0 + 1);
-        mma_step<1, NB>(acc, s, sah, sal, sb);
+        for (int nb = 0; nb < NB; ++nb) {
+          const v8i bv = b_operand(bq[j][nb]);
+          acc[nb] = mma_sel(j & 3, ahi, bv, acc[nb], sah, sbq[j >> 2][nb]);
+          acc[nb] = mma_sel(j & 3, alo, bv, acc[nb], sal, sbq[j >> 2][nb]);
+        }
+        const int kn = min(kt + P, g.KT - 1);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bq[j][nb] = *reinterpret_cast<const uint4*>(bptr[nb] + (size_t)kn * 1024);
+        if ((j & 3) == 3) {
+          const int grp = min((kt + P - 3) / 4, g.KG - 1);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            sbq[j >> 2][nb] = *reinterpret_cast<const uint32_t*>(sptr[nb] + (size_t)grp * 256);
+        }
+      };
+      int kb = c0;
+      for (; kb + P <= c0 + kcn; kb += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) step(j, kb + j);
       }
-      if (kt0 + 2 < g.KT) {
-        load_step<NB>(s, valid, arow, lo_off, 2 * (kt0 + 2) + half, bptr, kt0 + 2);
-        mma_step<2, NB>(acc, s, sah, sal, sb);
-      }
+#pragma unroll
+      for (int j = 0; j < P; ++j)
+        if (kb + j < c0 + kcn) step(j, kb + j);          // tail of the chunk (uniform)
     }
   }
+  if (!active) return;
 
-  if (STAGE == 0) {
+  if constexpr (STAGE == 0) {
     // SwiGLU epilogue: h = bf16(silu(clamp(g)) * clamp(u)), written as hi/lo MX6 block u of row p
     const int I = g.out_K;
     const size_t orb = act_row_bytes(I);
-    const int ktp = act_ktp(I);
     uint8_t* out = reinterpret_cast<uint8_t*>(g.out);
     const int c = lane & 31;
 #pragma unroll
@@ -204,31 +239,8 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       const float gv = fminf(fmaxf(acc[0][r], -g.limit), g.limit);
       const float uv = fminf(fmaxf(acc[1][r], -g.limit), g.limit);
       const float h = bf16_round(gv / (1.0f + expf(-gv)) * uv);
-      const uint32_t s_hi = e2m3_scale_byte(half_max(fabsf(h)));
-      float d;
-      const uint32_t c_hi = e2m3_encode(h, e8m0_to_inv(s_hi), e8m0_to_float(s_hi), &d);
-      const float res = h - d;
-      const uint32_t s_lo = e2m3_scale_byte(half_max(fabsf(res)));
-      const uint32_t c_lo = e2m3_encode(res, e8m0_to_inv(s_lo), e8m0_to_float(s_lo), &d);
-      uint32_t vh = c_hi << (6 * (c & 3));
-      uint32_t vl = c_lo << (6 * (c & 3));
-      vh |= __shfl_xor(vh, 1);
-      vl |= __shfl_xor(vl, 1);
-      vh |= __shfl_xor(vh, 2);
-      vl |= __shfl_xor(vl, 2);
-      if (m < nrows) {
-        uint8_t* row = out + (size_t)(p0 + m) * orb;
-        if ((c & 3) == 0) {
-          uint8_t* ph = row + (size_t)u * 24 + 3 * (c >> 2);
-          uint8_t* pl = row + act_lo_codes_off(I) + (size_t)u * 24 + 3 * (c >> 2);
-          ph[0] = (uint8_t)vh; ph[1] = (uint8_t)(vh >> 8); ph[2] = (uint8_t)(vh >> 16);
-          pl[0] = (uint8_t)vl; pl[1] = (uint8_t)(vl >> 8); pl[2] = (uint8_t)(vl >> 16);
-        }
-        if (c == 0) {
-          row[act_hi_scales_off(I) + (size_t)(u & 1) * ktp + (u >> 1)] = (uint8_t)s_hi;
-          row[act_lo_scales_off(I) + (size_t)(u & 1) * ktp + (u >> 1)] = (uint8_t)s_lo;
-        }
-      }
+      const Split32 sp = split_block32(h, c);
+      if (m < nrows) store_split32(out + (size_t)(p0 + m) * orb, I, u, c, sp);
     }
   } else {
     // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp32
@@ -262,12 +274,19 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   g.codes_per_expert = w_codes_per_expert(N, g.K);
   g.scales_per_expert = w_scales_per_expert(N, g.K);
   const long long n_assign = (long long)T * k;
-  const unsigned tiles_y = (unsigned)((n_assign + kMTile - 1) / kMTile + (E < n_assign ? E : n_assign));
+  // decode-sized batches (few rows per expert): 8-row tiles whose activations fit LDS whole;
+  // otherwise 32-row tiles (one full MFMA tile) with K staged in chunks
+  const bool small = n_assign <= 8LL * E;
+  const int bm = small ? 8 : kMTile;
+  const unsigned tiles_y = (unsigned)((n_assign + bm - 1) / bm + (E < n_assign ? E : n_assign));
   const dim3 grid((g.units + 3) / 4, tiles_y);
-  if (stage == 0)
-    expert_gemm_kernel<0><<<grid, dim3(256), 0, s>>>(g);
-  else
-    expert_gemm_kernel<1><<<grid, dim3(256), 0, s>>>(g);
+  if (stage == 0) {
+    if (small) expert_gemm_kernel<0, 8, 8><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<0, 8, kMTile><<<grid, dim3(256), 0, s>>>(g);
+  } else {
+    if (small) expert_gemm_kernel<1, 16, 8><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<1, 8, kMTile><<<grid, dim3(256), 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 

@@ -70,12 +70,13 @@ __device__ inline uint32_t e2m3_encode(float v, float inv_scale, float scale, fl
 }
 
 // Shared exponent of a block whose largest magnitude is amax: floor(log2 amax) - 2,
-// returned as the E8M0 byte (clamped to [1, 254]); amax == 0 gives 127.
+// returned as the E8M0 byte, clamped to [1, 253] so that both the scale and its
+// inverse are normal fp32 numbers; amax == 0 gives 127.
 __device__ inline uint32_t e2m3_scale_byte(float amax) {
   if (!(amax > 0.0f)) return 127u;
   int e = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 2;
   int b = e + 127;
-  return (uint32_t)(b < 1 ? 1 : (b > 254 ? 254 : b));
+  return (uint32_t)(b < 1 ? 1 : (b > 253 ? 253 : b));
 }
 
 __device__ inline float e8m0_to_float(uint32_t b) { return __uint_as_float(b << 23); }
@@ -88,6 +89,54 @@ __device__ inline float bf16_round(float v) {
 }
 
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ inline float half_wave_max(float v) {
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) v = fmaxf(v, __shfl_xor(v, d));
+  return v;
+}
+
+// Split one 32-value block held one value per lane of a half-wavefront (lane c of
+// the half holds element c) into hi/lo E2M3 terms.  All 64 lanes must call it.
+// vh / vl: the 24-bit little-endian code group of elements 4*(c/4)..+3 (valid in
+// every lane of the group); s_hi / s_lo: the E8M0 scale bytes of the block.
+struct Split32 {
+  uint32_t vh, vl, s_hi, s_lo;
+};
+
+__device__ inline Split32 split_block32(float v, int c) {
+  Split32 r;
+  r.s_hi = e2m3_scale_byte(half_wave_max(fabsf(v)));
+  float d;
+  const uint32_t c_hi = e2m3_encode(v, e8m0_to_inv(r.s_hi), e8m0_to_float(r.s_hi), &d);
+  const float res = v - d;
+  r.s_lo = e2m3_scale_byte(half_wave_max(fabsf(res)));
+  const uint32_t c_lo = e2m3_encode(res, e8m0_to_inv(r.s_lo), e8m0_to_float(r.s_lo), &d);
+  uint32_t vh = c_hi << (6 * (c & 3));
+  uint32_t vl = c_lo << (6 * (c & 3));
+  vh |= __shfl_xor(vh, 1);
+  vl |= __shfl_xor(vl, 1);
+  vh |= __shfl_xor(vh, 2);
+  vl |= __shfl_xor(vl, 2);
+  r.vh = vh;
+  r.vl = vl;
+  return r;
+}
+
+// Store block b of a packed row (K values) from lane c of the half-wave that split it.
+__device__ inline void store_split32(uint8_t* row, int K, int b, int c, const Split32& s) {
+  if ((c & 3) == 0) {
+    uint8_t* ph = row + (size_t)b * 24 + 3 * (c >> 2);
+    uint8_t* pl = row + act_lo_codes_off(K) + (size_t)b * 24 + 3 * (c >> 2);
+    ph[0] = (uint8_t)s.vh; ph[1] = (uint8_t)(s.vh >> 8); ph[2] = (uint8_t)(s.vh >> 16);
+    pl[0] = (uint8_t)s.vl; pl[1] = (uint8_t)(s.vl >> 8); pl[2] = (uint8_t)(s.vl >> 16);
+  }
+  if (c == 0) {
+    const int ktp = act_ktp(K);
+    row[act_hi_scales_off(K) + (size_t)(b & 1) * ktp + (b >> 1)] = (uint8_t)s.s_hi;
+    row[act_lo_scales_off(K) + (size_t)(b & 1) * ktp + (b >> 1)] = (uint8_t)s.s_lo;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Host-side launchers (one translation unit each); return the launch status.
