@@ -116,15 +116,20 @@ size_t moe_workspace_bytes(const moe_dims* dims, int32_t T);
  *   w_router  [n_experts][d_model] fp32, 16-byte aligned;  b_router [n_experts] fp32
  *   topk_idx  out [T][top_k] int32: selected expert ids, ascending per token
  *   topk_w    out [T][top_k] fp32: softmax of the selected logits (same order)
- *   logits    out [T][n_experts] fp32 or NULL: router logits (fp32 accumulation)
- * Selection is decided in float64: logits are accumulated in fp32 on the
- * matrix cores, and every expert within 1e-4 of the k-th largest is re-scored
- * in float64 before the final choice; exact ties go to the lower id.  Gates are
- * computed from float64 logits.
+ *   logits    out [T][n_experts] fp32 or NULL: router logits (rounded from float64)
+ *   ws        device scratch of at least moe_route_workspace_bytes(dims, T)
+ *             bytes, 256-byte aligned (float64 partial logits of the K slices)
+ * Logits are accumulated on the matrix cores (exact bf16 x split-fp32
+ * products, 16-term fp32 partial sums, float64 accumulation); any expert
+ * within 36 eps32 ||x_t|| max_e ||w_e|| of the k-th largest (twice the error
+ * bound) is re-scored exactly in float64 before the final choice, so the
+ * selection is the float64 one; exact ties go to the lower id.  Gates are the
+ * softmax of the float64 scores.
  */
+size_t moe_route_workspace_bytes(const moe_dims* dims, int32_t T);
 moe_status moe_route(const moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
                      const float* b_router, int32_t* topk_idx, float* topk_w, float* logits,
-                     hipStream_t stream);
+                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Group the T*top_k assignments by expert (deterministic, no atomics on order).

@@ -22,7 +22,7 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN = 0, 1
 
 # Symbols the header declares (checked by the CPU tests).
 EXPORTS = ("moe_status_str", "moe_act_pack_bytes", "moe_prepacked_codes_bytes", "moe_prepacked_scales_bytes",
-           "moe_workspace_bytes", "moe_route", "moe_permute", "moe_pack_act", "moe_expert_gemm_mxfp4",
+           "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_route", "moe_permute", "moe_pack_act", "moe_expert_gemm_mxfp4",
            "moe_combine", "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_prepack")
 
 
@@ -61,9 +61,10 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_prepacked_codes_bytes", "moe_prepacked_scales_bytes"):
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, ctypes.c_int]
-        L.moe_workspace_bytes.restype = sz
-        L.moe_workspace_bytes.argtypes = [dp, i32]
-        L.moe_route.argtypes = [dp, i32, vp, f32p, f32p, i32p, f32p, f32p, vp]
+        for name in ("moe_workspace_bytes", "moe_route_workspace_bytes"):
+            getattr(L, name).restype = sz
+            getattr(L, name).argtypes = [dp, i32]
+        L.moe_route.argtypes = [dp, i32, vp, f32p, f32p, i32p, f32p, f32p, vp, sz, vp]
         L.moe_permute.argtypes = [dp, i32, i32p, i32p, i32p, i32p, i32p, vp]
         L.moe_pack_act.argtypes = [i32, i32, vp, vp, vp]
         L.moe_expert_gemm_mxfp4.argtypes = [dp, i32, ctypes.c_int, vp, i32p, i32p, vp, vp, f32p, vp, vp]
@@ -125,9 +126,15 @@ def moe_workspace_bytes(d: moe_dims, T: int) -> int:
     return lib().moe_workspace_bytes(ctypes.byref(d), T)
 
 
-def moe_route(d, T, x, w_router, b_router, topk_idx, topk_w, logits=None, stream=None):
+def moe_route_workspace_bytes(d: moe_dims, T: int) -> int:
+    return lib().moe_route_workspace_bytes(ctypes.byref(d), T)
+
+
+def moe_route(d, T, x, w_router, b_router, topk_idx, topk_w, logits, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
     _check(lib().moe_route(ctypes.byref(d), T, _p(x), _p(w_router), _p(b_router), _p(topk_idx), _p(topk_w),
-                           _p(logits), _s(stream)), "moe_route")
+                           _p(logits), _p(ws), ws_bytes, _s(stream)), "moe_route")
 
 
 def moe_permute(d, T, topk_idx, counts, offsets, perm, inv, stream=None):

@@ -33,7 +33,7 @@ moe_status check_T(const moe_dims* d, int32_t T) {
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 struct WsLayout {
-  size_t idx, w, counts, offsets, perm, inv, xpack, hpack, yperm, total;
+  size_t idx, w, counts, offsets, perm, inv, xpack, hpack, yperm, route, total;
 };
 
 WsLayout ws_layout(const moe_dims* d, int32_t T) {
@@ -50,6 +50,7 @@ WsLayout ws_layout(const moe_dims* d, int32_t T) {
   L.xpack = take((size_t)T * act_row_bytes(d->d_model));
   L.hpack = take(n * act_row_bytes(d->d_ff));
   L.yperm = take(n * (size_t)d->d_model * 4);
+  L.route = take(route_workspace_bytes(T, d->d_model, d->n_experts));
   L.total = o;
   return L;
 }
@@ -93,19 +94,25 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T) {
   return ws_layout(d, T).total;
 }
 
+size_t moe_route_workspace_bytes(const moe_dims* d, int32_t T) {
+  if (check_dims(d) != MOE_OK || check_T(d, T) != MOE_OK) return 0;
+  return route_workspace_bytes(T, d->d_model, d->n_experts);
+}
+
 moe_status moe_route(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
-                     const float* b_router, int32_t* topk_idx, float* topk_w, float* logits,
-                     hipStream_t stream) {
+                     const float* b_router, int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_dims(d);
   if (st != MOE_OK) return st;
   if ((st = check_T(d, T)) != MOE_OK) return st;
-  if (!x_bf16 || !w_router || !b_router || !topk_idx || !topk_w) return MOE_EINVAL;
+  if (!x_bf16 || !w_router || !b_router || !topk_idx || !topk_w || (T > 0 && !ws)) return MOE_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(b_router, 4) || !aligned(topk_idx, 4) ||
-      !aligned(topk_w, 4) || (logits && !aligned(logits, 4)))
+      !aligned(topk_w, 4) || (logits && !aligned(logits, 4)) || !aligned(ws, kAlignWs))
     return MOE_EINVAL;
+  if (ws_bytes < route_workspace_bytes(T, d->d_model, d->n_experts)) return MOE_EWORKSPACE;
   if (T == 0) return MOE_OK;
   return hip_status(launch_route(T, d->d_model, d->n_experts, d->top_k, (const uint16_t*)x_bf16, w_router,
-                                 b_router, topk_idx, topk_w, logits, stream));
+                                 b_router, topk_idx, topk_w, logits, ws, stream));
 }
 
 moe_status moe_permute(const moe_dims* d, int32_t T, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -186,7 +193,8 @@ moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const f
   float* yperm = (float*)(base + L.yperm);
   const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
   hipError_t e;
-  if ((e = launch_route(T, D, E, k, (const uint16_t*)x_bf16, w_router, b_router, idx, w, nullptr, stream)))
+  if ((e = launch_route(T, D, E, k, (const uint16_t*)x_bf16, w_router, b_router, idx, w, nullptr, base + L.route,
+                        stream)))
     return MOE_EHIP;
   if ((e = launch_permute(T, E, k, idx, counts, offsets, perm, inv, stream))) return MOE_EHIP;
   if ((e = launch_pack(D, T, (const uint16_t*)x_bf16, xpack, stream))) return MOE_EHIP;

@@ -74,9 +74,18 @@ __device__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int bm
 
 constexpr int kAStageBytes = 36 * 1024;     // LDS for staged activation rows: 8 rows of K = 2880 fit whole
 
-__device__ inline v8i b_operand(const uint4 b) {
-  v8i v = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ inline v8i b_operand(const v4i b) {
+  v8i v = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
   return v;
+}
+
+// Raw buffer resource over [base, base + bytes): weight tiles are fetched with buffer loads, so a
+// wavefront needs one lane offset in a vector register and a scalar offset per k-tile (no 64-bit
+// address per load), and any read past `bytes` returns zero.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
 // scaled MFMA, A = FP6 E2M3 (scale byte 0 of sa), B = FP4 E2M1 (scale byte `ob` of sb)
@@ -106,7 +115,10 @@ __device__ inline v8i a_operand_lds(const uint8_t* p) {      // 24 bytes, 8-byte
 //   [hi codes KC x 48][lo codes KC x 48][hi scales: half 0 KC, half 1 KC][lo scales: 2 x KC]
 __host__ __device__ inline int stage_stride(int KC) { return (KC * 100 + 15) & ~15; }
 
-template <int STAGE, int P, int BM>
+// KTC: the number of 64-wide k-tiles when known at compile time (K = 2880 gives 45), else 0.
+// With KTC the whole K range is staged at once and the k-loop is fully unrolled, so the
+// weight ring is never drained at a loop back-edge.
+template <int STAGE, int P, int BM, int KTC>
 __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   constexpr int NB = STAGE == 0 ? 2 : 1;
   static_assert(P % 4 == 0, "prefetch depth must cover whole scale groups");
@@ -116,11 +128,14 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u = blockIdx.x * 4 + wave;                  // output unit of this wavefront
   const bool active = u < g.units;                      // inactive waves still join the barriers
   int e, p0, nrows;
   if (!find_row_tile(g.offsets, g.E, BM, blockIdx.y, e, p0, nrows)) return;   // uniform per workgroup
+  e = __builtin_amdgcn_readfirstlane(e);
+  p0 = __builtin_amdgcn_readfirstlane(p0);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);
 
   const int i = lane & 31;
   const int half = lane >> 5;
@@ -128,37 +143,48 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   if (tid < nrows) srow[tid] = STAGE == 0 ? g.perm[p0 + tid] / g.k : p0 + tid;
 
   // K chunk staged at once: everything if it fits, else a multiple of the prefetch depth
-  int KC = g.KT;
-  if (nrows * stage_stride(KC) > kAStageBytes) KC = (kAStageBytes / (nrows * 100)) / P * P;
+  int KC = KTC > 0 ? KTC : g.KT;
+  if (KTC == 0 && nrows * stage_stride(KC) > kAStageBytes) KC = (kAStageBytes / (nrows * 100)) / P * P;
   const int rs = stage_stride(KC);
   const size_t arb = act_row_bytes(g.K);
   const size_t lo_off = act_lo_codes_off(g.K);
   const int ktp = act_ktp(g.K);
 
-  const uint8_t* bptr[NB];
-  const uint8_t* sptr[NB];
+  // this expert's weights as buffer resources; tile q starts at q*KT k-tiles (codes) / q*KG groups (scales)
+  const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(g.codes + (size_t)e * g.codes_per_expert,
+                                                 (uint32_t)g.codes_per_expert);
+  const __amdgpu_buffer_rsrc_t rsS = buffer_rsrc(g.scales + (size_t)e * g.scales_per_expert,
+                                                 (uint32_t)g.scales_per_expert);
+  const int voffB = lane * 16, voffS = lane * 4;
+  int sbase[NB], ssbase[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int q = STAGE == 0 ? 2 * u + nb : u;
-    bptr[nb] = g.codes + (size_t)e * g.codes_per_expert + (size_t)q * g.KT * 1024 + (size_t)lane * 16;
-    sptr[nb] = g.scales + (size_t)e * g.scales_per_expert + (size_t)q * g.KG * 256 + (size_t)lane * 4;
+    sbase[nb] = q * g.KT * 1024;
+    ssbase[nb] = q * g.KG * 256;
   }
+  auto load_b = [&](const int nb, const int kt) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rsB, voffB, sbase[nb] + kt * 1024, 0);
+  };
+  auto load_s = [&](const int nb, const int grp) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsS, voffS, ssbase[nb] + grp * 256, 0);
+  };
 
   // weight ring: slot j holds k-tile kt with kt % P == j; scale slot s holds group (kt / 4) with (kt/4) % (P/4) == s
-  uint4 bq[P][NB];
+  v4i bq[P][NB];
   uint32_t sbq[P / 4][NB];
   if (active) {
 #pragma unroll
     for (int j = 0; j < P; ++j)
       if (j < g.KT) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bq[j][nb] = *reinterpret_cast<const uint4*>(bptr[nb] + (size_t)j * 1024);
+        for (int nb = 0; nb < NB; ++nb) bq[j][nb] = load_b(nb, j);
       }
 #pragma unroll
     for (int s = 0; s < P / 4; ++s)
       if (s < g.KG) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sbq[s][nb] = *reinterpret_cast<const uint32_t*>(sptr[nb] + (size_t)s * 256);
+        for (int nb = 0; nb < NB; ++nb) sbq[s][nb] = load_s(nb, s);
       }
   }
 
@@ -185,44 +211,57 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     __syncthreads();
     if (active) {
       const uint8_t* arow = sA + i * rs;
-      // one k-tile: A from LDS (every lane reads; rows past nrows are masked to zero), two MFMAs
-      // per weight tile, then refill slot j with k-tile kt + P.  The refill address is clamped
-      // to the last k-tile so the loop body has no branches (a clamped reload hits the cache).
-      auto step = [&](const int j, const int kt) {
+      const int kend = c0 + kcn;
+      // A operands of k-tile kt from LDS; rows past nrows read stale bytes and are masked to zero
+      auto lds_a = [&](const int kt, v8i& hi, v8i& lo, uint32_t& sh, uint32_t& sl) {
         const int kl = kt - c0;
-        v8i ahi = a_operand_lds(arow + kl * 48 + half * 24);
-        v8i alo = a_operand_lds(arow + KC * 48 + kl * 48 + half * 24);
-        uint32_t sah = arow[KC * 96 + half * KC + kl];
-        uint32_t sal = arow[KC * 96 + (2 + half) * KC + kl];
+        hi = a_operand_lds(arow + kl * 48 + half * 24);
+        lo = a_operand_lds(arow + KC * 48 + kl * 48 + half * 24);
+        sh = arow[KC * 96 + half * KC + kl];
+        sl = arow[KC * 96 + (2 + half) * KC + kl];
         const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
-        ahi = valid ? ahi : z;
-        alo = valid ? alo : z;
-        sah = valid ? sah : 127u;
-        sal = valid ? sal : 127u;
+        hi = valid ? hi : z;
+        lo = valid ? lo : z;
+        sh = valid ? sh : 127u;
+        sl = valid ? sl : 127u;
+      };
+      // one k-tile (slot j = kt % P): A from LDS, two MFMAs per weight tile, then refill slot j
+      // with k-tile kt + P (address clamped to the last k-tile so there is no branch; a clamped
+      // reload hits the cache).  The scheduling barrier keeps every refill where it is written,
+      // so each wavefront keeps P k-tiles of weights in flight.
+      auto step = [&](const int j, const int kt) {
+        v8i ah, al;
+        uint32_t sh, sl;
+        lds_a(kt, ah, al, sh, sl);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const v8i bv = b_operand(bq[j][nb]);
-          acc[nb] = mma_sel(j & 3, ahi, bv, acc[nb], sah, sbq[j >> 2][nb]);
-          acc[nb] = mma_sel(j & 3, alo, bv, acc[nb], sal, sbq[j >> 2][nb]);
+          acc[nb] = mma_sel(j & 3, ah, bv, acc[nb], sh, sbq[j >> 2][nb]);
+          acc[nb] = mma_sel(j & 3, al, bv, acc[nb], sl, sbq[j >> 2][nb]);
         }
         const int kn = min(kt + P, g.KT - 1);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bq[j][nb] = *reinterpret_cast<const uint4*>(bptr[nb] + (size_t)kn * 1024);
+        for (int nb = 0; nb < NB; ++nb) bq[j][nb] = load_b(nb, kn);
         if ((j & 3) == 3) {
           const int grp = min((kt + P - 3) / 4, g.KG - 1);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            sbq[j >> 2][nb] = *reinterpret_cast<const uint32_t*>(sptr[nb] + (size_t)grp * 256);
+          for (int nb = 0; nb < NB; ++nb) sbq[j >> 2][nb] = load_s(nb, grp);
         }
+        if constexpr (KTC > 0) __builtin_amdgcn_sched_barrier(0);
       };
-      int kb = c0;
-      for (; kb + P <= c0 + kcn; kb += P) {
+      if constexpr (KTC > 0) {
 #pragma unroll
-        for (int j = 0; j < P; ++j) step(j, kb + j);
+        for (int kt = 0; kt < KTC; ++kt) step(kt % P, kt);    // single chunk: c0 == 0, kcn == KTC
+      } else {
+        int kb = c0;
+        for (; kb + P <= kend; kb += P) {
+#pragma unroll
+          for (int j = 0; j < P; ++j) step(j, kb + j);
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+          if (kb + j < kend) step(j, kb + j);              // tail of the chunk (uniform)
       }
-#pragma unroll
-      for (int j = 0; j < P; ++j)
-        if (kb + j < c0 + kcn) step(j, kb + j);          // tail of the chunk (uniform)
     }
   }
   if (!active) return;
@@ -280,12 +319,16 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   const int bm = small ? 8 : kMTile;
   const unsigned tiles_y = (unsigned)((n_assign + bm - 1) / bm + (E < n_assign ? E : n_assign));
   const dim3 grid((g.units + 3) / 4, tiles_y);
+  // the model's K = 2880 (45 k-tiles) with decode tiles: fully unrolled k-loop
+  const bool k45 = g.KT == 45 && small && 8 * stage_stride(45) <= kAStageBytes;
   if (stage == 0) {
-    if (small) expert_gemm_kernel<0, 8, 8><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_kernel<0, 8, kMTile><<<grid, dim3(256), 0, s>>>(g);
+    if (k45) expert_gemm_kernel<0, 8, 8, 45><<<grid, dim3(256), 0, s>>>(g);
+    else if (small) expert_gemm_kernel<0, 8, 8, 0><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<0, 8, kMTile, 0><<<grid, dim3(256), 0, s>>>(g);
   } else {
-    if (small) expert_gemm_kernel<1, 16, 8><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_kernel<1, 8, kMTile><<<grid, dim3(256), 0, s>>>(g);
+    if (k45) expert_gemm_kernel<1, 16, 8, 45><<<grid, dim3(256), 0, s>>>(g);
+    else if (small) expert_gemm_kernel<1, 16, 8, 0><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<1, 8, kMTile, 0><<<grid, dim3(256), 0, s>>>(g);
   }
   return hipGetLastError();
 }

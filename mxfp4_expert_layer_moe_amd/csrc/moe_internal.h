@@ -142,7 +142,8 @@ __device__ inline void store_split32(uint8_t* row, int K, int b, int c, const Sp
 // Host-side launchers (one translation unit each); return the launch status.
 // ---------------------------------------------------------------------------
 hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
-                        int32_t* idx, float* w, float* logits, hipStream_t s);
+                        int32_t* idx, float* w, float* logits, void* ws, hipStream_t s);
+size_t route_workspace_bytes(int T, int D, int E);
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, hipStream_t s);
 hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipStream_t s);

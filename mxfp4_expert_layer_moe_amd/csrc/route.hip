@@ -6,30 +6,35 @@
 // Experts": the router picks several experts and weights them, e.g.
 // A = 0.7 NN2 + 0.3 NN4; gpt-oss keeps 4 of 32 / 128).
 //
-// Design (one workgroup of 8 wavefronts per 32 tokens):
-//  1. Logits on the bf16 matrix cores.  x is bf16; the fp32 router weight is
-//     split exactly into three bf16 terms (truncation: hi + mid + lo == w), so
-//     every product is exact.  Each 16-wide k-step's three MFMAs start from
-//     zero and their small fp32 result is added into a float64 accumulator, so
-//     the only fp32 roundings are those of 16-term partial sums.  Work items
-//     are (32-expert tile, K slice) pairs spread over the 8 waves; K slices are
-//     summed in LDS in a fixed order (deterministic).
-//  2. Per token (one wave per token): top-k by wave-wide arg-max over the
-//     float64 logits (larger first, lower id on ties).
-//  3. If any other expert lies within a band of the k-th largest, every expert
-//     in the band is re-scored exactly in float64 and the top-k is re-taken
-//     over those scores.  The band, 36 eps32 ||x_t|| max_e ||w_e||, is twice a
-//     worst-case bound of the step-1 error (at most 18 fp32 roundings per
-//     k-step, each at most eps32 times that k-step's sum of |x_d w_d|, and
-//     sum_d |x_d w_d| <= ||x_t|| ||w_e|| by Cauchy-Schwarz), so the result is
-//     the float64 selection at any input scale.  Gates are the softmax of the
-//     selected float64 scores.
+// Two kernels:
+//  route_logits: KW workgroups of 16 wavefronts per (32-token tile, 32-expert
+//     tile) split the K loop (KW > 1 only for small batches, so that a decode
+//     step still spreads over many compute units); each wavefront issues the
+//     loads of four k-steps before their matrix instructions.  Logits run on
+//     the bf16 matrix cores:
+//     x is bf16 and the fp32 router weight is split exactly into three bf16
+//     terms (truncation: hi + mid + lo == w), so every product is exact.  Each
+//     16-wide k-step's three MFMAs start from zero and their small fp32 result
+//     is added into a float64 accumulator, so the only fp32 roundings are those
+//     of 16-term partial sums.  The 16 K-partials of a workgroup are summed in
+//     LDS in a fixed order and its float64 tile is written to the workspace,
+//     with the squared norms of the x rows and w rows.
+//  route_select: one wavefront per token.  Sums the KW partial tiles in a
+//     fixed order (deterministic), adds the bias, takes the top-k by
+//     wave-wide arg-max (larger logit first, lower id on ties).  If any other
+//     expert lies within a band of the k-th largest, every expert in the band
+//     is re-scored exactly in float64 and the top-k is re-taken over those
+//     scores.  The band, 36 eps32 ||x_t|| max_e ||w_e||, is twice a worst-case
+//     bound of the logit error (at most 18 fp32 roundings per k-step, each at
+//     most eps32 times that k-step's sum of |x_d w_d|, and sum_d |x_d w_d| <=
+//     ||x_t|| ||w_e|| by Cauchy-Schwarz), so the result is the float64
+//     selection at any input scale.  Gates are the softmax of the selected
+//     float64 scores.
 #include "moe_internal.h"
 
 namespace moe {
 
 constexpr int kRouteTokens = 32;
-constexpr int kRouteWaves = 8;
 constexpr double kBandRel = 36.0 * 5.9604644775390625e-8;     // 36 eps32
 
 __device__ inline uint32_t trunc_bf16_bits(float v) { return __float_as_uint(v) & 0xFFFF0000u; }
@@ -59,59 +64,91 @@ __device__ double score_f64(const uint16_t* __restrict__ xr, const float* __rest
   return wave_sum_f64(acc) + bias;
 }
 
-__global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(int T, int D, int E, int k,
-                                                                 const uint16_t* __restrict__ x,
-                                                                 const float* __restrict__ wr,
-                                                                 const float* __restrict__ br,
-                                                                 int32_t* __restrict__ out_idx,
-                                                                 float* __restrict__ out_w,
-                                                                 float* __restrict__ out_logits) {
-  __shared__ double part[kRouteWaves][kRouteTokens][33];   // per work item: [token][expert in tile]
-  __shared__ float wsq[kRouteWaves][32];                    // partial ||w_e||^2 per work item
-  __shared__ float xsq[kRouteWaves][kRouteTokens];          // partial ||x_t||^2 per work item
+// ---- work split and workspace layout (shared by the ABI layer) --------------------
+constexpr int kLogitWaves = 16;
+constexpr int kLogitBatch = 4;                 // k-steps whose loads are issued together
 
+static int route_kw(int T, int E) {
+  const int tiles = ((T + kRouteTokens - 1) / kRouteTokens) * ((E + 31) / 32);
+  return tiles <= 64 ? 4 : (tiles <= 256 ? 2 : 1);
+}
+
+struct RouteWs {
+  size_t logit, xsq, wsq, total;
+};
+
+static RouteWs route_ws_layout(int T, int E) {
+  const int KW = route_kw(T, E);
+  const size_t epad = (size_t)((E + 31) / 32) * 32;
+  RouteWs L;
+  L.logit = 0;
+  L.xsq = ((size_t)KW * T * epad * 8 + 255) / 256 * 256;
+  L.wsq = L.xsq + ((size_t)KW * T * 4 + 255) / 256 * 256;
+  L.total = L.wsq + ((size_t)KW * epad * 4 + 255) / 256 * 256;
+  return L;
+}
+
+size_t route_workspace_bytes(int T, int D, int E) {
+  (void)D;
+  return T > 0 ? route_ws_layout(T, E).total : 0;
+}
+
+__global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, int D, int E, int KW,
+                                                                         const uint16_t* __restrict__ x,
+                                                                         const float* __restrict__ wr,
+                                                                         double* __restrict__ logit,
+                                                                         float* __restrict__ xsq,
+                                                                         float* __restrict__ wsq) {
+  __shared__ double red[8][32][33];          // K-partials: waves 0..7, then 8..15 added in place
+  __shared__ float rsq[kLogitWaves][2][32];  // partial ||x_t||^2 (0) and ||w_e||^2 (1)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int t0 = blockIdx.x * kRouteTokens;
-  const int nte = (E + 31) / 32;                   // <= 8
-  const int KS = nte >= kRouteWaves ? 1 : kRouteWaves / nte;
-  const int items = nte * KS;
+  const int nte = (E + 31) / 32;
+  const int kw = blockIdx.x % KW;
+  const int nt = (blockIdx.x / KW) % nte;
+  const int tt = blockIdx.x / (KW * nte);
+  const int epad = nte * 32;
   const int nsteps = D / 16;
+  const int kstride = kLogitWaves * KW;
   const int row = lane & 31;
   const int half = lane >> 5;
-
-  // ---- 1. logits: work item (nt, ks) handles expert tile nt over k-steps ks, ks+KS, ... ----
-  if (wave < items) {
-    const int nt = wave / KS, ks = wave % KS;
-    const int e = nt * 32 + row;
-    const int tok = t0 + row;
-    const uint16_t* xa = x + (size_t)tok * D + 8 * half;
-    const float* wb = wr + (size_t)e * D + 8 * half;
-    double accd[16];
+  const int e = nt * 32 + row;
+  const int tok = tt * kRouteTokens + row;
+  const uint16_t* xa = x + (size_t)tok * D + 8 * half;
+  const float* wb = wr + (size_t)e * D + 8 * half;
+  double accd[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) accd[r] = 0.0;
-    float sq = 0.0f, xs = 0.0f;
-#pragma unroll 2
-    for (int s = ks; s < nsteps; s += KS) {
-      v8bf a = {};
-      if (tok < T) {
-        const uint4 u = *reinterpret_cast<const uint4*>(xa + 16 * s);
-        a = __builtin_bit_cast(v8bf, u);
-        const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+  for (int r = 0; r < 16; ++r) accd[r] = 0.0;
+  float sq = 0.0f, xs = 0.0f;
+  for (int s0 = kw * kLogitWaves + wave; s0 < nsteps; s0 += kLogitBatch * kstride) {
+    uint4 xu[kLogitBatch];
+    float4 wa[kLogitBatch], wc[kLogitBatch];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float lo = __uint_as_float(uw[i] << 16), hi = __uint_as_float(uw[i] & 0xFFFF0000u);
-          xs += lo * lo + hi * hi;
+    for (int b = 0; b < kLogitBatch; ++b) {
+      const int s = s0 + b * kstride;
+      xu[b] = make_uint4(0, 0, 0, 0);
+      wa[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      wc[b] = wa[b];
+      if (s < nsteps) {
+        if (tok < T) xu[b] = *reinterpret_cast<const uint4*>(xa + 16 * s);
+        if (e < E) {
+          wa[b] = *reinterpret_cast<const float4*>(wb + 16 * s);
+          wc[b] = *reinterpret_cast<const float4*>(wb + 16 * s + 4);
         }
       }
-      float wv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (e < E) {
-        const float4 w0 = *reinterpret_cast<const float4*>(wb + 16 * s);
-        const float4 w1 = *reinterpret_cast<const float4*>(wb + 16 * s + 4);
-        wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-        wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+    }
+#pragma unroll
+    for (int b = 0; b < kLogitBatch; ++b) {
+      if (s0 + b * kstride >= nsteps) break;             // uniform
+      const uint32_t uw[4] = {xu[b].x, xu[b].y, xu[b].z, xu[b].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(uw[i] << 16), hi = __uint_as_float(uw[i] & 0xFFFF0000u);
+        xs += lo * lo + hi * hi;
       }
+      const v8bf a = __builtin_bit_cast(v8bf, xu[b]);
+      const float wv[8] = {wa[b].x, wa[b].y, wa[b].z, wa[b].w, wc[b].x, wc[b].y, wc[b].z, wc[b].w};
       uint32_t hb[8], mb[8], lb[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -132,57 +169,137 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(int T, int D, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) accd[r] += (double)t[r];
     }
+  }
+  sq += __shfl_xor(sq, 32);
+  xs += __shfl_xor(xs, 32);
+  if (half == 0) {
+    rsq[wave][0][row] = xs;
+    rsq[wave][1][row] = sq;
+  }
+  // fixed-order reduction of the 16 K-partials: slot s = p_s + p_(s+8), then sum of the 8 slots
+  if (wave < 8) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part[wave][8 * (r >> 2) + 4 * half + (r & 3)][row] = accd[r];
-    sq += __shfl_xor(sq, 32);
-    xs += __shfl_xor(xs, 32);
-    if (half == 0) {
-      wsq[wave][row] = sq;
-      xsq[wave][row] = xs;
-    }
+    for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * half + (r & 3)][row] = accd[r];
   }
   __syncthreads();
-  // fixed-order sum of the K slices, in place into slice 0 of each tile
-  for (int j = tid; j < kRouteTokens * nte * 32; j += kRouteWaves * 64) {
-    const int m = j / (nte * 32), ec = j % (nte * 32), nt = ec >> 5, c = ec & 31;
-    double s = part[nt * KS][m][c];
-    for (int ks = 1; ks < KS; ++ks) s += part[nt * KS + ks][m][c];
-    part[nt * KS][m][c] = s;
+  if (wave >= 8) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave - 8][8 * (r >> 2) + 4 * half + (r & 3)][row] += accd[r];
   }
   __syncthreads();
+  double* lt = logit + ((size_t)kw * T + (size_t)tt * kRouteTokens) * epad + nt * 32;
+  for (int j = tid; j < 32 * 32; j += kLogitWaves * 64) {
+    const int m = j >> 5, c = j & 31;
+    double v = red[0][m][c];
+#pragma unroll
+    for (int s = 1; s < 8; ++s) v += red[s][m][c];
+    if (tt * kRouteTokens + m < T) lt[(size_t)m * epad + c] = v;
+  }
+  if (tid < 64) {
+    const int which = tid >> 5, r = tid & 31;
+    float v = 0.0f;
+    for (int w = 0; w < kLogitWaves; ++w) v += rsq[w][which][r];
+    if (which == 0 && nt == 0 && tt * kRouteTokens + r < T) xsq[(size_t)kw * T + tt * kRouteTokens + r] = v;
+    if (which == 1 && tt == 0) wsq[(size_t)kw * epad + nt * 32 + r] = v;
+  }
+}
 
-  // ---- 2./3. per-token selection -------------------------------------------------------
+__global__ __launch_bounds__(256) void route_select_kernel(int T, int D, int E, int k, int KW,
+                                                           const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ wr,
+                                                           const float* __restrict__ br,
+                                                           const double* __restrict__ logit,
+                                                           const float* __restrict__ xsq,
+                                                           const float* __restrict__ wsq,
+                                                           int32_t* __restrict__ out_idx, float* __restrict__ out_w,
+                                                           float* __restrict__ out_logits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                                     // no barriers in this kernel
+  const int epad = ((E + 31) / 32) * 32;
+
+  // partial tiles of the KW K-ranges are summed in a fixed order (KW <= 4)
   float wmax2 = 0.0f;
   for (int e = lane; e < E; e += 64) {
     float s = 0.0f;
-    for (int ks = 0; ks < KS; ++ks) s += wsq[(e >> 5) * KS + ks][e & 31];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < KW) s += wsq[(size_t)q * epad + e];
     wmax2 = fmaxf(wmax2, s);
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) wmax2 = fmaxf(wmax2, __shfl_xor(wmax2, d));
+  float xn2 = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < KW) xn2 += xsq[(size_t)q * T + t];
 
-  for (int i = wave; i < kRouteTokens; i += kRouteWaves) {
-    const int t = t0 + i;
-    if (t >= T) break;                                   // uniform per wave
-    float xn2 = 0.0f;
-    for (int ks = 0; ks < KS; ++ks) xn2 += xsq[ks][i];
-    double v[4];
+  double v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    double s = -INFINITY;
+    if (e < E) {
+      s = 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < KW) s += logit[((size_t)q * T + t) * epad + e];
+      s += (double)br[e];
+    }
+    v[c] = s;
+    if (out_logits && e < E) out_logits[(size_t)t * E + e] = (float)v[c];
+  }
+  // k rounds of arg-max; taken experts are excluded by a per-lane bit mask
+  uint32_t taken = 0;
+  double kth = 0.0;
+  for (int j = 0; j < k; ++j) {
+    double bv = -INFINITY;
+    int be = 0x7fffffff;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int e = lane + 64 * c;
-      v[c] = e < E ? part[(e >> 5) * KS][i][e & 31] + (double)br[e] : -INFINITY;
-      if (out_logits && e < E) out_logits[(size_t)t * E + e] = (float)v[c];
+      if (e < E && !(taken & (1u << c)) && (v[c] > bv || (v[c] == bv && e < be))) { bv = v[c]; be = e; }
     }
-    // k rounds of arg-max; taken experts are excluded by a per-lane bit mask
-    uint32_t taken = 0;
-    double kth = 0.0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const double ov = __shfl_xor(bv, d);
+      const int oe = __shfl_xor(be, d);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    kth = bv;
+  }
+  const double band = kBandRel * sqrt((double)xn2 * (double)wmax2);
+  bool cand[4];
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    cand[c] = e < E && ((taken & (1u << c)) || v[c] >= kth - band);
+    n += __popcll(__ballot(cand[c]));
+  }
+  if (n > k) {
+    // near the boundary: re-score every candidate exactly, then re-take the top-k
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint64_t m = __ballot(cand[c]);
+      while (m) {                                        // uniform loop over the candidate set
+        const int src = __ffsll((long long)m) - 1;
+        m &= m - 1;
+        const int e = src + 64 * c;
+        const double s = score_f64(x + (size_t)t * D, wr + (size_t)e * D, (double)br[e], D, lane);
+        if (lane == src) v[c] = s;
+      }
+      if (!cand[c]) v[c] = -INFINITY;
+    }
+    taken = 0;
     for (int j = 0; j < k; ++j) {
       double bv = -INFINITY;
       int be = 0x7fffffff;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int e = lane + 64 * c;
-        if (e < E && !(taken & (1u << c)) && (v[c] > bv || (v[c] == bv && e < be))) { bv = v[c]; be = e; }
+        if (cand[c] && !(taken & (1u << c)) && (v[c] > bv || (v[c] == bv && e < be))) { bv = v[c]; be = e; }
       }
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) {
@@ -191,82 +308,50 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(int T, int D, i
         if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
       }
       if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      kth = bv;
     }
-    const double band = kBandRel * sqrt((double)xn2 * (double)wmax2);
-    bool cand[4];
-    int n = 0;
+  }
+  // gates: softmax over the selected scores; slots in ascending expert id
+  double mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = lane + 64 * c;
-      cand[c] = e < E && ((taken & (1u << c)) || v[c] >= kth - band);
-      n += __popcll(__ballot(cand[c]));
+  for (int c = 0; c < 4; ++c)
+    if (taken & (1u << c)) mx = fmax(mx, v[c]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = fmax(mx, __shfl_xor(mx, d));
+  double ex[4], part_sum = 0.0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    ex[c] = (taken & (1u << c)) ? exp(v[c] - mx) : 0.0;
+    part_sum += ex[c];
+  }
+  const double sum = wave_sum_f64(part_sum);
+  int before = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint64_t m = __ballot((taken >> c) & 1u);
+    const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
+    if (taken & (1u << c)) {
+      out_idx[(size_t)t * k + slot] = lane + 64 * c;
+      out_w[(size_t)t * k + slot] = (float)(ex[c] / sum);
     }
-    if (n > k) {
-      // near the boundary: re-score every candidate exactly, then re-take the top-k
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint64_t m = __ballot(cand[c]);
-        while (m) {                                      // uniform loop over the candidate set
-          const int src = __ffsll((long long)m) - 1;
-          m &= m - 1;
-          const int e = src + 64 * c;
-          const double s = score_f64(x + (size_t)t * D, wr + (size_t)e * D, (double)br[e], D, lane);
-          if (lane == src) v[c] = s;
-        }
-        if (!cand[c]) v[c] = -INFINITY;
-      }
-      taken = 0;
-      for (int j = 0; j < k; ++j) {
-        double bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = lane + 64 * c;
-          if (cand[c] && !(taken & (1u << c)) && (v[c] > bv || (v[c] == bv && e < be))) { bv = v[c]; be = e; }
-        }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-          const double ov = __shfl_xor(bv, d);
-          const int oe = __shfl_xor(be, d);
-          if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      }
-    }
-    // gates: softmax over the selected scores; slots in ascending expert id
-    double mx = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (taken & (1u << c)) mx = fmax(mx, v[c]);
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) mx = fmax(mx, __shfl_xor(mx, d));
-    double ex[4], part_sum = 0.0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      ex[c] = (taken & (1u << c)) ? exp(v[c] - mx) : 0.0;
-      part_sum += ex[c];
-    }
-    const double sum = wave_sum_f64(part_sum);
-    int before = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint64_t m = __ballot((taken >> c) & 1u);
-      const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
-      if (taken & (1u << c)) {
-        out_idx[(size_t)t * k + slot] = lane + 64 * c;
-        out_w[(size_t)t * k + slot] = (float)(ex[c] / sum);
-      }
-      before += __popcll(m);
-    }
+    before += __popcll(m);
   }
 }
 
 hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
-                        int32_t* idx, float* w, float* logits, hipStream_t s) {
+                        int32_t* idx, float* w, float* logits, void* ws, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int blocks = (T + kRouteTokens - 1) / kRouteTokens;
-  route_kernel<<<dim3(blocks), dim3(kRouteWaves * 64), 0, s>>>(T, D, E, k, x, wr, br, idx, w, logits);
+  const RouteWs L = route_ws_layout(T, E);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  double* logit = reinterpret_cast<double*>(base + L.logit);
+  float* xsq = reinterpret_cast<float*>(base + L.xsq);
+  float* wsq = reinterpret_cast<float*>(base + L.wsq);
+  const int KW = route_kw(T, E);
+  const int tiles = ((T + kRouteTokens - 1) / kRouteTokens) * ((E + 31) / 32);
+  route_logits_kernel<<<dim3(tiles * KW), dim3(kLogitWaves * 64), 0, s>>>(T, D, E, KW, x, wr, logit, xsq, wsq);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  route_select_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq, idx, w,
+                                                              logits);
   return hipGetLastError();
 }
 

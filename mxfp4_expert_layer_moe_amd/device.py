@@ -11,7 +11,7 @@ import torch
 
 from . import (MOE_BF16, MOE_FP32, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, dims, moe_act_pack_bytes, moe_combine,
                moe_expert_gemm_mxfp4, moe_forward, moe_mxfp4_prepack, moe_pack_act, moe_permute, moe_route,
-               moe_weights, moe_workspace_bytes)
+               moe_route_workspace_bytes, moe_weights, moe_workspace_bytes)
 
 
 def _u8(a: np.ndarray, device) -> torch.Tensor:
@@ -72,11 +72,13 @@ class DeviceLayer:
         self.y32 = torch.empty((T, D), dtype=torch.float32, device=device)
         self.y16 = torch.empty((T, D), dtype=torch.bfloat16, device=device)
         self.ws = torch.empty(max(moe_workspace_bytes(self.dims, T), 256), dtype=torch.uint8, device=device)
+        self.route_ws = torch.empty(max(moe_route_workspace_bytes(self.dims, T), 256), dtype=torch.uint8,
+                                    device=device)
 
     # ---- step by step (the C entry points in order) ---------------------------
     def route(self, logits=True, stream=None):
         moe_route(self.dims, self.T, self.x, self.w_router, self.b_router, self.topk_idx, self.topk_w,
-                  self.logits if logits else None, stream)
+                  self.logits if logits else None, self.route_ws, None, stream)
 
     def permute(self, stream=None):
         moe_permute(self.dims, self.T, self.topk_idx, self.counts, self.offsets, self.perm, self.inv, stream)

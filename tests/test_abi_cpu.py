@@ -70,7 +70,7 @@ def test_bad_dims_rejected(L, bad, status):
     args = dict(d_model=2880, d_ff=2880, n_experts=32, top_k=4, swiglu_limit=7.0)
     args.update(bad)
     d = M.moe_dims(**args)
-    st = L.moe_route(ctypes.byref(d), 4, 16, 16, 16, 16, 16, None, None)
+    st = L.moe_route(ctypes.byref(d), 4, 16, 16, 16, 16, 16, None, 256, 1 << 30, None)
     assert st == status
     assert L.moe_workspace_bytes(ctypes.byref(d), 4) == 0
 
@@ -78,12 +78,17 @@ def test_bad_dims_rejected(L, bad, status):
 def test_bad_arguments_rejected_before_launch(L):
     d = ctypes.byref(D)
     A = 1 << 20                                   # fake, aligned, never dereferenced
-    assert L.moe_route(None, 4, A, A, A, A, A, None, None) == M.MOE_EINVAL
-    assert L.moe_route(d, -1, A, A, A, A, A, None, None) == M.MOE_EINVAL
-    assert L.moe_route(d, 1 << 22, A, A, A, A, A, None, None) == M.MOE_EUNSUPPORTED   # T*k >= 2^24
-    assert L.moe_route(d, 4, None, A, A, A, A, None, None) == M.MOE_EINVAL
-    assert L.moe_route(d, 4, A + 2, A, A, A, A, None, None) == M.MOE_EINVAL          # misaligned x
-    assert L.moe_route(d, 0, A, A, A, A, A, None, None) == M.MOE_OK                  # T = 0: no-op
+    R = L.moe_route_workspace_bytes(d, 4)
+    assert R > 0 and L.moe_route_workspace_bytes(d, 0) == 0
+    assert L.moe_route(None, 4, A, A, A, A, A, None, A, R, None) == M.MOE_EINVAL
+    assert L.moe_route(d, -1, A, A, A, A, A, None, A, R, None) == M.MOE_EINVAL
+    assert L.moe_route(d, 1 << 22, A, A, A, A, A, None, A, R, None) == M.MOE_EUNSUPPORTED   # T*k >= 2^24
+    assert L.moe_route(d, 4, None, A, A, A, A, None, A, R, None) == M.MOE_EINVAL
+    assert L.moe_route(d, 4, A + 2, A, A, A, A, None, A, R, None) == M.MOE_EINVAL          # misaligned x
+    assert L.moe_route(d, 4, A, A, A, A, A, None, None, R, None) == M.MOE_EINVAL           # no workspace
+    assert L.moe_route(d, 4, A, A, A, A, A, None, A + 16, R, None) == M.MOE_EINVAL         # misaligned ws
+    assert L.moe_route(d, 4, A, A, A, A, A, None, A, R - 1, None) == M.MOE_EWORKSPACE
+    assert L.moe_route(d, 0, A, A, A, A, A, None, None, 0, None) == M.MOE_OK               # T = 0: no-op
     assert L.moe_permute(d, 4, A, A, A, None, A, None) == M.MOE_EINVAL
     assert L.moe_permute(d, 0, A, A, A, A, A, None) == M.MOE_OK
     assert L.moe_pack_act(96, 4, A, A, None) == M.MOE_EUNSUPPORTED
