@@ -132,14 +132,20 @@ moe_status moe_route(const moe_dims* dims, int32_t T, const void* x_bf16, const 
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Group the T*top_k assignments by expert (deterministic, no atomics on order).
+ * Group the T*top_k assignments by expert (deterministic, no atomics on order)
+ * and cut every expert's rows into row tiles for the expert GEMMs.
  *   topk_idx  [T][top_k] int32, every entry in [0, n_experts)
  *   counts    out [n_experts]; offsets out [n_experts + 1] (exclusive prefix sum)
  *   perm      out [T*top_k]: assignment id at each grouped position
  *   inv       out [T*top_k]: inv[perm[p]] = p
+ *   tiles     out, moe_tile_table_bytes(dims, T) bytes, 16-byte aligned: the
+ *             row-tile table (per slot: expert or -1, first grouped position,
+ *             row count, then the assignment id of each row; 8-row tiles when
+ *             T*top_k <= 8*n_experts, else 32-row tiles)
  */
+size_t moe_tile_table_bytes(const moe_dims* dims, int32_t T);
 moe_status moe_permute(const moe_dims* dims, int32_t T, const int32_t* topk_idx, int32_t* counts,
-                       int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t stream);
+                       int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t stream);
 
 /*
  * Split bf16 rows into the packed hi/lo MX6 activation format above.
@@ -151,7 +157,7 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
 /*
  * Grouped expert GEMM on MXFP4 weights with the CDNA4 scaled FP4 matrix cores.
  *  MOE_STAGE_GATE_UP:
- *    a_packed  packed x, T rows of d_model (moe_pack_act output); row of
+ *    a_packed  packed x, T rows of d_model (moe_pack_act output); the row of
  *              grouped position p is token perm[p] / top_k
  *    codes/scales  prepacked gate/up weights (moe_mxfp4_prepack, stage GATE_UP)
  *    out       packed h, T*top_k rows of d_ff, row p = grouped position p, with
@@ -162,12 +168,12 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
  *    codes/scales  prepacked down weights (stage DOWN)
  *    topk_w    [T][top_k] fp32 gates; row p is scaled by topk_w[perm[p]]
  *    out       y_perm [T*top_k][d_model] fp32, row p = gate-weighted expert output
- *  perm/offsets are moe_permute's outputs.  Experts with no token are skipped
- *  (their weights are not read).
+ *  tiles is moe_permute's row-tile table for the same T.  Experts with no token
+ *  have no tile (their weights are not read).
  */
 moe_status moe_expert_gemm_mxfp4(const moe_dims* dims, int32_t T, moe_stage stage, const void* a_packed,
-                                 const int32_t* perm, const int32_t* offsets, const uint8_t* codes,
-                                 const uint8_t* scales, const float* topk_w, void* out, hipStream_t stream);
+                                 const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
+                                 const float* topk_w, void* out, hipStream_t stream);
 
 /*
  * Weighted combine: y[t] = sum over the token's slots j (ascending expert id)
@@ -180,7 +186,7 @@ moe_status moe_combine(const moe_dims* dims, int32_t T, const float* y_perm, con
 
 /*
  * The whole layer: route -> permute -> pack x -> gate/up + SwiGLU -> down ->
- * combine, six launches on `stream`, no host synchronisation.
+ * combine, enqueued on `stream` with no host synchronisation.
  *   ws / ws_bytes: device scratch of at least moe_workspace_bytes(dims, T)
  *   bytes, 256-byte aligned; its contents are undefined after the call.
  */

@@ -22,8 +22,9 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN = 0, 1
 
 # Symbols the header declares (checked by the CPU tests).
 EXPORTS = ("moe_status_str", "moe_act_pack_bytes", "moe_prepacked_codes_bytes", "moe_prepacked_scales_bytes",
-           "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_route", "moe_permute", "moe_pack_act", "moe_expert_gemm_mxfp4",
-           "moe_combine", "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_prepack")
+           "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes", "moe_route", "moe_permute",
+           "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine", "moe_forward", "moe_mxfp4_quantize",
+           "moe_mxfp4_prepack")
 
 
 class MoeError(RuntimeError):
@@ -61,13 +62,13 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_prepacked_codes_bytes", "moe_prepacked_scales_bytes"):
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, ctypes.c_int]
-        for name in ("moe_workspace_bytes", "moe_route_workspace_bytes"):
+        for name in ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes"):
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, i32]
         L.moe_route.argtypes = [dp, i32, vp, f32p, f32p, i32p, f32p, f32p, vp, sz, vp]
-        L.moe_permute.argtypes = [dp, i32, i32p, i32p, i32p, i32p, i32p, vp]
+        L.moe_permute.argtypes = [dp, i32, i32p, i32p, i32p, i32p, i32p, i32p, vp]
         L.moe_pack_act.argtypes = [i32, i32, vp, vp, vp]
-        L.moe_expert_gemm_mxfp4.argtypes = [dp, i32, ctypes.c_int, vp, i32p, i32p, vp, vp, f32p, vp, vp]
+        L.moe_expert_gemm_mxfp4.argtypes = [dp, i32, ctypes.c_int, vp, i32p, vp, vp, f32p, vp, vp]
         L.moe_combine.argtypes = [dp, i32, f32p, i32p, vp, ctypes.c_int, vp]
         L.moe_forward.argtypes = [dp, i32, vp, f32p, f32p, ctypes.POINTER(moe_weights), vp, ctypes.c_int, vp, sz, vp]
         L.moe_mxfp4_quantize.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
@@ -137,17 +138,21 @@ def moe_route(d, T, x, w_router, b_router, topk_idx, topk_w, logits, ws, ws_byte
                            _p(logits), _p(ws), ws_bytes, _s(stream)), "moe_route")
 
 
-def moe_permute(d, T, topk_idx, counts, offsets, perm, inv, stream=None):
+def moe_tile_table_bytes(d: moe_dims, T: int) -> int:
+    return lib().moe_tile_table_bytes(ctypes.byref(d), T)
+
+
+def moe_permute(d, T, topk_idx, counts, offsets, perm, inv, tiles, stream=None):
     _check(lib().moe_permute(ctypes.byref(d), T, _p(topk_idx), _p(counts), _p(offsets), _p(perm), _p(inv),
-                             _s(stream)), "moe_permute")
+                             _p(tiles), _s(stream)), "moe_permute")
 
 
 def moe_pack_act(K, rows, a, a_packed, stream=None):
     _check(lib().moe_pack_act(K, rows, _p(a), _p(a_packed), _s(stream)), "moe_pack_act")
 
 
-def moe_expert_gemm_mxfp4(d, T, stage, a_packed, perm, offsets, codes, scales, topk_w, out, stream=None):
-    _check(lib().moe_expert_gemm_mxfp4(ctypes.byref(d), T, stage, _p(a_packed), _p(perm), _p(offsets), _p(codes),
+def moe_expert_gemm_mxfp4(d, T, stage, a_packed, tiles, codes, scales, topk_w, out, stream=None):
+    _check(lib().moe_expert_gemm_mxfp4(ctypes.byref(d), T, stage, _p(a_packed), _p(tiles), _p(codes),
                                        _p(scales), _p(topk_w), _p(out), _s(stream)), "moe_expert_gemm_mxfp4")
 
 

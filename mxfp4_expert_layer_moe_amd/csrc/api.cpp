@@ -33,8 +33,12 @@ moe_status check_T(const moe_dims* d, int32_t T) {
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 struct WsLayout {
-  size_t idx, w, counts, offsets, perm, inv, xpack, hpack, yperm, route, total;
+  size_t idx, w, counts, offsets, perm, inv, tiles, xpack, hpack, yperm, route, total;
 };
+
+size_t tile_table_bytes(const moe_dims* d, int32_t T) {
+  return (size_t)tile_slots((long long)T * d->top_k, d->n_experts) * kTileInts * 4;
+}
 
 WsLayout ws_layout(const moe_dims* d, int32_t T) {
   WsLayout L;
@@ -47,6 +51,7 @@ WsLayout ws_layout(const moe_dims* d, int32_t T) {
   L.offsets = take(((size_t)d->n_experts + 1) * 4);
   L.perm = take(n * 4);
   L.inv = take(n * 4);
+  L.tiles = take(tile_table_bytes(d, T));
   L.xpack = take((size_t)T * act_row_bytes(d->d_model));
   L.hpack = take(n * act_row_bytes(d->d_ff));
   L.yperm = take(n * (size_t)d->d_model * 4);
@@ -115,17 +120,22 @@ moe_status moe_route(const moe_dims* d, int32_t T, const void* x_bf16, const flo
                                  b_router, topk_idx, topk_w, logits, ws, stream));
 }
 
+size_t moe_tile_table_bytes(const moe_dims* d, int32_t T) {
+  if (check_dims(d) != MOE_OK || check_T(d, T) != MOE_OK) return 0;
+  return tile_table_bytes(d, T);
+}
+
 moe_status moe_permute(const moe_dims* d, int32_t T, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
-                       int32_t* perm, int32_t* inv, hipStream_t stream) {
+                       int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t stream) {
   moe_status st = check_dims(d);
   if (st != MOE_OK) return st;
   if ((st = check_T(d, T)) != MOE_OK) return st;
-  if (!topk_idx || !counts || !offsets || !perm || !inv) return MOE_EINVAL;
+  if (!topk_idx || !counts || !offsets || !perm || !inv || !tiles) return MOE_EINVAL;
   if (!aligned(topk_idx, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) ||
-      !aligned(inv, 4))
+      !aligned(inv, 4) || !aligned(tiles, 16))
     return MOE_EINVAL;
   if (T == 0) return MOE_OK;
-  return hip_status(launch_permute(T, d->n_experts, d->top_k, topk_idx, counts, offsets, perm, inv, stream));
+  return hip_status(launch_permute(T, d->n_experts, d->top_k, topk_idx, counts, offsets, perm, inv, tiles, stream));
 }
 
 moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_packed, hipStream_t stream) {
@@ -137,21 +147,21 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
 }
 
 moe_status moe_expert_gemm_mxfp4(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed,
-                                 const int32_t* perm, const int32_t* offsets, const uint8_t* codes,
-                                 const uint8_t* scales, const float* topk_w, void* out, hipStream_t stream) {
+                                 const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
+                                 const float* topk_w, void* out, hipStream_t stream) {
   moe_status st = check_dims(d);
   if (st != MOE_OK) return st;
   if ((st = check_T(d, T)) != MOE_OK) return st;
   if (stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN) return MOE_EINVAL;
-  if (!a_packed || !perm || !offsets || !codes || !scales || !out) return MOE_EINVAL;
+  if (!a_packed || !tiles || !codes || !scales || !out) return MOE_EINVAL;
   if (stage == MOE_STAGE_DOWN && !topk_w) return MOE_EINVAL;
   if (!aligned(a_packed, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(out, 16) ||
-      !aligned(perm, 4) || !aligned(offsets, 4) || (topk_w && !aligned(topk_w, 4)))
+      !aligned(tiles, 16) || (topk_w && !aligned(topk_w, 4)))
     return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   return hip_status(launch_gemm(stage == MOE_STAGE_GATE_UP ? 0 : 1, T, d->d_model, d->d_ff, d->n_experts,
-                                d->top_k, d->swiglu_limit, (const uint8_t*)a_packed, perm, offsets, codes, scales,
-                                topk_w, out, stream));
+                                d->top_k, d->swiglu_limit, (const uint8_t*)a_packed, tiles, codes, scales, topk_w,
+                                out, stream));
 }
 
 moe_status moe_combine(const moe_dims* d, int32_t T, const float* y_perm, const int32_t* inv, void* y,
@@ -188,6 +198,7 @@ moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const f
   int32_t* offsets = (int32_t*)(base + L.offsets);
   int32_t* perm = (int32_t*)(base + L.perm);
   int32_t* inv = (int32_t*)(base + L.inv);
+  int32_t* tiles = (int32_t*)(base + L.tiles);
   uint8_t* xpack = base + L.xpack;
   uint8_t* hpack = base + L.hpack;
   float* yperm = (float*)(base + L.yperm);
@@ -196,13 +207,13 @@ moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const f
   if ((e = launch_route(T, D, E, k, (const uint16_t*)x_bf16, w_router, b_router, idx, w, nullptr, base + L.route,
                         stream)))
     return MOE_EHIP;
-  if ((e = launch_permute(T, E, k, idx, counts, offsets, perm, inv, stream))) return MOE_EHIP;
+  if ((e = launch_permute(T, E, k, idx, counts, offsets, perm, inv, tiles, stream))) return MOE_EHIP;
   if ((e = launch_pack(D, T, (const uint16_t*)x_bf16, xpack, stream))) return MOE_EHIP;
-  if ((e = launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, perm, offsets, wts->gu_codes, wts->gu_scales,
-                       nullptr, hpack, stream)))
+  if ((e = launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, tiles, wts->gu_codes, wts->gu_scales, nullptr,
+                       hpack, stream)))
     return MOE_EHIP;
-  if ((e = launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, perm, offsets, wts->dn_codes, wts->dn_scales, w,
-                       yperm, stream)))
+  if ((e = launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, tiles, wts->dn_codes, wts->dn_scales, w, yperm,
+                       stream)))
     return MOE_EHIP;
   if ((e = launch_combine(T, D, k, yperm, inv, y, y_dtype == MOE_BF16, stream))) return MOE_EHIP;
   return MOE_OK;

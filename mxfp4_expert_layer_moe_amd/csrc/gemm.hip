@@ -16,8 +16,8 @@
 // dword, byte `opsel`.  Result: lane l, register r holds row 8(r/4)+4(l/32)+r%4,
 // column l%32.
 //
-// Work decomposition: grid.y walks the 32-row tiles of every expert's rows
-// (located from `offsets` on the device; slots past the last tile exit), and
+// Work decomposition: grid.y walks the row tiles of every expert (the row-tile
+// table written by the permutation; empty slots exit), and
 // grid.x walks output units: a gate/up pair of 32-column tiles (stage 0) or
 // one 32-column tile (stage 1), one unit per wavefront.  Weights stream from
 // HBM once per (row tile, unit); a wavefront issues the loads of four k-tiles
@@ -30,47 +30,13 @@ struct GemmArgs {
   int T, k, E, K, KT, KG, units, out_K;
   float limit;
   const uint8_t* a_packed;
-  const int32_t* perm;
-  const int32_t* offsets;
+  const int32_t* tiles;
   const uint8_t* codes;
   const uint8_t* scales;
   const float* topk_w;
   void* out;
   size_t codes_per_expert, scales_per_expert;
 };
-
-// Locate row tile `mt` among all experts' tiles of bm rows.  Every lane gets the
-// expert, the first grouped position and the number of valid rows (<= bm).
-__device__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int bm, int mt, int& e_out, int& p0,
-                              int& nrows) {
-  const int lane = threadIdx.x & 63;
-  int before = 0;
-  for (int c = 0; c < E; c += 64) {
-    const int e = c + lane;
-    int off = 0, cnt = 0;
-    if (e < E) { off = offsets[e]; cnt = offsets[e + 1] - off; }
-    const int tiles = (cnt + bm - 1) / bm;
-    int incl = tiles;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    const int excl = incl - tiles;
-    const bool mine = e < E && mt >= before + excl && mt < before + incl;
-    const uint64_t m = __ballot(mine);
-    if (m) {
-      const int src = __ffsll((long long)m) - 1;
-      e_out = c + src;
-      const int lt = mt - before - __shfl(excl, src);
-      p0 = __shfl(off, src) + lt * bm;
-      nrows = min(bm, __shfl(cnt, src) - lt * bm);
-      return true;
-    }
-    before += __shfl(incl, 63);
-  }
-  return false;
-}
 
 constexpr int kAStageBytes = 36 * 1024;     // LDS for staged activation rows: 8 rows of K = 2880 fit whole
 
@@ -118,7 +84,10 @@ __host__ __device__ inline int stage_stride(int KC) { return (KC * 100 + 15) & ~
 // KTC: the number of 64-wide k-tiles when known at compile time (K = 2880 gives 45), else 0.
 // With KTC the whole K range is staged at once and the k-loop is fully unrolled, so the
 // weight ring is never drained at a loop back-edge.
-template <int STAGE, int P, int BM, int KTC>
+// ABUF: 2 reads the next k-tile's activations from LDS while the current one computes (costs
+// registers), 1 reads them at the start of each k-tile.  SB: with KTC, a scheduling barrier
+// after every SB k-tiles pins the refill loads in place.
+template <int STAGE, int P, int BM, int KTC, int ABUF, int SB = 1>
 __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   constexpr int NB = STAGE == 0 ? 2 : 1;
   static_assert(P % 4 == 0, "prefetch depth must cover whole scale groups");
@@ -131,16 +100,17 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u = blockIdx.x * 4 + wave;                  // output unit of this wavefront
   const bool active = u < g.units;                      // inactive waves still join the barriers
-  int e, p0, nrows;
-  if (!find_row_tile(g.offsets, g.E, BM, blockIdx.y, e, p0, nrows)) return;   // uniform per workgroup
-  e = __builtin_amdgcn_readfirstlane(e);
-  p0 = __builtin_amdgcn_readfirstlane(p0);
-  nrows = __builtin_amdgcn_readfirstlane(nrows);
+  const int32_t* tile = g.tiles + (size_t)blockIdx.y * kTileInts;
+  const int4 hdr = *reinterpret_cast<const int4*>(tile);
+  const int e = __builtin_amdgcn_readfirstlane(hdr.x);
+  if (e < 0) return;                                    // empty slot (uniform per workgroup)
+  const int p0 = __builtin_amdgcn_readfirstlane(hdr.y);
+  const int nrows = __builtin_amdgcn_readfirstlane(hdr.z);
 
   const int i = lane & 31;
   const int half = lane >> 5;
   const bool valid = i < nrows;
-  if (tid < nrows) srow[tid] = STAGE == 0 ? g.perm[p0 + tid] / g.k : p0 + tid;
+  if (tid < nrows) srow[tid] = STAGE == 0 ? tile[4 + tid] / g.k : p0 + tid;
 
   // K chunk staged at once: everything if it fits, else a multiple of the prefetch depth
   int KC = KTC > 0 ? KTC : g.KT;
@@ -229,15 +199,20 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       // with k-tile kt + P (address clamped to the last k-tile so there is no branch; a clamped
       // reload hits the cache).  The scheduling barrier keeps every refill where it is written,
       // so each wavefront keeps P k-tiles of weights in flight.
+      v8i ah[ABUF], al[ABUF];
+      uint32_t sh[ABUF], sl[ABUF];
+      if constexpr (ABUF == 2) lds_a(c0, ah[0], al[0], sh[0], sl[0]);
       auto step = [&](const int j, const int kt) {
-        v8i ah, al;
-        uint32_t sh, sl;
-        lds_a(kt, ah, al, sh, sl);
+        const int cur = ABUF == 2 ? (j & 1) : 0;
+        if constexpr (ABUF == 2)
+          lds_a(min(kt + 1, kend - 1), ah[cur ^ 1], al[cur ^ 1], sh[cur ^ 1], sl[cur ^ 1]);
+        else
+          lds_a(kt, ah[0], al[0], sh[0], sl[0]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const v8i bv = b_operand(bq[j][nb]);
-          acc[nb] = mma_sel(j & 3, ah, bv, acc[nb], sh, sbq[j >> 2][nb]);
-          acc[nb] = mma_sel(j & 3, al, bv, acc[nb], sl, sbq[j >> 2][nb]);
+          acc[nb] = mma_sel(j & 3, ah[cur], bv, acc[nb], sh[cur], sbq[j >> 2][nb]);
+          acc[nb] = mma_sel(j & 3, al[cur], bv, acc[nb], sl[cur], sbq[j >> 2][nb]);
         }
         const int kn = min(kt + P, g.KT - 1);
 #pragma unroll
@@ -247,7 +222,9 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) sbq[j >> 2][nb] = load_s(nb, grp);
         }
-        if constexpr (KTC > 0) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KTC > 0 && SB > 0) {
+          if (kt % SB == SB - 1) __builtin_amdgcn_sched_barrier(0);
+        }
       };
       if constexpr (KTC > 0) {
 #pragma unroll
@@ -272,8 +249,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     const size_t orb = act_row_bytes(I);
     uint8_t* out = reinterpret_cast<uint8_t*>(g.out);
     const int c = lane & 31;
+    // register r holds rows 8(r/4) + {0..7}; tiles of BM rows only fill r < BM/2, and row
+    // groups at or past nrows are skipped (uniform per wavefront)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < BM / 2; ++r) {
+      if (8 * (r >> 2) >= nrows) break;
       const int m = 8 * (r >> 2) + 4 * half + (r & 3);
       const float gv = fminf(fmaxf(acc[0][r], -g.limit), g.limit);
       const float uv = fminf(fmaxf(acc[1][r], -g.limit), g.limit);
@@ -285,10 +265,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp32
     const int D = g.units * kNTile;
     float wl = 0.0f;
-    if (valid) wl = g.topk_w[g.perm[p0 + i]];
+    if (valid) wl = g.topk_w[tile[4 + i]];
     float* out = reinterpret_cast<float*>(g.out);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < BM / 2; ++r) {
+      if (8 * (r >> 2) >= nrows) break;
       const int m = 8 * (r >> 2) + 4 * half + (r & 3);
       const float wm = __shfl(wl, m);
       if (m < nrows) out[(size_t)(p0 + m) * D + (size_t)u * kNTile + (lane & 31)] = acc[0][r] * wm;
@@ -297,12 +278,12 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 }
 
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
-                       const int32_t* perm, const int32_t* offsets, const uint8_t* codes, const uint8_t* scales,
-                       const float* topk_w, void* out, hipStream_t s) {
+                       const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
+                       void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   GemmArgs g;
   g.T = T; g.k = k; g.E = E; g.limit = limit;
-  g.a_packed = a_packed; g.perm = perm; g.offsets = offsets; g.codes = codes; g.scales = scales;
+  g.a_packed = a_packed; g.tiles = tiles; g.codes = codes; g.scales = scales;
   g.topk_w = topk_w; g.out = out;
   const int N = stage == 0 ? 2 * I : D;
   g.K = stage == 0 ? D : I;
@@ -314,21 +295,19 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   g.scales_per_expert = w_scales_per_expert(N, g.K);
   const long long n_assign = (long long)T * k;
   // decode-sized batches (few rows per expert): 8-row tiles whose activations fit LDS whole;
-  // otherwise 32-row tiles (one full MFMA tile) with K staged in chunks
-  const bool small = n_assign <= 8LL * E;
-  const int bm = small ? 8 : kMTile;
-  const unsigned tiles_y = (unsigned)((n_assign + bm - 1) / bm + (E < n_assign ? E : n_assign));
-  const dim3 grid((g.units + 3) / 4, tiles_y);
+  // otherwise 32-row tiles (one full MFMA tile) with K staged in chunks.  Same rule as the table.
+  const bool small = tile_rows(n_assign, E) == 8;
+  const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));
   // the model's K = 2880 (45 k-tiles) with decode tiles: fully unrolled k-loop
   const bool k45 = g.KT == 45 && small && 8 * stage_stride(45) <= kAStageBytes;
   if (stage == 0) {
-    if (k45) expert_gemm_kernel<0, 8, 8, 45><<<grid, dim3(256), 0, s>>>(g);
-    else if (small) expert_gemm_kernel<0, 8, 8, 0><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_kernel<0, 8, kMTile, 0><<<grid, dim3(256), 0, s>>>(g);
+    if (k45) expert_gemm_kernel<0, 8, 8, 45, 1><<<grid, dim3(256), 0, s>>>(g);
+    else if (small) expert_gemm_kernel<0, 8, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<0, 8, kMTile, 0, 1><<<grid, dim3(256), 0, s>>>(g);
   } else {
-    if (k45) expert_gemm_kernel<1, 16, 8, 45><<<grid, dim3(256), 0, s>>>(g);
-    else if (small) expert_gemm_kernel<1, 16, 8, 0><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_kernel<1, 8, kMTile, 0><<<grid, dim3(256), 0, s>>>(g);
+    if (k45) expert_gemm_kernel<1, 16, 8, 45, 2><<<grid, dim3(256), 0, s>>>(g);
+    else if (small) expert_gemm_kernel<1, 16, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<1, 8, kMTile, 0, 1><<<grid, dim3(256), 0, s>>>(g);
   }
   return hipGetLastError();
 }

@@ -47,6 +47,20 @@ __host__ __device__ inline size_t w_scales_per_expert(int N, int K) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-tile table (written by the permutation, read by the expert GEMMs): the
+// grouped rows of every expert are cut into tiles of tile_rows() rows; slot s
+// holds {expert (-1 = empty slot), first grouped position p0, rows, 0} and then,
+// for each row i < rows, the assignment id perm[p0 + i].  Decode-sized batches
+// (at most 8 rows per expert on average) use 8-row tiles, larger ones 32.
+// ---------------------------------------------------------------------------
+constexpr int kTileInts = 48;      // 4 header ints + up to 32 assignment ids, padded to 192 bytes
+__host__ __device__ inline int tile_rows(long long n_assign, int E) { return n_assign <= 8LL * E ? 8 : 32; }
+__host__ __device__ inline long long tile_slots(long long n_assign, int E) {
+  const int bm = tile_rows(n_assign, E);
+  return (n_assign + bm - 1) / bm + (E < n_assign ? E : n_assign);
+}
+
+// ---------------------------------------------------------------------------
 // FP6 E2M3 encoding of v / 2^e (round to nearest even, saturate at 7.5).
 // Returns the 6-bit code; *dec receives the decoded value times 2^e.
 // ---------------------------------------------------------------------------
@@ -145,11 +159,11 @@ hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const flo
                         int32_t* idx, float* w, float* logits, void* ws, hipStream_t s);
 size_t route_workspace_bytes(int T, int D, int E);
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, int32_t* inv, hipStream_t s);
+                          int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s);
 hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipStream_t s);
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
-                       const int32_t* perm, const int32_t* offsets, const uint8_t* codes,
-                       const uint8_t* scales, const float* topk_w, void* out, hipStream_t s);
+                       const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
+                       void* out, hipStream_t s);
 hipError_t launch_combine(int T, int D, int k, const float* y_perm, const int32_t* inv, void* y,
                           int y_bf16, hipStream_t s);
 

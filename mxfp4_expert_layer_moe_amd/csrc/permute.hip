@@ -8,6 +8,10 @@
 // The result is unique and deterministic: positions come from counts and
 // in-order ranks, never from the order in which atomics land.
 //
+// It also writes the row-tile table the expert GEMMs start from (expert, first
+// row, row count and the assignment id of every row of each tile), so a GEMM
+// workgroup learns everything about its rows with one load.
+//
 // One workgroup of 1024 threads walks the assignments in chunks of 1024 (each
 // thread keeps its assignments in registers).  Within a wavefront, a thread's
 // rank among equal experts comes from a ballot-based match (one ballot per
@@ -21,13 +25,17 @@ constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kPermRegs = 32;          // assignments held per thread per pass
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, const int32_t* __restrict__ idx,
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, int bm, int slots,
+                                                               const int32_t* __restrict__ idx,
                                                                int32_t* __restrict__ counts,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ perm,
-                                                               int32_t* __restrict__ inv) {
+                                                               int32_t* __restrict__ inv,
+                                                               int32_t* __restrict__ tiles) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int base[kMaxExperts];
+  __shared__ int off0[kMaxExperts];
+  __shared__ int tstart[kMaxExperts + 1];
   __shared__ int wcnt[kPermWaves][kMaxExperts];
 
   const int tid = threadIdx.x;
@@ -59,14 +67,44 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, con
       }
       if (e < E) {
         base[e] = carry + incl - v;
+        off0[e] = carry + incl - v;
         counts[e] = v;
         offsets[e] = carry + incl - v;
       }
       carry += __shfl(incl, 63);
     }
     if (lane == 0) offsets[E] = carry;
+    // first tile slot of every expert
+    int tcarry = 0;
+    for (int c = 0; c < E; c += 64) {
+      const int e = c + lane;
+      const int v = e < E ? (cnt[e] + bm - 1) / bm : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      if (e < E) tstart[e] = tcarry + incl - v;
+      tcarry += __shfl(incl, 63);
+    }
+    if (lane == 0) tstart[E] = tcarry;
   }
   __syncthreads();
+  // tile headers: slot s of expert e (binary search over tstart); slots past the last tile are empty
+  for (int s = tid; s < slots; s += kPermThreads) {
+    int4 h = make_int4(-1, 0, 0, 0);
+    if (s < tstart[E]) {
+      int lo = 0, hi = E - 1;                       // largest e with tstart[e] <= s
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tstart[mid] <= s) lo = mid; else hi = mid - 1;
+      }
+      const int t = s - tstart[lo];
+      h = make_int4(lo, off0[lo] + t * bm, min(bm, cnt[lo] - t * bm), 0);
+    }
+    *reinterpret_cast<int4*>(tiles + (size_t)s * kTileInts) = h;
+  }
 
   // ---- stable scatter, chunk by chunk --------------------------------------
   const int nchunks = (n + kPermThreads - 1) / kPermThreads;
@@ -100,6 +138,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, con
         for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
         perm[pos] = a;
         inv[a] = pos;
+        const int r = pos - off0[e];
+        tiles[(size_t)(tstart[e] + r / bm) * kTileInts + 4 + r % bm] = a;
       }
       __syncthreads();
       for (int e2 = tid; e2 < E; e2 += kPermThreads) {
@@ -113,9 +153,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, con
 }
 
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, int32_t* inv, hipStream_t s) {
+                          int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s) {
   const int n = T * k;
-  permute_kernel<<<dim3(1), dim3(kPermThreads), 0, s>>>(n, E, idx, counts, offsets, perm, inv);
+  permute_kernel<<<dim3(1), dim3(kPermThreads), 0, s>>>(n, E, tile_rows(n, E), (int)tile_slots(n, E), idx, counts,
+                                                        offsets, perm, inv, tiles);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ import torch
 
 from . import (MOE_BF16, MOE_FP32, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, dims, moe_act_pack_bytes, moe_combine,
                moe_expert_gemm_mxfp4, moe_forward, moe_mxfp4_prepack, moe_pack_act, moe_permute, moe_route,
-               moe_route_workspace_bytes, moe_weights, moe_workspace_bytes)
+               moe_route_workspace_bytes, moe_tile_table_bytes, moe_weights, moe_workspace_bytes)
 
 
 def _u8(a: np.ndarray, device) -> torch.Tensor:
@@ -66,6 +66,7 @@ class DeviceLayer:
         self.offsets = torch.empty(E + 1, **i32)
         self.perm = torch.empty(n, **i32)
         self.inv = torch.empty(n, **i32)
+        self.tiles = torch.empty(max(moe_tile_table_bytes(self.dims, T) // 4, 4), **i32)
         self.x_packed = torch.empty(max(moe_act_pack_bytes(D, T), 16), dtype=torch.uint8, device=device)
         self.h_packed = torch.empty(max(moe_act_pack_bytes(I, n), 16), dtype=torch.uint8, device=device)
         self.y_perm = torch.empty((n, D), dtype=torch.float32, device=device)
@@ -81,20 +82,21 @@ class DeviceLayer:
                   self.logits if logits else None, self.route_ws, None, stream)
 
     def permute(self, stream=None):
-        moe_permute(self.dims, self.T, self.topk_idx, self.counts, self.offsets, self.perm, self.inv, stream)
+        moe_permute(self.dims, self.T, self.topk_idx, self.counts, self.offsets, self.perm, self.inv, self.tiles,
+                    stream)
 
     def pack_x(self, stream=None):
         moe_pack_act(self.D, self.T, self.x, self.x_packed, stream)
 
     def gate_up(self, weights: DeviceWeights | None = None, stream=None):
         w = weights or self.weights
-        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_GATE_UP, self.x_packed, self.perm, self.offsets,
-                              w.gu_codes, w.gu_scales, None, self.h_packed, stream)
+        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_GATE_UP, self.x_packed, self.tiles, w.gu_codes,
+                              w.gu_scales, None, self.h_packed, stream)
 
     def down(self, weights: DeviceWeights | None = None, stream=None):
         w = weights or self.weights
-        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_DOWN, self.h_packed, self.perm, self.offsets,
-                              w.dn_codes, w.dn_scales, self.topk_w, self.y_perm, stream)
+        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_DOWN, self.h_packed, self.tiles, w.dn_codes,
+                              w.dn_scales, self.topk_w, self.y_perm, stream)
 
     def combine(self, bf16=False, stream=None):
         moe_combine(self.dims, self.T, self.y_perm, self.inv, self.y16 if bf16 else self.y32,

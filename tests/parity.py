@@ -20,12 +20,28 @@ def run_gpu(layer, stream=None) -> dict:
     T, k = layer.T, layer.k
     r = dict(idx=layer.topk_idx.cpu().numpy(), w=layer.topk_w.cpu().numpy(), logits=layer.logits.cpu().numpy(),
              counts=layer.counts.cpu().numpy(), offsets=layer.offsets.cpu().numpy(),
-             perm=layer.perm.cpu().numpy(), inv=layer.inv.cpu().numpy(),
+             perm=layer.perm.cpu().numpy(), inv=layer.inv.cpu().numpy(), tiles=layer.tiles.cpu().numpy(),
              x_packed=layer.x_packed.cpu().numpy(), h_packed=layer.h_packed.cpu().numpy(),
              y_perm=layer.y_perm.cpu().numpy(), y32=layer.y32.cpu().numpy(),
              y16=layer.y16.view(torch.int16).cpu().numpy().view(np.uint16))
     assert r["idx"].shape == (T, k)
     return r
+
+
+def check_tiles(tiles: np.ndarray, offsets: np.ndarray, perm: np.ndarray, n: int, E: int):
+    """The row-tile table (include/moe_mxfp4.h): every expert's grouped rows cut into tiles of
+    8 rows (n <= 8E) or 32 rows, in expert order, each listing its assignment ids; then empty slots."""
+    bm = 8 if n <= 8 * E else 32
+    slots = -(-n // bm) + min(E, n)
+    t = tiles.reshape(-1, 48)[:slots]
+    s = 0
+    for e in range(E):
+        for p0 in range(int(offsets[e]), int(offsets[e + 1]), bm):
+            rows = min(bm, int(offsets[e + 1]) - p0)
+            assert list(t[s, :3]) == [e, p0, rows], (s, t[s, :4], e, p0, rows)
+            assert np.array_equal(t[s, 4:4 + rows], perm[p0:p0 + rows])
+            s += 1
+    assert np.all(t[s:, 0] == -1)
 
 
 def rne_bf16_bits(y32: np.ndarray) -> np.ndarray:
@@ -70,6 +86,7 @@ def compare(inp, g: dict, o: dict, check_h: bool = True) -> dict:
     assert np.array_equal(g["offsets"], o["offsets"])
     assert np.array_equal(g["perm"], o["perm"])
     assert np.array_equal(g["inv"], o["inv"])
+    check_tiles(g["tiles"], o["offsets"], o["perm"], T * k, inp.E)
     dw = np.abs(g["w"].astype(np.float64) - o["w"]).max()
     stats["max_dw"] = float(dw)
     assert dw <= TOL_W, dw

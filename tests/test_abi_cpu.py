@@ -89,15 +89,21 @@ def test_bad_arguments_rejected_before_launch(L):
     assert L.moe_route(d, 4, A, A, A, A, A, None, A + 16, R, None) == M.MOE_EINVAL         # misaligned ws
     assert L.moe_route(d, 4, A, A, A, A, A, None, A, R - 1, None) == M.MOE_EWORKSPACE
     assert L.moe_route(d, 0, A, A, A, A, A, None, None, 0, None) == M.MOE_OK               # T = 0: no-op
-    assert L.moe_permute(d, 4, A, A, A, None, A, None) == M.MOE_EINVAL
-    assert L.moe_permute(d, 0, A, A, A, A, A, None) == M.MOE_OK
+    assert L.moe_permute(d, 4, A, A, A, None, A, A, None) == M.MOE_EINVAL
+    assert L.moe_permute(d, 4, A, A, A, A, A, None, None) == M.MOE_EINVAL             # no tile table
+    assert L.moe_permute(d, 4, A, A, A, A, A, A + 4, None) == M.MOE_EINVAL            # misaligned tiles
+    assert L.moe_permute(d, 0, A, A, A, A, A, A, None) == M.MOE_OK
+    # tile table: 8-row tiles at decode sizes, 32-row tiles beyond 8 rows per expert on average
+    assert L.moe_tile_table_bytes(d, 32) == (128 // 8 + 32) * 192
+    assert L.moe_tile_table_bytes(d, 4096) == (16384 // 32 + 32) * 192
     assert L.moe_pack_act(96, 4, A, A, None) == M.MOE_EUNSUPPORTED
     assert L.moe_pack_act(64, 4, A, A + 8, None) == M.MOE_EINVAL
     assert L.moe_pack_act(64, 0, A, A, None) == M.MOE_OK
-    assert L.moe_expert_gemm_mxfp4(d, 4, 7, A, A, A, A, A, A, A, None) == M.MOE_EINVAL
-    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, A, None, A, None) == M.MOE_EINVAL
-    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_GATE_UP, A, A, A, A + 4, A, None, A, None) == M.MOE_EINVAL
-    assert L.moe_expert_gemm_mxfp4(d, 0, M.MOE_STAGE_GATE_UP, A, A, A, A, A, None, A, None) == M.MOE_OK
+    assert L.moe_expert_gemm_mxfp4(d, 4, 7, A, A, A, A, A, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_GATE_UP, A, A, A + 4, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_GATE_UP, A, A + 8, A, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4(d, 0, M.MOE_STAGE_GATE_UP, A, A, A, A, None, A, None) == M.MOE_OK
     assert L.moe_combine(d, 4, A, A, A, 5, None) == M.MOE_EINVAL
     assert L.moe_combine(d, 4, A, A, A + 4, M.MOE_FP32, None) == M.MOE_EINVAL
     w = M.moe_weights(A, A, A, A)

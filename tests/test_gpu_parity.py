@@ -117,11 +117,16 @@ def test_identity_activation_probe_down_gemm_is_exact():
     hb = torch.from_numpy(synth.f32_to_bf16_bits(h).view(np.int16)).to(dev).view(torch.bfloat16)
     hp = torch.empty(M.moe_act_pack_bytes(I, I), dtype=torch.uint8, device=dev)
     M.moe_pack_act(I, I, hb, hp)
-    perm = torch.arange(I, dtype=torch.int32, device=dev)
-    offsets = torch.tensor([0, I], dtype=torch.int32, device=dev)
+    # one expert, k = 1: every token routes to expert 0, so row p of y is token p (32-row tiles)
+    idx = torch.zeros((I, 1), dtype=torch.int32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts, offsets = torch.empty(1, **i32), torch.empty(2, **i32)
+    perm, inv = torch.empty(I, **i32), torch.empty(I, **i32)
+    tiles = torch.empty(M.moe_tile_table_bytes(d, I) // 4, **i32)
+    M.moe_permute(d, I, idx, counts, offsets, perm, inv, tiles)
     w = torch.ones(I, dtype=torch.float32, device=dev)
     y = torch.empty((I, D), dtype=torch.float32, device=dev)
-    M.moe_expert_gemm_mxfp4(d, I, M.MOE_STAGE_DOWN, hp, perm, offsets, torch.from_numpy(dc).to(dev),
+    M.moe_expert_gemm_mxfp4(d, I, M.MOE_STAGE_DOWN, hp, tiles, torch.from_numpy(dc).to(dev),
                             torch.from_numpy(ds).to(dev), w, y)
     torch.cuda.synchronize()
     from tests import actpack
