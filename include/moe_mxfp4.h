@@ -39,12 +39,13 @@
  * The expert GEMMs consume activations that are already split into two MX
  * terms, hi + lo, each stored as FP6 E2M3 codes with one E8M0 scale per 32
  * values; hi + lo reproduces a bf16 row to about 2^-9 of its block maximum.
- * One packed row of K values (K % 64 == 0) is moe_act_pack_bytes(K, 1) bytes:
- *     [hi codes : K/32 blocks x 24 B][lo codes : K/32 blocks x 24 B]
- *     [hi scales: 2 x KTp B][lo scales: 2 x KTp B]        KTp = roundup(K/64, 4)
- * Block b's 32 codes are 6-bit fields packed little-endian (element i at bits
- * 6i..6i+5); E2M3 = sign | 2 exponent bits (bias 1) | 3 mantissa bits.  The
- * scale of block b sits at index [b % 2][b / 2] of its 2 x KTp array.
+ * One packed row of K values (K % 64 == 0) is moe_act_pack_bytes(K, 1) = (K/64) * 112
+ * bytes: one 112-byte chunk per 64-wide k-tile kt, holding
+ *     [0,24) hi codes of block 2kt    [24,48) hi codes of block 2kt+1
+ *     [48,72) lo codes of block 2kt   [72,96) lo codes of block 2kt+1
+ *     [96],[97] hi scales of blocks 2kt, 2kt+1   [98],[99] lo scales   [100,112) unused
+ * A block's 32 codes are 6-bit fields packed little-endian (element i at bits
+ * 6i..6i+5); E2M3 = sign | 2 exponent bits (bias 1) | 3 mantissa bits.
  *
  * Prepacked weight format
  * -----------------------

@@ -204,11 +204,9 @@ moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const f
   float* yperm = (float*)(base + L.yperm);
   const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
   hipError_t e;
-  if ((e = launch_route(T, D, E, k, (const uint16_t*)x_bf16, w_router, b_router, idx, w, nullptr, base + L.route,
-                        stream)))
+  if ((e = launch_route_front(T, D, E, k, (const uint16_t*)x_bf16, w_router, b_router, idx, w, base + L.route, xpack,
+                              counts, offsets, perm, inv, tiles, stream)))
     return MOE_EHIP;
-  if ((e = launch_permute(T, E, k, idx, counts, offsets, perm, inv, tiles, stream))) return MOE_EHIP;
-  if ((e = launch_pack(D, T, (const uint16_t*)x_bf16, xpack, stream))) return MOE_EHIP;
   if ((e = launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, tiles, wts->gu_codes, wts->gu_scales, nullptr,
                        hpack, stream)))
     return MOE_EHIP;

@@ -38,7 +38,7 @@ struct GemmArgs {
   size_t codes_per_expert, scales_per_expert;
 };
 
-constexpr int kAStageBytes = 36 * 1024;     // LDS for staged activation rows: 8 rows of K = 2880 fit whole
+constexpr int kAStageBytes = 40 * 1024;     // LDS for staged activation rows: 8 rows of K = 2880 fit whole
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -77,9 +77,8 @@ __device__ inline v8i a_operand_lds(const uint8_t* p) {      // 24 bytes, 8-byte
   return v;
 }
 
-// Staged row layout in LDS (per tile row, stride rs = roundup(100 * KC, 16) bytes):
-//   [hi codes KC x 48][lo codes KC x 48][hi scales: half 0 KC, half 1 KC][lo scales: 2 x KC]
-__host__ __device__ inline int stage_stride(int KC) { return (KC * 100 + 15) & ~15; }
+// Staged rows in LDS: the packed row's chunks for k-tiles [c0, c0 + KC), row stride KC * 112 bytes.
+__host__ __device__ inline int stage_stride(int KC) { return KC * kActChunk; }
 
 // KTC: the number of 64-wide k-tiles when known at compile time (K = 2880 gives 45), else 0.
 // With KTC the whole K range is staged at once and the k-loop is fully unrolled, so the
@@ -91,7 +90,7 @@ template <int STAGE, int P, int BM, int KTC, int ABUF, int SB = 1>
 __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   constexpr int NB = STAGE == 0 ? 2 : 1;
   static_assert(P % 4 == 0, "prefetch depth must cover whole scale groups");
-  static_assert(BM <= kMTile && BM * 100 * P <= kAStageBytes, "a chunk of P k-tiles must fit for BM rows");
+  static_assert(BM <= kMTile && BM * kActChunk * P <= kAStageBytes, "a chunk of P k-tiles must fit for BM rows");
   __shared__ __attribute__((aligned(16))) uint8_t sA[kAStageBytes];
   __shared__ int srow[BM];
 
@@ -114,11 +113,9 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 
   // K chunk staged at once: everything if it fits, else a multiple of the prefetch depth
   int KC = KTC > 0 ? KTC : g.KT;
-  if (KTC == 0 && nrows * stage_stride(KC) > kAStageBytes) KC = (kAStageBytes / (nrows * 100)) / P * P;
+  if (KTC == 0 && nrows * stage_stride(KC) > kAStageBytes) KC = (kAStageBytes / (nrows * kActChunk)) / P * P;
   const int rs = stage_stride(KC);
   const size_t arb = act_row_bytes(g.K);
-  const size_t lo_off = act_lo_codes_off(g.K);
-  const int ktp = act_ktp(g.K);
 
   // this expert's weights as buffer resources; tile q starts at q*KT k-tiles (codes) / q*KG groups (scales)
   const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(g.codes + (size_t)e * g.codes_per_expert,
@@ -165,18 +162,12 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   for (int c0 = 0; c0 < g.KT; c0 += KC) {
     const int kcn = min(KC, g.KT - c0);
     __syncthreads();                                    // previous chunk consumed; srow visible
-    // stage rows [0, nrows) x k-tiles [c0, c0 + kcn): codes as 16-byte words, scales as bytes
-    const int n16 = kcn * 3;                            // 16-byte words per term per row
-    for (int w = tid; w < nrows * 2 * n16; w += 256) {
-      const int r = w / (2 * n16), rem = w - r * 2 * n16, term = rem / n16, o = rem - term * n16;
-      const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + term * lo_off + (size_t)c0 * 48 + (size_t)o * 16;
-      *reinterpret_cast<uint4*>(sA + r * rs + term * KC * 48 + o * 16) = *reinterpret_cast<const uint4*>(src);
-    }
-    for (int w = tid; w < nrows * 4 * kcn; w += 256) {
-      const int r = w / (4 * kcn), rem = w - r * 4 * kcn, arr = rem / kcn, j = rem - arr * kcn;
-      // arr: 0 = hi half 0, 1 = hi half 1, 2 = lo half 0, 3 = lo half 1
-      const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + act_hi_scales_off(g.K) + (size_t)arr * ktp + c0 + j;
-      sA[r * rs + KC * 96 + arr * KC + j] = *src;
+    // stage rows [0, nrows) x k-tiles [c0, c0 + kcn): contiguous chunks, 16-byte words
+    const int n16 = kcn * (kActChunk / 16);
+    for (int w = tid; w < nrows * n16; w += 256) {
+      const int r = w / n16, o = w - r * n16;
+      const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + (size_t)c0 * kActChunk + (size_t)o * 16;
+      *reinterpret_cast<uint4*>(sA + r * rs + o * 16) = *reinterpret_cast<const uint4*>(src);
     }
     __syncthreads();
     if (active) {
@@ -184,11 +175,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       const int kend = c0 + kcn;
       // A operands of k-tile kt from LDS; rows past nrows read stale bytes and are masked to zero
       auto lds_a = [&](const int kt, v8i& hi, v8i& lo, uint32_t& sh, uint32_t& sl) {
-        const int kl = kt - c0;
-        hi = a_operand_lds(arow + kl * 48 + half * 24);
-        lo = a_operand_lds(arow + KC * 48 + kl * 48 + half * 24);
-        sh = arow[KC * 96 + half * KC + kl];
-        sl = arow[KC * 96 + (2 + half) * KC + kl];
+        const uint8_t* chunk = arow + (kt - c0) * kActChunk;
+        hi = a_operand_lds(chunk + half * 24);
+        lo = a_operand_lds(chunk + 48 + half * 24);
+        sh = chunk[96 + half];
+        sl = chunk[98 + half];
         const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
         hi = valid ? hi : z;
         lo = valid ? lo : z;
@@ -259,7 +250,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       const float uv = fminf(fmaxf(acc[1][r], -g.limit), g.limit);
       const float h = bf16_round(gv / (1.0f + expf(-gv)) * uv);
       const Split32 sp = split_block32(h, c);
-      if (m < nrows) store_split32(out + (size_t)(p0 + m) * orb, I, u, c, sp);
+      if (m < nrows) store_split32(out + (size_t)(p0 + m) * orb, u, c, sp);
     }
   } else {
     // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp32
@@ -299,7 +290,7 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   const bool small = tile_rows(n_assign, E) == 8;
   const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));
   // the model's K = 2880 (45 k-tiles) with decode tiles: fully unrolled k-loop
-  const bool k45 = g.KT == 45 && small && 8 * stage_stride(45) <= kAStageBytes;
+  const bool k45 = g.KT == 45 && small && 8 * stage_stride(45) <= kAStageBytes;   // 40320 <= 40960
   if (stage == 0) {
     if (k45) expert_gemm_kernel<0, 8, 8, 45, 1><<<grid, dim3(256), 0, s>>>(g);
     else if (small) expert_gemm_kernel<0, 8, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);

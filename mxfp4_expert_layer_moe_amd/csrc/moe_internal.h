@@ -20,18 +20,15 @@ constexpr int kMaxExperts = 256;
 
 // ---------------------------------------------------------------------------
 // Packed activation rows ("split MX6"): hi and lo FP6 E2M3 terms per 32-block.
-//   [hi codes K/32 x 24 B][lo codes K/32 x 24 B][hi scales 2 x KTp][lo scales 2 x KTp]
+// A row of K values is K/64 chunks of 112 bytes, one per 64-wide k-tile kt:
+//   [0,24) hi codes of block 2kt   [24,48) hi codes of block 2kt+1
+//   [48,72) lo codes of block 2kt  [72,96) lo codes of block 2kt+1
+//   [96] [97] hi scales of blocks 2kt, 2kt+1   [98] [99] lo scales   [100,112) unused
+// so one 16-byte-aligned chunk holds everything a k-tile of the GEMM reads.
 // ---------------------------------------------------------------------------
+constexpr int kActChunk = 112;
 __host__ __device__ inline int act_ktiles(int K) { return K / kKTile; }
-__host__ __device__ inline int act_ktp(int K) { return (act_ktiles(K) + 3) & ~3; }
-__host__ __device__ inline size_t act_row_bytes(int K) {
-  return (size_t)(K / kBlock) * 48 + 4 * (size_t)act_ktp(K);
-}
-__host__ __device__ inline size_t act_lo_codes_off(int K) { return (size_t)(K / kBlock) * 24; }
-__host__ __device__ inline size_t act_hi_scales_off(int K) { return (size_t)(K / kBlock) * 48; }
-__host__ __device__ inline size_t act_lo_scales_off(int K) {
-  return (size_t)(K / kBlock) * 48 + 2 * (size_t)act_ktp(K);
-}
+__host__ __device__ inline size_t act_row_bytes(int K) { return (size_t)act_ktiles(K) * kActChunk; }
 
 // ---------------------------------------------------------------------------
 // Prepacked weights: for each expert, for each output tile q of 32 rows, for
@@ -137,19 +134,33 @@ __device__ inline Split32 split_block32(float v, int c) {
   return r;
 }
 
-// Store block b of a packed row (K values) from lane c of the half-wave that split it.
-__device__ inline void store_split32(uint8_t* row, int K, int b, int c, const Split32& s) {
+// Store block b of a packed row from lane c of the half-wave that split it.
+__device__ inline void store_split32(uint8_t* row, int b, int c, const Split32& s) {
+  uint8_t* chunk = row + (size_t)(b >> 1) * kActChunk;
+  const int half = b & 1;
   if ((c & 3) == 0) {
-    uint8_t* ph = row + (size_t)b * 24 + 3 * (c >> 2);
-    uint8_t* pl = row + act_lo_codes_off(K) + (size_t)b * 24 + 3 * (c >> 2);
+    uint8_t* ph = chunk + half * 24 + 3 * (c >> 2);
+    uint8_t* pl = chunk + 48 + half * 24 + 3 * (c >> 2);
     ph[0] = (uint8_t)s.vh; ph[1] = (uint8_t)(s.vh >> 8); ph[2] = (uint8_t)(s.vh >> 16);
     pl[0] = (uint8_t)s.vl; pl[1] = (uint8_t)(s.vl >> 8); pl[2] = (uint8_t)(s.vl >> 16);
   }
   if (c == 0) {
-    const int ktp = act_ktp(K);
-    row[act_hi_scales_off(K) + (size_t)(b & 1) * ktp + (b >> 1)] = (uint8_t)s.s_hi;
-    row[act_lo_scales_off(K) + (size_t)(b & 1) * ktp + (b >> 1)] = (uint8_t)s.s_lo;
+    chunk[96 + half] = (uint8_t)s.s_hi;
+    chunk[98 + half] = (uint8_t)s.s_lo;
   }
+}
+
+// Pack block hw (= row * K/32 + b) of bf16 rows [rows][K]: one half-wavefront, lane c holds element c.
+// All 64 lanes call it; a half-wave past the last block only joins the lane exchanges.
+__device__ inline void pack_block_halfwave(const uint16_t* __restrict__ a, int K, int rows, long long hw, int c,
+                                           uint8_t* __restrict__ packed) {
+  const int nblk = K / kBlock;
+  const bool live = hw < (long long)rows * nblk;
+  const int row = live ? (int)(hw / nblk) : 0;
+  const int b = live ? (int)(hw - (long long)row * nblk) : 0;
+  const float v = live ? bf16_bits_to_float(a[(size_t)row * K + (size_t)b * kBlock + c]) : 0.0f;
+  const Split32 sp = split_block32(v, c);
+  if (live) store_split32(packed + (size_t)row * act_row_bytes(K), b, c, sp);
 }
 
 // ---------------------------------------------------------------------------
@@ -157,6 +168,12 @@ __device__ inline void store_split32(uint8_t* row, int K, int b, int c, const Sp
 // ---------------------------------------------------------------------------
 hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
                         int32_t* idx, float* w, float* logits, void* ws, hipStream_t s);
+// The whole routing front end of a forward pass: logits (with the activation split of x
+// into xpack done by extra workgroups), selection and grouping; small batches fuse the
+// selection and the grouping into one workgroup.
+hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
+                              int32_t* idx, float* w, void* ws, uint8_t* xpack, int32_t* counts,
+                              int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s);
 size_t route_workspace_bytes(int T, int D, int E);
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s);

@@ -16,15 +16,8 @@ namespace moe {
 
 __global__ __launch_bounds__(256) void pack_act_kernel(int K, int rows, const uint16_t* __restrict__ a,
                                                        uint8_t* __restrict__ packed) {
-  const int nblk = K / kBlock;
   const long long hw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;   // half-wave = one block
-  const int c = threadIdx.x & 31;
-  const bool live = hw < (long long)rows * nblk;                 // uniform per half-wave
-  const int row = live ? (int)(hw / nblk) : 0;
-  const int b = live ? (int)(hw - (long long)row * nblk) : 0;
-  const float v = live ? bf16_bits_to_float(a[(size_t)row * K + (size_t)b * kBlock + c]) : 0.0f;
-  const Split32 sp = split_block32(v, c);
-  if (live) store_split32(packed + (size_t)row * act_row_bytes(K), K, b, c, sp);
+  pack_block_halfwave(a, K, rows, hw, threadIdx.x & 31, packed);
 }
 
 hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipStream_t s) {

@@ -17,13 +17,9 @@
 // rank among equal experts comes from a ballot-based match (one ballot per
 // expert-id bit); across wavefronts, per-(wave, expert) counts in LDS give the
 // offsets.
-#include "moe_internal.h"
+#include "permute_body.h"
 
 namespace moe {
-
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / 64;
-constexpr int kPermRegs = 32;          // assignments held per thread per pass
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, int bm, int slots,
                                                                const int32_t* __restrict__ idx,
@@ -32,124 +28,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, int
                                                                int32_t* __restrict__ perm,
                                                                int32_t* __restrict__ inv,
                                                                int32_t* __restrict__ tiles) {
-  __shared__ int cnt[kMaxExperts];
-  __shared__ int base[kMaxExperts];
-  __shared__ int off0[kMaxExperts];
-  __shared__ int tstart[kMaxExperts + 1];
-  __shared__ int wcnt[kPermWaves][kMaxExperts];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-
-  for (int e = tid; e < E; e += kPermThreads) cnt[e] = 0;
-  __syncthreads();
-
-  // ---- histogram (integer LDS atomics: the totals do not depend on order) ----
-  for (int a = tid; a < n; a += kPermThreads) {
-    const int e = idx[a];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-
-  // ---- exclusive scan by wave 0 --------------------------------------------
-  if (wave == 0) {
-    int carry = 0;
-    for (int c = 0; c < E; c += 64) {
-      const int e = c + lane;
-      const int v = e < E ? cnt[e] : 0;
-      int incl = v;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-      }
-      if (e < E) {
-        base[e] = carry + incl - v;
-        off0[e] = carry + incl - v;
-        counts[e] = v;
-        offsets[e] = carry + incl - v;
-      }
-      carry += __shfl(incl, 63);
-    }
-    if (lane == 0) offsets[E] = carry;
-    // first tile slot of every expert
-    int tcarry = 0;
-    for (int c = 0; c < E; c += 64) {
-      const int e = c + lane;
-      const int v = e < E ? (cnt[e] + bm - 1) / bm : 0;
-      int incl = v;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-      }
-      if (e < E) tstart[e] = tcarry + incl - v;
-      tcarry += __shfl(incl, 63);
-    }
-    if (lane == 0) tstart[E] = tcarry;
-  }
-  __syncthreads();
-  // tile headers: slot s of expert e (binary search over tstart); slots past the last tile are empty
-  for (int s = tid; s < slots; s += kPermThreads) {
-    int4 h = make_int4(-1, 0, 0, 0);
-    if (s < tstart[E]) {
-      int lo = 0, hi = E - 1;                       // largest e with tstart[e] <= s
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tstart[mid] <= s) lo = mid; else hi = mid - 1;
-      }
-      const int t = s - tstart[lo];
-      h = make_int4(lo, off0[lo] + t * bm, min(bm, cnt[lo] - t * bm), 0);
-    }
-    *reinterpret_cast<int4*>(tiles + (size_t)s * kTileInts) = h;
-  }
-
-  // ---- stable scatter, chunk by chunk --------------------------------------
-  const int nchunks = (n + kPermThreads - 1) / kPermThreads;
-  for (int c0 = 0; c0 < nchunks; c0 += kPermRegs) {
-    int ev[kPermRegs];
-#pragma unroll
-    for (int r = 0; r < kPermRegs; ++r) {
-      const int a = (c0 + r) * kPermThreads + tid;
-      ev[r] = (c0 + r < nchunks && a < n) ? idx[a] : -1;
-    }
-#pragma unroll
-    for (int r = 0; r < kPermRegs; ++r) {
-      if (c0 + r >= nchunks) break;                      // uniform
-      const int a = (c0 + r) * kPermThreads + tid;
-      const int e = ev[r];
-      const bool valid = (unsigned)e < (unsigned)E;
-      // lanes holding the same expert: intersect ballots over the id bits
-      uint64_t same = __ballot(valid);
-#pragma unroll
-      for (int bit = 0; bit < 8; ++bit) {
-        const uint64_t b = __ballot(valid && ((e >> bit) & 1));
-        same &= ((e >> bit) & 1) ? b : ~b;
-      }
-      const int rank = __popcll(same & lt_mask);
-      for (int e2 = tid; e2 < kPermWaves * kMaxExperts; e2 += kPermThreads) (&wcnt[0][0])[e2] = 0;
-      __syncthreads();
-      if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
-      __syncthreads();
-      if (valid) {
-        int pos = base[e] + rank;
-        for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-        perm[pos] = a;
-        inv[a] = pos;
-        const int r = pos - off0[e];
-        tiles[(size_t)(tstart[e] + r / bm) * kTileInts + 4 + r % bm] = a;
-      }
-      __syncthreads();
-      for (int e2 = tid; e2 < E; e2 += kPermThreads) {
-        int s = 0;
-        for (int w = 0; w < kPermWaves; ++w) s += wcnt[w][e2];
-        base[e2] += s;
-      }
-      __syncthreads();
-    }
-  }
+  permute_group(n, E, bm, slots, idx, counts, offsets, perm, inv, tiles);
 }
 
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,

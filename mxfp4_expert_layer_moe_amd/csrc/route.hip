@@ -30,7 +30,7 @@
 //     ||x_t|| ||w_e|| by Cauchy-Schwarz), so the result is the float64
 //     selection at any input scale.  Gates are the softmax of the selected
 //     float64 scores.
-#include "moe_internal.h"
+#include "permute_body.h"
 
 namespace moe {
 
@@ -93,14 +93,23 @@ size_t route_workspace_bytes(int T, int D, int E) {
   return T > 0 ? route_ws_layout(T, E).total : 0;
 }
 
+// Workgroups past the logit tiles (when xpack is given) split x into the packed activation
+// format for the gate/up GEMM instead: 32 blocks of 32 values per workgroup.
 __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, int D, int E, int KW,
                                                                          const uint16_t* __restrict__ x,
                                                                          const float* __restrict__ wr,
                                                                          double* __restrict__ logit,
                                                                          float* __restrict__ xsq,
-                                                                         float* __restrict__ wsq) {
+                                                                         float* __restrict__ wsq,
+                                                                         int logit_wgs,
+                                                                         uint8_t* __restrict__ xpack) {
   __shared__ double red[8][32][33];          // K-partials: waves 0..7, then 8..15 added in place
   __shared__ float rsq[kLogitWaves][2][32];  // partial ||x_t||^2 (0) and ||w_e||^2 (1)
+  if ((int)blockIdx.x >= logit_wgs) {        // activation split (no barriers on this path)
+    const long long hw = (long long)(blockIdx.x - logit_wgs) * (kLogitWaves * 2) + (threadIdx.x >> 5);
+    pack_block_halfwave(x, D, T, hw, threadIdx.x & 31, xpack);
+    return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -204,82 +213,110 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, i
   }
 }
 
-__global__ __launch_bounds__(256) void route_select_kernel(int T, int D, int E, int k, int KW,
-                                                           const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ wr,
-                                                           const float* __restrict__ br,
-                                                           const double* __restrict__ logit,
-                                                           const float* __restrict__ xsq,
-                                                           const float* __restrict__ wsq,
-                                                           int32_t* __restrict__ out_idx, float* __restrict__ out_w,
-                                                           float* __restrict__ out_logits) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;                                     // no barriers in this kernel
-  const int epad = ((E + 31) / 32) * 32;
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
 
-  // partial tiles of the KW K-ranges are summed in a fixed order (KW <= 4)
-  float wmax2 = 0.0f;
-  for (int e = lane; e < E; e += 64) {
-    float s = 0.0f;
+// Lane-to-lane move inside rows of 16 lanes (DPP), applied to both halves of a double.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+
+// Maximum over the 64 lanes, returned in every lane: quad swaps and row rotations by 4 and 8
+// leave each row of 16 holding its maximum, then the four row maxima are read out.
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dpp_f64<0xB1>(v));     // quad_perm [1,0,3,2]
+  v = fmax(v, dpp_f64<0x4E>(v));     // quad_perm [2,3,0,1]
+  v = fmax(v, dpp_f64<0x124>(v));    // row_ror:4
+  v = fmax(v, dpp_f64<0x128>(v));    // row_ror:8
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
+// The k best live experts of the wavefront's token, in order of score (higher first, lower
+// expert id first on equal scores): k rounds of a wave-wide maximum, each taking the lowest id
+// that reaches it.  Lane l holds experts l + 64c.  Marks the winners in taken[]; returns the
+// first and the k-th winning score.
+__device__ __forceinline__ void top_k(const double* v, const bool* live, int k, int lane, bool* taken,
+                                      double& first, double& kth) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q < KW) s += wsq[(size_t)q * epad + e];
-    wmax2 = fmaxf(wmax2, s);
+  for (int c = 0; c < 4; ++c) taken[c] = false;
+  first = kth = -INFINITY;
+  for (int r = 0; r < k; ++r) {
+    double best = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) best = live[c] && !taken[c] ? fmax(best, v[c]) : best;
+    const double mx = wave_max_f64(best);
+    int win = -1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint64_t m = __ballot(live[c] && !taken[c] && v[c] == mx);
+      if (win < 0 && m) win = 64 * c + __ffsll((long long)m) - 1;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) taken[c] = taken[c] || lane + 64 * c == win;
+    if (r == 0) first = mx;
+    kth = mx;
   }
+}
+
+// Selection and gates of token t by one wavefront (all 64 lanes).  wmax2 = max_e ||w_e||^2.
+__device__ __forceinline__ void select_token(int t, int T, int D, int E, int k, int KW, float wmax2,
+                                             const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                             const float* __restrict__ br, const double* __restrict__ logit,
+                                             const float* __restrict__ xsq, int32_t* __restrict__ out_idx,
+                                             float* __restrict__ out_w, float* __restrict__ out_logits) {
+  const int lane = threadIdx.x & 63;
+  const int epad = ((E + 31) / 32) * 32;
+  // the KW partial tiles are summed in a fixed order (KW <= 4)
+  // loads are unconditional (indices clamped into range) so they issue together; the partials
+  // past KW and experts past E are masked afterwards
+  float xp[4];
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) wmax2 = fmaxf(wmax2, __shfl_xor(wmax2, d));
+  for (int q = 0; q < 4; ++q) xp[q] = xsq[(size_t)min(q, KW - 1) * T + t];
   float xn2 = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (q < KW) xn2 += xsq[(size_t)q * T + t];
-
+  for (int q = 0; q < 4; ++q) xn2 += q < KW ? xp[q] : 0.0f;
+  double lp[4][4];
+  float bias[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ec = min(lane + 64 * c, E - 1);
+    bias[c] = br[ec];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lp[c][q] = logit[((size_t)min(q, KW - 1) * T + t) * epad + ec];
+  }
   double v[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
-    double s = -INFINITY;
-    if (e < E) {
-      s = 0.0;
+    double s = 0.0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (q < KW) s += logit[((size_t)q * T + t) * epad + e];
-      s += (double)br[e];
-    }
-    v[c] = s;
+    for (int q = 0; q < 4; ++q) s += q < KW ? lp[c][q] : 0.0;
+    v[c] = e < E ? s + (double)bias[c] : -INFINITY;
     if (out_logits && e < E) out_logits[(size_t)t * E + e] = (float)v[c];
   }
-  // k rounds of arg-max; taken experts are excluded by a per-lane bit mask
-  uint32_t taken = 0;
-  double kth = 0.0;
-  for (int j = 0; j < k; ++j) {
-    double bv = -INFINITY;
-    int be = 0x7fffffff;
+  bool live[4], taken[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = lane + 64 * c;
-      if (e < E && !(taken & (1u << c)) && (v[c] > bv || (v[c] == bv && e < be))) { bv = v[c]; be = e; }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const double ov = __shfl_xor(bv, d);
-      const int oe = __shfl_xor(be, d);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    kth = bv;
-  }
+  for (int c = 0; c < 4; ++c) live[c] = lane + 64 * c < E;
+  double mx, kth;
+  top_k(v, live, k, lane, taken, mx, kth);
   const double band = kBandRel * sqrt((double)xn2 * (double)wmax2);
   bool cand[4];
   int n = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int e = lane + 64 * c;
-    cand[c] = e < E && ((taken & (1u << c)) || v[c] >= kth - band);
+    cand[c] = live[c] && (taken[c] || v[c] >= kth - band);
     n += __popcll(__ballot(cand[c]));
   }
   if (n > k) {
-    // near the boundary: re-score every candidate exactly, then re-take the top-k
+    // near the boundary: re-score every candidate exactly, then select again among the candidates
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint64_t m = __ballot(cand[c]);
@@ -290,46 +327,29 @@ __global__ __launch_bounds__(256) void route_select_kernel(int T, int D, int E, 
         const double s = score_f64(x + (size_t)t * D, wr + (size_t)e * D, (double)br[e], D, lane);
         if (lane == src) v[c] = s;
       }
-      if (!cand[c]) v[c] = -INFINITY;
     }
-    taken = 0;
-    for (int j = 0; j < k; ++j) {
-      double bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e = lane + 64 * c;
-        if (cand[c] && !(taken & (1u << c)) && (v[c] > bv || (v[c] == bv && e < be))) { bv = v[c]; be = e; }
-      }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) {
-        const double ov = __shfl_xor(bv, d);
-        const int oe = __shfl_xor(be, d);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    }
+    top_k(v, cand, k, lane, taken, mx, kth);
   }
-  // gates: softmax over the selected scores; slots in ascending expert id
-  double mx = -INFINITY;
+  // gates: softmax over the selected scores (mx is the largest), summed in ascending expert id
+  double ex[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    if (taken & (1u << c)) mx = fmax(mx, v[c]);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmax(mx, __shfl_xor(mx, d));
-  double ex[4], part_sum = 0.0;
+  for (int c = 0; c < 4; ++c) ex[c] = taken[c] ? exp(v[c] - mx) : 0.0;
+  double sum = 0.0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    ex[c] = (taken & (1u << c)) ? exp(v[c] - mx) : 0.0;
-    part_sum += ex[c];
+    uint64_t m = __ballot(taken[c]);
+    while (m) {
+      const int l = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      sum += readlane_f64(ex[c], l);
+    }
   }
-  const double sum = wave_sum_f64(part_sum);
   int before = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint64_t m = __ballot((taken >> c) & 1u);
+    const uint64_t m = __ballot(taken[c]);
     const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
-    if (taken & (1u << c)) {
+    if (taken[c]) {
       out_idx[(size_t)t * k + slot] = lane + 64 * c;
       out_w[(size_t)t * k + slot] = (float)(ex[c] / sum);
     }
@@ -337,22 +357,106 @@ __global__ __launch_bounds__(256) void route_select_kernel(int T, int D, int E, 
   }
 }
 
+// max_e ||w_e||^2 over the KW partial sums (fixed order); one value per wavefront
+__device__ __forceinline__ float max_wnorm2(int E, int KW, const float* __restrict__ wsq) {
+  const int lane = threadIdx.x & 63;
+  const int epad = ((E + 31) / 32) * 32;
+  float wmax2 = 0.0f;
+  for (int c = 0; 64 * c < E; ++c) {
+    const int e = lane + 64 * c;
+    float wp[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wp[q] = wsq[(size_t)min(q, KW - 1) * epad + min(e, E - 1)];
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += q < KW ? wp[q] : 0.0f;
+    wmax2 = fmaxf(wmax2, e < E ? s : 0.0f);
+  }
+  wmax2 = (float)wave_max_f64((double)wmax2);
+  return wmax2;
+}
+
+__global__ __launch_bounds__(256) void route_select_kernel(int T, int D, int E, int k, int KW,
+                                                           const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ wr,
+                                                           const float* __restrict__ br,
+                                                           const double* __restrict__ logit,
+                                                           const float* __restrict__ xsq,
+                                                           const float* __restrict__ wsq,
+                                                           int32_t* __restrict__ out_idx, float* __restrict__ out_w,
+                                                           float* __restrict__ out_logits) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                                     // no barriers in this kernel
+  select_token(t, T, D, E, k, KW, max_wnorm2(E, KW, wsq), x, wr, br, logit, xsq, out_idx, out_w, out_logits);
+}
+
+// Small batches: one workgroup selects every token, then groups the assignments
+// (the selection's global writes are visible to the workgroup after the barrier).
+__global__ __launch_bounds__(kPermThreads) void route_select_permute_kernel(
+    int T, int D, int E, int k, int KW, const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ br, const double* __restrict__ logit, const float* __restrict__ xsq,
+    const float* __restrict__ wsq, int32_t* __restrict__ out_idx, float* __restrict__ out_w, int bm, int slots,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ tiles) {
+  const float wmax2 = max_wnorm2(E, KW, wsq);
+  for (int t = threadIdx.x >> 6; t < T; t += kPermWaves)
+    select_token(t, T, D, E, k, KW, wmax2, x, wr, br, logit, xsq, out_idx, out_w, nullptr);
+  __syncthreads();
+  permute_group(T * k, E, bm, slots, out_idx, counts, offsets, perm, inv, tiles);
+}
+
+static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
+                                hipStream_t s, double** logit, float** xsq, float** wsq, int* KW) {
+  *KW = route_kw(T, E);
+  const RouteWs L = route_ws_layout(T, E);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  *logit = reinterpret_cast<double*>(base + L.logit);
+  *xsq = reinterpret_cast<float*>(base + L.xsq);
+  *wsq = reinterpret_cast<float*>(base + L.wsq);
+  const int logit_wgs = ((T + kRouteTokens - 1) / kRouteTokens) * ((E + 31) / 32) * *KW;
+  const long long pack_halfwaves = xpack ? (long long)T * (D / kBlock) : 0;
+  const long long pack_wgs = (pack_halfwaves + 2 * kLogitWaves - 1) / (2 * kLogitWaves);
+  route_logits_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kLogitWaves * 64), 0, s>>>(
+      T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
                         int32_t* idx, float* w, float* logits, void* ws, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const RouteWs L = route_ws_layout(T, E);
-  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
-  double* logit = reinterpret_cast<double*>(base + L.logit);
-  float* xsq = reinterpret_cast<float*>(base + L.xsq);
-  float* wsq = reinterpret_cast<float*>(base + L.wsq);
-  const int KW = route_kw(T, E);
-  const int tiles = ((T + kRouteTokens - 1) / kRouteTokens) * ((E + 31) / 32);
-  route_logits_kernel<<<dim3(tiles * KW), dim3(kLogitWaves * 64), 0, s>>>(T, D, E, KW, x, wr, logit, xsq, wsq);
-  hipError_t err = hipGetLastError();
+  double* logit;
+  float *xsq, *wsq;
+  int KW;
+  hipError_t err = launch_logits(T, D, E, x, wr, ws, nullptr, s, &logit, &xsq, &wsq, &KW);
   if (err != hipSuccess) return err;
   route_select_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq, idx, w,
                                                               logits);
   return hipGetLastError();
+}
+
+constexpr int kFusedSelectMaxT = 64;         // up to here one workgroup selects and groups
+
+hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
+                              int32_t* idx, float* w, void* ws, uint8_t* xpack, int32_t* counts,
+                              int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  double* logit;
+  float *xsq, *wsq;
+  int KW;
+  hipError_t err = launch_logits(T, D, E, x, wr, ws, xpack, s, &logit, &xsq, &wsq, &KW);
+  if (err != hipSuccess) return err;
+  const int n = T * k;
+  if (T <= kFusedSelectMaxT) {
+    route_select_permute_kernel<<<dim3(1), dim3(kPermThreads), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq,
+                                                                       idx, w, tile_rows(n, E),
+                                                                       (int)tile_slots(n, E), counts, offsets, perm,
+                                                                       inv, tiles);
+    return hipGetLastError();
+  }
+  route_select_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq, idx, w,
+                                                              nullptr);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  return launch_permute(T, E, k, idx, counts, offsets, perm, inv, tiles, s);
 }
 
 }  // namespace moe

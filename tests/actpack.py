@@ -1,10 +1,11 @@
 """CPU decoder of the library's packed activation rows (hi/lo FP6 E2M3 + E8M0).
 
-Format (documented in include/moe_mxfp4.h): per row of K values
-  [hi codes K/32 x 24 B][lo codes K/32 x 24 B][hi scales 2 x KTp][lo scales 2 x KTp],
-KTp = roundup(K/64, 4); block b's codes are 6-bit fields, element i at bits
-6i..6i+5 (little-endian); block b's scale byte sits at [b % 2][b // 2].
-E2M3: sign bit 5, exponent bits 4-3 (bias 1), mantissa bits 2-0.
+Format (documented in include/moe_mxfp4.h): per row of K values, K/64 chunks of
+112 bytes, one per 64-wide k-tile kt: [0,24) hi codes of block 2kt, [24,48) hi
+codes of block 2kt+1, [48,72) and [72,96) the lo codes, [96],[97] the hi scale
+bytes and [98],[99] the lo scale bytes of blocks 2kt, 2kt+1.  Codes are 6-bit
+fields, element i at bits 6i..6i+5 (little-endian).  E2M3: sign bit 5, exponent
+bits 4-3 (bias 1), mantissa bits 2-0.
 """
 import numpy as np
 
@@ -22,25 +23,19 @@ _E2M3 = e2m3_table()
 
 
 def row_bytes(K: int) -> int:
-    ktp = (K // 64 + 3) // 4 * 4
-    return K // 32 * 48 + 4 * ktp
+    return K // 64 * 112
 
 
 def decode(buf, K: int, rows: int):
     """buf: uint8 array (at least rows*row_bytes(K)) -> (hi, lo) float64 [rows][K]."""
-    nb = K // 32
-    ktp = (K // 64 + 3) // 4 * 4
-    rb = row_bytes(K)
-    a = np.asarray(buf, dtype=np.uint8)[: rows * rb].reshape(rows, rb)
+    kt = K // 64
+    a = np.asarray(buf, dtype=np.uint8)[: rows * row_bytes(K)].reshape(rows, kt, 112)
     out = []
     for term in range(2):
-        codes = a[:, term * nb * 24:(term + 1) * nb * 24].reshape(rows, nb, 24)
-        bits = np.unpackbits(codes, axis=2, bitorder="little").reshape(rows, nb, 32, 6)
-        c = (bits * (1 << np.arange(6))).sum(axis=3)
-        so = nb * 48 + term * 2 * ktp
-        sc = a[:, so:so + 2 * ktp].reshape(rows, 2, ktp)
-        b = np.arange(nb)
-        sbyte = sc[:, b % 2, b // 2].astype(np.int64)                  # [rows][nb]
+        codes = a[:, :, term * 48:(term + 1) * 48].reshape(rows, kt, 2, 24)
+        bits = np.unpackbits(codes, axis=3, bitorder="little").reshape(rows, kt, 2, 32, 6)
+        c = (bits * (1 << np.arange(6))).sum(axis=4)
+        sbyte = a[:, :, 96 + 2 * term:98 + 2 * term].astype(np.int64)          # [rows][kt][2]
         val = _E2M3[c] * np.ldexp(1.0, sbyte - 127)[..., None]
         out.append(val.reshape(rows, K))
     return out[0], out[1]

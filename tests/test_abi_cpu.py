@@ -45,8 +45,8 @@ D = M.dims(2880, 2880, 32, 4)
 
 
 def test_size_functions_closed_forms():
-    assert M.moe_act_pack_bytes(2880, 1) == 90 * 48 + 4 * 48
-    assert M.moe_act_pack_bytes(64, 3) == 3 * (2 * 48 + 16)
+    assert M.moe_act_pack_bytes(2880, 1) == 45 * 112
+    assert M.moe_act_pack_bytes(64, 3) == 3 * 112
     assert M.moe_act_pack_bytes(96, 1) == 0                    # K % 64 != 0
     # prepacked codes are exactly the MXFP4 code bytes: 4 bits per weight
     assert M.moe_prepacked_codes_bytes(D, M.MOE_STAGE_GATE_UP) == 32 * 5760 * 2880 // 2

@@ -81,8 +81,9 @@ def test_small_case_parity(name):
     _full_check(name, inp)
 
 
-def test_forward_equals_steps_and_is_deterministic():
-    inp = synth.make_inputs(dict(T=64, D=128, E=8, k=2, I=192, seed=50))
+@pytest.mark.parametrize("T", [64, 200])          # fused small-batch front end / separate kernels
+def test_forward_equals_steps_and_is_deterministic(T):
+    inp = synth.make_inputs(dict(T=T, D=128, E=8, k=2, I=192, seed=50))
     layer = _layer(inp)
     g = parity.run_gpu(layer)
     y1 = layer.forward(bf16=False).clone()
