@@ -10,8 +10,8 @@ step through every layer of the 20b model: 10.2 GB) so each step streams its
 weights from HBM rather than from the 256 MB last-level cache.
 
 Prints one JSON line.  ``value`` is tokens/s of the layer; ``roofline`` is the
-dominant kernel (the gate/up expert GEMM) timed alone with HIP events on its
-stream; ``cpu_baseline`` is the float64 oracle on the host on a bounded sample.
+dominant kernel (the gate/up expert GEMM) launched back to back on its stream,
+between two HIP events; ``cpu_baseline`` is the float64 oracle on the host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -40,7 +40,106 @@ def parse():
     p.add_argument("--kernel-steps", type=int, default=None, help="launches of the dominant kernel to time")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-tokens", type=int, default=None, help="tokens in the CPU-baseline sample")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="after the measurements, run 3 plain device-to-device copies of this many MiB "
+                        "(the calibration of the HBM byte counters)")
+    p.add_argument("--traffic-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write the gate/up kernel's HBM traffic from two rocprofv3 --pmc runs "
+                        "(FETCH_SIZE, WRITE_SIZE) of this script with --copy-mib, then exit")
+    p.add_argument("--stats-report", nargs=2, metavar=("STATS_CSV", "OUT_TXT"),
+                   help="summarise a rocprofv3 --stats kernel table as text, then exit")
+    p.add_argument("--command", default="", help="the command that made the profile (for the reports)")
     return p.parse_args()
+
+
+def workload_name(cfg: dict) -> str:
+    return (f"gpt-oss MoE layer ({cfg['name']}): T={cfg['T']} tokens, d_model={cfg['D']}, d_ff={cfg['I']}, "
+            f"{cfg['E']} experts, top-{cfg['k']}, MXFP4 experts, bf16 activations")
+
+
+GEMM_SRC = os.path.join(ROOT, "mxfp4_expert_layer_moe_amd", "csrc", "gemm.hip")
+GU_KERNEL_PREFIX = "void moe::expert_gemm_kernel<0,"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _per_dispatch(rows, counter: str):
+    """{dispatch id: (kernel name, summed counter value)} in dispatch order."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, v = out.get(d, (r["Kernel_Name"], 0.0))
+        out[d] = (name, v + float(r["Counter_Value"]))
+    return dict(sorted(out.items()))
+
+
+def traffic_report(args):
+    """Gate/up kernel HBM bytes per launch, each counter scaled by what it reads for a plain copy.
+
+    FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  The last three copyBuffer dispatches
+    of each run are the --copy-mib calibration copies (read and write copy_mib MiB each).
+    """
+    cfg = dict(__import__("synth").CONFIGS[args.config])
+    known = args.copy_mib * 2 ** 20
+    if known <= 0:
+        raise SystemExit("--traffic-report needs the --copy-mib the runs used")
+    rec = {"workload": workload_name(cfg),
+           "kernel": "expert_gemm_kernel<0> (gate/up + SwiGLU)",
+           "kernel_source_sha256_16": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16],
+           "command": args.command}
+    total = 0.0
+    for key, d, counter in (("fetch", args.traffic_report[0], "FETCH_SIZE"),
+                            ("write", args.traffic_report[1], "WRITE_SIZE")):
+        per = _per_dispatch(_counter_rows(d), counter)
+        gu = [v for n, v in per.values() if n.startswith(GU_KERNEL_PREFIX)]
+        cp = [v for n, v in per.values() if n.startswith(COPY_KERNEL)][-3:]
+        if not gu or len(cp) < 3:
+            raise SystemExit(f"{d}: {len(gu)} gate/up dispatches, {len(cp)} calibration copies")
+        kib = sum(gu) / len(gu)
+        factor = known / (sum(cp) / len(cp) * 1024.0)
+        rec[f"{key}_kib_per_launch_raw"] = round(kib, 1)
+        rec[f"{key}_gate_up_dispatches"] = len(gu)
+        rec[f"{key}_copy_kib_raw"] = [round(v, 1) for v in cp]
+        rec[f"{key}_copy_scale"] = round(factor, 5)
+        rec[f"{key}_bytes_per_launch"] = int(kib * 1024.0 * factor)
+        total += kib * 1024.0 * factor
+    rec["copy_bytes_each_way"] = known
+    rec["hbm_bytes_per_launch"] = int(total)
+    path = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def stats_report(args):
+    """Text table of a rocprofv3 kernel_stats.csv (per-kernel calls and durations)."""
+    import csv
+    rows = list(csv.DictReader(open(args.stats_report[0])))
+    lines = [f"# rocprofv3 --kernel-trace --stats summary",
+             f"# command: {args.command}" if args.command else "# command: (not given)",
+             f"{'kernel':<72} {'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:72]:<72} {int(r['Calls']):>7} {float(r['AverageNs']) / 1e3:>9.2f} "
+                     f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
+                     f"{float(r['Percentage']):>6.2f}")
+    with open(args.stats_report[1], "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def traffic_for(kernel_src: str, workload: str):
@@ -74,6 +173,10 @@ def cpu_baseline(inp, n_tokens):
 
 def main():
     args = parse()
+    if args.traffic_report:
+        return traffic_report(args)
+    if args.stats_report:
+        return stats_report(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
                           "(the multi-GPU sharding is described in the design notes, not built)"}))
@@ -123,21 +226,20 @@ def main():
     counts = layer.counts.cpu().numpy()
     touched = int((counts > 0).sum())
     nk = args.kernel_steps or args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
     for s in range(args.warmup):
         layer.gate_up(weights=copies[s % L])
+    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ka.record(stream)                        # the launches run back to back on this stream
     for s in range(nk):
-        evs[s][0].record(stream)
         layer.gate_up(weights=copies[s % L])
-        evs[s][1].record(stream)
+    kb.record(stream)
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    k_ms = ka.elapsed_time(kb) / nk
     gu_weight_bytes = touched * 2 * I * D * EXPERT_BYTES_PER_PARAM
     gu_alg_bytes = gu_weight_bytes + T * D * 2 + T * k * I * 2            # weights + x in + h out (bf16)
     gu_flops = 2.0 * T * k * D * 2 * I
-    workload = (f"gpt-oss MoE layer ({cfg['name']}): T={T} tokens, d_model={D}, d_ff={I}, "
-                f"{E} experts, top-{k}, MXFP4 experts, bf16 activations")
-    src = os.path.join(ROOT, "mxfp4_expert_layer_moe_amd", "csrc", "gemm.hip")
+    workload = workload_name(cfg)
+    src = GEMM_SRC
     if decode or gu_alg_bytes / HBM_PEAK_GBS > gu_flops / FP4_PEAK_TFLOPS / 1e3:
         achieved = gu_alg_bytes / (k_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -177,6 +279,16 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if args.copy_mib > 0:                     # counter calibration: plain copies of known size, untimed
+        n = args.copy_mib * 2 ** 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens or (T if decode else 8))
     print(json.dumps(out), flush=True)
