@@ -77,8 +77,10 @@ __device__ inline v8i a_operand_lds(const uint8_t* p) {      // 24 bytes, 8-byte
   return v;
 }
 
-// Staged rows in LDS: the packed row's chunks for k-tiles [c0, c0 + KC), row stride KC * 112 bytes.
-__host__ __device__ inline int stage_stride(int KC) { return KC * kActChunk; }
+// Staged rows in LDS: the packed row's chunks for k-tiles [c0, c0 + KC), row stride KC * 112 + 8
+// bytes.  The 8-byte pad keeps the rows of one read on different banks (KC * 112 alone is a
+// multiple of the 128-byte bank cycle for every even KC).
+__host__ __device__ inline int stage_stride(int KC) { return KC * kActChunk + 8; }
 
 // KTC: the number of 64-wide k-tiles when known at compile time (K = 2880 gives 45), else 0.
 // With KTC the whole K range is staged at once and the k-loop is fully unrolled, so the
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 
   // K chunk staged at once: everything if it fits, else a multiple of the prefetch depth
   int KC = KTC > 0 ? KTC : g.KT;
-  if (KTC == 0 && nrows * stage_stride(KC) > kAStageBytes) KC = (kAStageBytes / (nrows * kActChunk)) / P * P;
+  if (KTC == 0 && nrows * stage_stride(KC) > kAStageBytes) KC = ((kAStageBytes / nrows - 8) / kActChunk) / P * P;
   const int rs = stage_stride(KC);
   const size_t arb = act_row_bytes(g.K);
 
@@ -162,16 +164,16 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   for (int c0 = 0; c0 < g.KT; c0 += KC) {
     const int kcn = min(KC, g.KT - c0);
     __syncthreads();                                    // previous chunk consumed; srow visible
-    // stage rows [0, nrows) x k-tiles [c0, c0 + kcn): contiguous chunks, 16-byte words
-    const int n16 = kcn * (kActChunk / 16);
-    for (int w = tid; w < nrows * n16; w += 256) {
-      const int r = w / n16, o = w - r * n16;
-      const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + (size_t)c0 * kActChunk + (size_t)o * 16;
-      *reinterpret_cast<uint4*>(sA + r * rs + o * 16) = *reinterpret_cast<const uint4*>(src);
+    // stage rows [0, nrows) x k-tiles [c0, c0 + kcn): contiguous chunks, 8-byte words
+    const int n8 = kcn * (kActChunk / 8);
+    for (int w = tid; w < nrows * n8; w += 256) {
+      const int r = w / n8, o = w - r * n8;
+      const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + (size_t)c0 * kActChunk + (size_t)o * 8;
+      *reinterpret_cast<uint2*>(sA + r * rs + o * 8) = *reinterpret_cast<const uint2*>(src);
     }
     __syncthreads();
     if (active) {
-      const uint8_t* arow = sA + i * rs;
+      const uint8_t* arow = sA + min(i, BM - 1) * rs;       // lanes past BM rows are masked below
       const int kend = c0 + kcn;
       // A operands of k-tile kt from LDS; rows past nrows read stale bytes and are masked to zero
       auto lds_a = [&](const int kt, v8i& hi, v8i& lo, uint32_t& sh, uint32_t& sl) {
@@ -290,7 +292,7 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   const bool small = tile_rows(n_assign, E) == 8;
   const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));
   // the model's K = 2880 (45 k-tiles) with decode tiles: fully unrolled k-loop
-  const bool k45 = g.KT == 45 && small && 8 * stage_stride(45) <= kAStageBytes;   // 40320 <= 40960
+  const bool k45 = g.KT == 45 && small && 8 * stage_stride(45) <= kAStageBytes;   // 40384 <= 40960
   if (stage == 0) {
     if (k45) expert_gemm_kernel<0, 8, 8, 45, 1><<<grid, dim3(256), 0, s>>>(g);
     else if (small) expert_gemm_kernel<0, 8, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
