@@ -15,12 +15,15 @@ LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe_mxfp4.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "pack.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "pack.hip", "gemm.hip", "gemm_prefill.hip", "combine.hip"]
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled: plain fp32 VALU only
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
+# per-source extras: the prefill GEMM's 45-step k-loop is unrolled whole (its ring slots and scale
+# byte selectors must be compile-time constants), past LLVM's default pragma-unroll size limit
+EXTRA = {"gemm_prefill.hip": ["-mllvm", "-pragma-unroll-threshold=100000"]}
 
 
 def hipcc() -> str:
@@ -38,7 +41,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(LIBDIR, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *HIPFLAGS, "-x", "hip", "-c", path, "-o", obj]
+        cmd = [cc, *HIPFLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

@@ -21,12 +21,17 @@ moe_status check_dims(const moe_dims* d) {
   if (!(d->swiglu_limit > 0.0f) || !isfinite(d->swiglu_limit)) return MOE_EINVAL;
   if (d->d_model % kKTile || d->d_ff % kKTile) return MOE_EUNSUPPORTED;
   if (d->top_k > d->n_experts || d->n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
+  // one expert's weights are addressed with 32-bit buffer offsets
+  if ((int64_t)d->d_model * d->d_ff >= (int64_t)1 << 32) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
 moe_status check_T(const moe_dims* d, int32_t T) {
   if (T < 0) return MOE_EINVAL;
   if ((int64_t)T * d->top_k >= (1 << 24)) return MOE_EUNSUPPORTED;
+  // packed activation rows (x and h) are addressed with 32-bit buffer offsets
+  const int kmax = d->d_model > d->d_ff ? d->d_model : d->d_ff;
+  if ((int64_t)T * d->top_k * (int64_t)act_row_bytes(kmax) >= (int64_t)1 << 32) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -37,7 +42,8 @@ struct WsLayout {
 };
 
 size_t tile_table_bytes(const moe_dims* d, int32_t T) {
-  return (size_t)tile_slots((long long)T * d->top_k, d->n_experts) * kTileInts * 4;
+  const long long n = (long long)T * d->top_k;
+  return (size_t)tile_slots(n, d->n_experts) * tile_ints(tile_rows(n, d->n_experts)) * 4;
 }
 
 WsLayout ws_layout(const moe_dims* d, int32_t T) {

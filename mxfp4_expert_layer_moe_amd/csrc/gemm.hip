@@ -22,7 +22,7 @@
 // one 32-column tile (stage 1), one unit per wavefront.  Weights stream from
 // HBM once per (row tile, unit); a wavefront issues the loads of four k-tiles
 // before their eight matrix instructions.
-#include "moe_internal.h"
+#include "mfma_ops.h"
 
 namespace moe {
 
@@ -39,36 +39,6 @@ struct GemmArgs {
 };
 
 constexpr int kAStageBytes = 40 * 1024;     // LDS for staged activation rows: 8 rows of K = 2880 fit whole
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-__device__ inline v8i b_operand(const v4i b) {
-  v8i v = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
-  return v;
-}
-
-// Raw buffer resource over [base, base + bytes): weight tiles are fetched with buffer loads, so a
-// wavefront needs one lane offset in a vector register and a scalar offset per k-tile (no 64-bit
-// address per load), and any read past `bytes` returns zero.
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
-// scaled MFMA, A = FP6 E2M3 (scale byte 0 of sa), B = FP4 E2M1 (scale byte `ob` of sb)
-template <int OB>
-__device__ inline v16f mma_fp6_fp4(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 4, 0, sa, OB, sb);
-}
-
-// ob is a compile-time constant after unrolling, so the switch folds away
-__device__ inline v16f mma_sel(int ob, v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
-  switch (ob) {
-    case 0: return mma_fp6_fp4<0>(a, b, c, sa, sb);
-    case 1: return mma_fp6_fp4<1>(a, b, c, sa, sb);
-    case 2: return mma_fp6_fp4<2>(a, b, c, sa, sb);
-    default: return mma_fp6_fp4<3>(a, b, c, sa, sb);
-  }
-}
 
 __device__ inline v8i a_operand_lds(const uint8_t* p) {      // 24 bytes, 8-byte aligned
   const uint2* q = reinterpret_cast<const uint2*>(p);
@@ -287,20 +257,19 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   g.codes_per_expert = w_codes_per_expert(N, g.K);
   g.scales_per_expert = w_scales_per_expert(N, g.K);
   const long long n_assign = (long long)T * k;
-  // decode-sized batches (few rows per expert): 8-row tiles whose activations fit LDS whole;
-  // otherwise 32-row tiles (one full MFMA tile) with K staged in chunks.  Same rule as the table.
-  const bool small = tile_rows(n_assign, E) == 8;
+  // batches with many rows per expert (128-row tiles) go to the prefill kernel
+  if (tile_rows(n_assign, E) != 8)
+    return launch_gemm_prefill(stage, T, D, I, E, k, limit, a_packed, tiles, codes, scales, topk_w, out, s);
+  // decode-sized batches (8-row tiles whose activations fit LDS whole)
   const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));
-  // the model's K = 2880 (45 k-tiles) with decode tiles: fully unrolled k-loop
-  const bool k45 = g.KT == 45 && small && 8 * stage_stride(45) <= kAStageBytes;   // 40384 <= 40960
+  // the model's K = 2880 (45 k-tiles): fully unrolled k-loop
+  const bool k45 = g.KT == 45 && 8 * stage_stride(45) <= kAStageBytes;   // 40384 <= 40960
   if (stage == 0) {
     if (k45) expert_gemm_kernel<0, 8, 8, 45, 1><<<grid, dim3(256), 0, s>>>(g);
-    else if (small) expert_gemm_kernel<0, 8, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_kernel<0, 8, kMTile, 0, 1><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<0, 8, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
   } else {
     if (k45) expert_gemm_kernel<1, 16, 8, 45, 2><<<grid, dim3(256), 0, s>>>(g);
-    else if (small) expert_gemm_kernel<1, 16, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_kernel<1, 8, kMTile, 0, 1><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<1, 16, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
   }
   return hipGetLastError();
 }

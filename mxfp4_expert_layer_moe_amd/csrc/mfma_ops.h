@@ -1,0 +1,103 @@
+// gfx950 operand helpers shared by the expert GEMM kernels.
+//
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 computes a 32x32 fp32 tile from a 32x64
+// A block and a 64x32 B block, each in an FP8/FP6/FP4 format with one E8M0
+// scale per 32 K values.  Here B is always the MXFP4 weight (E2M1 codes and
+// E8M0 scales as stored, "gpt-oss architecture walk-through", section
+// "Quantization") and A one FP6 E2M3 term of the activation.
+// Lane l holds row l%32 (A) / column l%32 (B) and the 32 K values of block
+// l/32; its scale is byte `opsel` of the lane's scale dword.  Result: lane l,
+// register r holds row 8(r/4) + 4(l/32) + r%4, column l%32.
+#pragma once
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+
+// FP4 operand: 16 bytes per lane (32 E2M1 codes) in the low four dwords
+__device__ inline v8i b_operand(const v4i b) {
+  v8i v = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+  return v;
+}
+
+// Raw buffer resource over [base, base + bytes): loads take a 32-bit lane offset in a vector
+// register and a scalar offset, and any read past `bytes` returns zero.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// scaled MFMA, A = FP6 E2M3 (scale byte 0 of sa), B = FP4 E2M1 (scale byte OB of sb)
+template <int OB>
+__device__ inline v16f mma_fp6_fp4(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 4, 0, sa, OB, sb);
+}
+
+// ob is a compile-time constant after unrolling, so the switch folds away
+__device__ inline v16f mma_sel(int ob, v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  switch (ob) {
+    case 0: return mma_fp6_fp4<0>(a, b, c, sa, sb);
+    case 1: return mma_fp6_fp4<1>(a, b, c, sa, sb);
+    case 2: return mma_fp6_fp4<2>(a, b, c, sa, sb);
+    default: return mma_fp6_fp4<3>(a, b, c, sa, sb);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gfx950 packed FP6 conversions.  cvt_fp6x32: 32 fp32 values -> 32 E2M3 codes
+// of v / 2^e (e = the exponent of `scale`), rounded to nearest even and
+// saturated at 7.5; the two 16-value halves are interleaved, so passing the
+// even and the odd elements puts element i at bits 6i.  dequant_fp6x32 is the
+// inverse (code value times 2^e).  Written as inline asm with an early-clobber
+// output: the 6- and 32-register results must not overlap the sources, which
+// the instructions still read while writing.
+// ---------------------------------------------------------------------------
+__device__ inline v6i cvt_fp6x32(const v16f even, const v16f odd, float scale) {
+  v6i c;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(c) : "v"(even), "v"(odd), "v"(scale));
+  return c;
+}
+
+__device__ inline v32f dequant_fp6x32(const v6i c, float scale) {
+  v32f d;
+  asm("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(d) : "v"(c), "v"(scale));
+  return d;
+}
+
+// hi/lo MX6 split of one 32-value block held by one lane: hi = E2M3(v) with the block scale
+// 2^(floor(log2 amax) - 2), lo = the same of v - hi.  Codes element i at bits 6i.
+struct Fp6Split {
+  v6i hi, lo;
+  uint32_t s_hi, s_lo;
+};
+
+__device__ __forceinline__ Fp6Split split_fp6x32(const float (&v)[32]) {
+  Fp6Split r;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  r.s_hi = e2m3_scale_byte(amax);
+  const float sh = e8m0_to_float(r.s_hi);
+  v16f ev, od;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    ev[j] = v[2 * j];
+    od[j] = v[2 * j + 1];
+  }
+  r.hi = cvt_fp6x32(ev, od, sh);
+  const v32f d = dequant_fp6x32(r.hi, sh);
+  float amax2 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    ev[j] = v[2 * j] - d[2 * j];
+    od[j] = v[2 * j + 1] - d[2 * j + 1];
+    amax2 = fmaxf(amax2, fmaxf(fabsf(ev[j]), fabsf(od[j])));
+  }
+  r.s_lo = e2m3_scale_byte(amax2);
+  r.lo = cvt_fp6x32(ev, od, e8m0_to_float(r.s_lo));
+  return r;
+}
+
+}  // namespace moe

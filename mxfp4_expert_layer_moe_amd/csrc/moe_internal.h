@@ -46,12 +46,17 @@ __host__ __device__ inline size_t w_scales_per_expert(int N, int K) {
 // ---------------------------------------------------------------------------
 // Row-tile table (written by the permutation, read by the expert GEMMs): the
 // grouped rows of every expert are cut into tiles of tile_rows() rows; slot s
-// holds {expert (-1 = empty slot), first grouped position p0, rows, 0} and then,
-// for each row i < rows, the assignment id perm[p0 + i].  Decode-sized batches
-// (at most 8 rows per expert on average) use 8-row tiles, larger ones 32.
+// (tile_ints() int32 each) holds {expert (-1 = empty slot), first grouped
+// position p0, rows, tiles in use} and then the assignment id perm[p0 + i] of
+// each row i < rows.  Decode-sized batches (at most 8 rows per expert on
+// average) use 8-row tiles, larger ones 128-row tiles.
 // ---------------------------------------------------------------------------
-constexpr int kTileInts = 48;      // 4 header ints + up to 32 assignment ids, padded to 192 bytes
-__host__ __device__ inline int tile_rows(long long n_assign, int E) { return n_assign <= 8LL * E ? 8 : 32; }
+constexpr int kTileInts = 48;      // slot of an 8-row tile: 4 header ints + ids, padded to 192 bytes
+constexpr int kPrefillRows = 128;  // rows per tile of large batches
+__host__ __device__ inline int tile_rows(long long n_assign, int E) {
+  return n_assign <= 8LL * E ? 8 : kPrefillRows;
+}
+__host__ __device__ inline int tile_ints(int bm) { return 4 + bm > kTileInts ? 4 + bm : kTileInts; }
 __host__ __device__ inline long long tile_slots(long long n_assign, int E) {
   const int bm = tile_rows(n_assign, E);
   return (n_assign + bm - 1) / bm + (E < n_assign ? E : n_assign);
@@ -181,6 +186,9 @@ hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipS
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
                        void* out, hipStream_t s);
+hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
+                               const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
+                               const uint8_t* scales, const float* topk_w, void* out, hipStream_t s);
 hipError_t launch_combine(int T, int D, int k, const float* y_perm, const int32_t* inv, void* y,
                           int y_bf16, hipStream_t s);
 

@@ -28,6 +28,7 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int ti = tile_ints(bm);
 
   for (int e = tid; e < E; e += kPermThreads) cnt[e] = 0;
   __syncthreads();
@@ -77,9 +78,10 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
     if (lane == 0) tstart[E] = tcarry;
   }
   __syncthreads();
-  // tile headers: slot s of expert e (binary search over tstart); slots past the last tile are empty
+  // tile headers: slot s of expert e (binary search over tstart); slots past the last tile are
+  // empty.  Every header's 4th field holds the number of tiles in use.
   for (int s = tid; s < slots; s += kPermThreads) {
-    int4 h = make_int4(-1, 0, 0, 0);
+    int4 h = make_int4(-1, 0, 0, tstart[E]);
     if (s < tstart[E]) {
       int lo = 0, hi = E - 1;                       // largest e with tstart[e] <= s
       while (lo < hi) {
@@ -87,9 +89,9 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
         if (tstart[mid] <= s) lo = mid; else hi = mid - 1;
       }
       const int t = s - tstart[lo];
-      h = make_int4(lo, off0[lo] + t * bm, min(bm, cnt[lo] - t * bm), 0);
+      h = make_int4(lo, off0[lo] + t * bm, min(bm, cnt[lo] - t * bm), tstart[E]);
     }
-    *reinterpret_cast<int4*>(tiles + (size_t)s * kTileInts) = h;
+    *reinterpret_cast<int4*>(tiles + (size_t)s * ti) = h;
   }
 
   // ---- stable scatter, chunk by chunk --------------------------------------
@@ -125,7 +127,7 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
         perm[pos] = a;
         inv[a] = pos;
         const int r = pos - off0[e];
-        tiles[(size_t)(tstart[e] + r / bm) * kTileInts + 4 + r % bm] = a;
+        tiles[(size_t)(tstart[e] + r / bm) * ti + 4 + r % bm] = a;
       }
       __syncthreads();
       for (int e2 = tid; e2 < E; e2 += kPermThreads) {

@@ -30,10 +30,13 @@ def run_gpu(layer, stream=None) -> dict:
 
 def check_tiles(tiles: np.ndarray, offsets: np.ndarray, perm: np.ndarray, n: int, E: int):
     """The row-tile table (include/moe_mxfp4.h): every expert's grouped rows cut into tiles of
-    8 rows (n <= 8E) or 32 rows, in expert order, each listing its assignment ids; then empty slots."""
-    bm = 8 if n <= 8 * E else 32
+    8 rows (n <= 8E, 48 ints per slot) or 128 rows (132 ints per slot), in expert order; each slot
+    holds {expert, first position, rows, tiles in use} and the assignment id of every row; then
+    empty slots (expert -1)."""
+    bm = 8 if n <= 8 * E else 128
+    ints = max(48, 4 + bm)
     slots = -(-n // bm) + min(E, n)
-    t = tiles.reshape(-1, 48)[:slots]
+    t = tiles[: slots * ints].reshape(slots, ints)
     s = 0
     for e in range(E):
         for p0 in range(int(offsets[e]), int(offsets[e + 1]), bm):
@@ -41,6 +44,7 @@ def check_tiles(tiles: np.ndarray, offsets: np.ndarray, perm: np.ndarray, n: int
             assert list(t[s, :3]) == [e, p0, rows], (s, t[s, :4], e, p0, rows)
             assert np.array_equal(t[s, 4:4 + rows], perm[p0:p0 + rows])
             s += 1
+    assert np.all(t[:, 3] == s), "every slot records the number of tiles in use"
     assert np.all(t[s:, 0] == -1)
 
 

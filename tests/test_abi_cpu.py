@@ -93,9 +93,11 @@ def test_bad_arguments_rejected_before_launch(L):
     assert L.moe_permute(d, 4, A, A, A, A, A, None, None) == M.MOE_EINVAL             # no tile table
     assert L.moe_permute(d, 4, A, A, A, A, A, A + 4, None) == M.MOE_EINVAL            # misaligned tiles
     assert L.moe_permute(d, 0, A, A, A, A, A, A, None) == M.MOE_OK
-    # tile table: 8-row tiles at decode sizes, 32-row tiles beyond 8 rows per expert on average
+    # tile table: 8-row tiles (48-int slots) at decode sizes, 128-row tiles (132-int slots) beyond
+    # 8 rows per expert on average
     assert L.moe_tile_table_bytes(d, 32) == (128 // 8 + 32) * 192
-    assert L.moe_tile_table_bytes(d, 4096) == (16384 // 32 + 32) * 192
+    assert L.moe_tile_table_bytes(d, 4096) == (16384 // 128 + 32) * 132 * 4
+    assert L.moe_tile_table_bytes(d, 4097) == (-(-16388 // 128) + 32) * 132 * 4
     assert L.moe_pack_act(96, 4, A, A, None) == M.MOE_EUNSUPPORTED
     assert L.moe_pack_act(64, 4, A, A + 8, None) == M.MOE_EINVAL
     assert L.moe_pack_act(64, 0, A, A, None) == M.MOE_OK
