@@ -218,9 +218,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     for (int r = 0; r < BM / 2; ++r) {
       if (8 * (r >> 2) >= nrows) break;
       const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-      const float gv = fminf(fmaxf(acc[0][r], -g.limit), g.limit);
-      const float uv = fminf(fmaxf(acc[1][r], -g.limit), g.limit);
-      const float h = bf16_round(gv / (1.0f + expf(-gv)) * uv);
+      const float h = swiglu_bf16(acc[0][r], acc[1][r], g.limit);
       const Split32 sp = split_block32(h, c);
       if (m < nrows) store_split32(out + (size_t)(p0 + m) * orb, u, c, sp);
     }

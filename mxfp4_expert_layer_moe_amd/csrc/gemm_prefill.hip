@@ -17,9 +17,10 @@
 //  - The LDS holds a ring of 4 staged k-tiles. k-tile kt+2 is written from
 //    registers while kt is computed, and kt+4 is loading into registers.
 //    There is one barrier per k-tile.
-//  - Staged layout, per 32-row block: the seven 16-byte pieces of every row's
-//    112-byte chunk, piece-major (piece j of row r at (j*32 + r) * 16). A half
-//    wavefront's operand read then covers 512 contiguous bytes.
+//  - Staged layout: the 128 rows' 112-byte chunks back to back.  The staging
+//    loads give consecutive lanes consecutive 16-byte pieces of a row (each load
+//    instruction reads about 9 whole gathered row chunks), and an operand read
+//    by 8 consecutive rows hits 8 different 16-byte bank groups (7r mod 8).
 //  - Work items (row tile, 512-column group) are dealt to the 8 XCDs in
 //    contiguous blocks, so the workgroups sharing an expert's weights share
 //    an L2.
@@ -47,26 +48,29 @@ constexpr int kPWaveTiles = 4;                         // 32-column weight tiles
 constexpr int kPGroupTiles = 4 * kPWaveTiles;          // per workgroup
 constexpr int kPSlots = 4;                             // staged k-tiles in the LDS ring
 constexpr int kPPieces = kActChunk / 16;               // 16-byte pieces per row chunk (7)
-constexpr int kPBlockBytes = kPPieces * 32 * 16;       // one 32-row block of a staged k-tile
+constexpr int kPBlockBytes = 32 * kActChunk;           // one 32-row block of a staged k-tile
 constexpr int kPStagePieces = kPrefillRows * kPPieces; // 896 pieces per staged k-tile
 constexpr int kPSlotBytes = 1024 * 16;                 // 896 pieces + 128 dummy (4 unconditional per thread)
-constexpr int kPRing = 4;                              // weight k-tiles in flight per wavefront
+constexpr int kPStageAhead = 2;                        // k-tile kt + 2 is written to LDS during k-tile kt
 constexpr int kPEpiStride = 68;                        // floats per row of the transposed h block
 static_assert(kPSlots * kPSlotBytes >= 4 * 32 * kPEpiStride * 4, "h transposition fits the ring");
 
-// FP6 operand from a piece-major staged block: this lane's 24 bytes are bytes [24h, 24h+24) of the
-// hi (or lo) half of its row's chunk, i.e. the 16 bytes of piece p16 and 8 bytes of piece p8.
-__device__ __forceinline__ v8i staged_operand(const uint8_t* blk, int r, int h, int p16, int p8) {
-  const v4i q = *reinterpret_cast<const v4i*>(blk + (p16 * 32 + r) * 16);
-  const uint2 t = *reinterpret_cast<const uint2*>(blk + (p8 * 32 + r) * 16 + 8 * h);
+// FP6 operand of one staged row chunk: lane half h takes bytes [base + 24h, base + 24h + 24)
+// (base 0: hi term, 48: lo term), i.e. 16 bytes at base + 32h and 8 bytes at base + 16 + 8h.
+__device__ __forceinline__ v8i staged_operand(const uint8_t* row, int h, int base) {
+  const v4i q = *reinterpret_cast<const v4i*>(row + base + 32 * h);
+  const uint2 t = *reinterpret_cast<const uint2*>(row + base + 16 + 8 * h);
   const bool up = h != 0;
   v8i v = {up ? (int)t.x : q.x, up ? (int)t.y : q.y, up ? q.x : q.z, up ? q.y : q.w,
            up ? q.z : (int)t.x, up ? q.w : (int)t.y, 0, 0};
   return v;
 }
 
-template <int STAGE, int KTC>
+// NA: activation k-tiles in flight in registers (k-tile t is fetched NA k-tiles before it is
+// written to LDS); P: weight k-tiles in flight per wavefront.  Both divide 8.
+template <int STAGE, int KTC, int NA, int P>
 __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g) {
+  static_assert(8 % NA == 0 && 8 % P == 0 && P >= 4, "ring depths divide the 8-step unroll");
   __shared__ __attribute__((aligned(16))) uint8_t sA[kPSlots * kPSlotBytes];
   __shared__ int srow[kPrefillRows];
   __shared__ float sgate[kPrefillRows];
@@ -105,9 +109,8 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = min(tid + 256 * i, kPStagePieces - 1); // the dummy pieces re-read a real one
-    const int rb = q / (32 * kPPieces);
-    const int rem = q - rb * 32 * kPPieces;
-    aoff[i] = (uint32_t)srow[rb * 32 + (rem & 31)] * g.arb + (uint32_t)(rem >> 5) * 16u;
+    const int row = q / kPPieces;
+    aoff[i] = (uint32_t)srow[row] * g.arb + (uint32_t)(q - row * kPPieces) * 16u;
   }
   auto load_a = [&](const int kt, v4i (&buf)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -138,16 +141,20 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsS, lane * 4, sbase[cb] + grp * 256, 0);
   };
 
-  // ---- prologue: k-tiles 0, 1 staged; 2, 3 in registers; weight ring filled ---------------------
+  // ---- prologue: k-tiles 0, 1 staged; the next NA in registers; weight ring filled -------------
   // Every load index is clamped to the last k-tile, so no load or store depends on K: a k-tile
-  // past the end is staged into a slot nobody reads.
-  v4i abuf[2][4];
-  load_a(0, abuf[0]);
-  load_a(min(1, KT - 1), abuf[1]);
-  v4i bq[kPRing][kPWaveTiles];
+  // past the end is staged into a slot nobody reads.  Register set t % NA holds k-tile t.
+  v4i abuf[NA][4];
+  load_a(0, abuf[0 % NA]);
+  store_a(0, abuf[0 % NA]);
+  load_a(min(1, KT - 1), abuf[1 % NA]);
+  store_a(1, abuf[1 % NA]);
+#pragma unroll
+  for (int t = kPStageAhead; t < kPStageAhead + NA; ++t) load_a(min(t, KT - 1), abuf[t % NA]);
+  v4i bq[P][kPWaveTiles];
   uint32_t sq[2][kPWaveTiles];
 #pragma unroll
-  for (int j = 0; j < kPRing; ++j)
+  for (int j = 0; j < P; ++j)
 #pragma unroll
     for (int cb = 0; cb < kPWaveTiles; ++cb) bq[j][cb] = load_b(cb, min(j, KT - 1));
 #pragma unroll
@@ -155,10 +162,6 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     sq[0][cb] = load_s(cb, 0);
     sq[1][cb] = load_s(cb, min(1, g.KG - 1));
   }
-  store_a(0, abuf[0]);
-  store_a(1, abuf[1]);
-  load_a(min(2, KT - 1), abuf[0]);
-  load_a(min(3, KT - 1), abuf[1]);
   __syncthreads();
 
   v16f acc[4][kPWaveTiles];
@@ -169,27 +172,43 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
 
   const int r32 = lane & 31;
   const int h = lane >> 5;
+  // A operands of (k-tile kt, row block rb) from the staged slot kt % 4
+  struct AOps {
+    v8i hi, lo;
+    uint32_t sh, sl;
+  };
+  auto read_ops = [&](const int kt, const int rb) __attribute__((always_inline)) {
+    const uint8_t* row = sA + (kt & 3) * kPSlotBytes + rb * kPBlockBytes + r32 * kActChunk;
+    AOps o;
+    o.hi = staged_operand(row, h, 0);
+    o.lo = staged_operand(row, h, 48);
+    const uint32_t s4 = *reinterpret_cast<const uint32_t*>(row + 96);
+    o.sh = s4 >> (8 * h);
+    o.sl = s4 >> (16 + 8 * h);
+    return o;
+  };
+  // Operands are read one row block ahead of the matrix instructions that use them; the first
+  // block of k-tile kt + 1 is read before the barrier that ends k-tile kt (its slot was published
+  // before the previous barrier), so no k-tile starts by waiting on LDS.
+  AOps nxt = read_ops(0, 0);
   // k-tile kt, j = kt % 8 (compile-time: selects the register ring slots)
   auto step = [&](const int kt, const int j) __attribute__((always_inline)) {
-    store_a((kt + 2) & 3, abuf[j & 1]);                  // publish k-tile kt + 2
-    load_a(min(kt + 4, KT - 1), abuf[j & 1]);            // fetch k-tile kt + 4
-    const uint8_t* slotp = sA + (kt & 3) * kPSlotBytes;
+    constexpr int D = kPStageAhead;
+    store_a((kt + D) & 3, abuf[(j + D) % NA]);           // publish k-tile kt + D
+    load_a(min(kt + D + NA, KT - 1), abuf[(j + D) % NA]);  // fetch k-tile kt + D + NA
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      const uint8_t* blk = slotp + rb * kPBlockBytes;
-      const v8i ahi = staged_operand(blk, r32, h, h ? 2 : 0, 1);
-      const v8i alo = staged_operand(blk, r32, h, h ? 5 : 3, 4);
-      const uint32_t s4 = *reinterpret_cast<const uint32_t*>(blk + (6 * 32 + r32) * 16);
-      const uint32_t sh = s4 >> (8 * h), sl = s4 >> (16 + 8 * h);
+      const AOps cur = nxt;
+      nxt = rb < 3 ? read_ops(kt, rb + 1) : read_ops(min(kt + 1, KT - 1), 0);
 #pragma unroll
       for (int cb = 0; cb < kPWaveTiles; ++cb) {
-        const v8i bv = b_operand(bq[j & 3][cb]);
-        acc[rb][cb] = mma_sel(j & 3, ahi, bv, acc[rb][cb], sh, sq[(j >> 2) & 1][cb]);
-        acc[rb][cb] = mma_sel(j & 3, alo, bv, acc[rb][cb], sl, sq[(j >> 2) & 1][cb]);
+        const v8i bv = b_operand(bq[j % P][cb]);
+        acc[rb][cb] = mma_sel(j & 3, cur.hi, bv, acc[rb][cb], cur.sh, sq[(j >> 2) & 1][cb]);
+        acc[rb][cb] = mma_sel(j & 3, cur.lo, bv, acc[rb][cb], cur.sl, sq[(j >> 2) & 1][cb]);
       }
     }
 #pragma unroll
-    for (int cb = 0; cb < kPWaveTiles; ++cb) bq[j & 3][cb] = load_b(cb, min(kt + kPRing, KT - 1));
+    for (int cb = 0; cb < kPWaveTiles; ++cb) bq[j % P][cb] = load_b(cb, min(kt + P, KT - 1));
     if ((j & 3) == 3) {                                   // scale group kt/4 done: fetch group kt/4 + 2
 #pragma unroll
       for (int cb = 0; cb < kPWaveTiles; ++cb) sq[(j >> 2) & 1][cb] = load_s(cb, min(kt / 4 + 2, g.KG - 1));
@@ -232,9 +251,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = 8 * (r >> 2) + 4 * h + (r & 3);
-          const float gv = fminf(fmaxf(acc[rb][2 * u2][r], -g.limit), g.limit);
-          const float uv = fminf(fmaxf(acc[rb][2 * u2 + 1][r], -g.limit), g.limit);
-          ep[m * kPEpiStride + u2 * 32 + r32] = bf16_round(gv / (1.0f + expf(-gv)) * uv);
+          ep[m * kPEpiStride + u2 * 32 + r32] = swiglu_bf16(acc[rb][2 * u2][r], acc[rb][2 * u2 + 1][r], g.limit);
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -281,6 +298,15 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   }
 }
 
+#ifndef MOE_PREFILL_NA
+#define MOE_PREFILL_NA 2
+#endif
+#ifndef MOE_PREFILL_P
+#define MOE_PREFILL_P 4
+#endif
+constexpr int kPNA = MOE_PREFILL_NA;
+constexpr int kPP = MOE_PREFILL_P;
+
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
                                const uint8_t* scales, const float* topk_w, void* out, hipStream_t s) {
@@ -306,12 +332,18 @@ hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, flo
   g.scales_per_expert = w_scales_per_expert(N, K);
   const long long items = tile_slots((long long)T * k, E) * g.ngroups;
   const dim3 grid((unsigned)((items + 7) / 8 * 8));
+#ifdef MOE_PREFILL_GENERIC_ONLY
+  g.KT = g.KT + 0 * 45;
+  if (stage == 0) expert_gemm_prefill_kernel<0, 0, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
+  else expert_gemm_prefill_kernel<1, 0, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
+  return hipGetLastError();
+#endif
   if (stage == 0) {
-    if (g.KT == 45) expert_gemm_prefill_kernel<0, 45><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_prefill_kernel<0, 0><<<grid, dim3(256), 0, s>>>(g);
+    if (g.KT == 45) expert_gemm_prefill_kernel<0, 45, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_prefill_kernel<0, 0, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
   } else {
-    if (g.KT == 45) expert_gemm_prefill_kernel<1, 45><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_prefill_kernel<1, 0><<<grid, dim3(256), 0, s>>>(g);
+    if (g.KT == 45) expert_gemm_prefill_kernel<1, 45, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_prefill_kernel<1, 0, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
   }
   return hipGetLastError();
 }

@@ -104,6 +104,16 @@ __device__ inline float bf16_round(float v) {
   return __uint_as_float(u);
 }
 
+// SwiGLU of one (gate, up) pair: h = bf16(silu(clamp(g)) * clamp(u)), both pre-activations
+// clamped to [-limit, limit].  silu(g) = g / (1 + e^-g) uses the hardware exp2 and reciprocal
+// (about 1 ulp each in fp32), far inside the bf16 rounding of h.
+__device__ inline float swiglu_bf16(float g, float u, float limit) {
+  const float gv = fminf(fmaxf(g, -limit), limit);
+  const float uv = fminf(fmaxf(u, -limit), limit);
+  const float e = __builtin_amdgcn_exp2f(gv * -1.4426950408889634f);
+  return bf16_round(gv * __builtin_amdgcn_rcpf(1.0f + e) * uv);
+}
+
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ inline float half_wave_max(float v) {
