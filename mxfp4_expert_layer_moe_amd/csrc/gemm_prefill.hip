@@ -55,15 +55,31 @@ constexpr int kPStageAhead = 2;                        // k-tile kt + 2 is writt
 constexpr int kPEpiStride = 68;                        // floats per row of the transposed h block
 static_assert(kPSlots * kPSlotBytes >= 4 * 32 * kPEpiStride * 4, "h transposition fits the ring");
 
-// FP6 operand of one staged row chunk: lane half h takes bytes [base + 24h, base + 24h + 24)
-// (base 0: hi term, 48: lo term), i.e. 16 bytes at base + 32h and 8 bytes at base + 16 + 8h.
-__device__ __forceinline__ v8i staged_operand(const uint8_t* row, int h, int base) {
-  const v4i q = *reinterpret_cast<const v4i*>(row + base + 32 * h);
-  const uint2 t = *reinterpret_cast<const uint2*>(row + base + 16 + 8 * h);
-  const bool up = h != 0;
-  v8i v = {up ? (int)t.x : q.x, up ? (int)t.y : q.y, up ? q.x : q.z, up ? q.y : q.w,
-           up ? q.z : (int)t.x, up ? q.w : (int)t.y, 0, 0};
+// Matrix-instruction pairing.  Each 64-wide k-tile holds two 32-value blocks b = 0, 1 of the
+// activation, each stored as hi + lo FP6 terms.  One MFMA per block: lanes 0-31 supply the hi term
+// and lanes 32-63 the lo term of block b as the instruction's two K halves, and the weight operand
+// holds block b in both halves, so the instruction sums (hi + lo) * w over the block.  A lane half's
+// 24-byte term then starts at the same offset pattern in both halves (no per-lane reordering).
+__device__ __forceinline__ v8i fp6_operand(v4i q, uint2 t, bool q_first) {
+  v8i v;
+  if (q_first) v = {q.x, q.y, q.z, q.w, (int)t.x, (int)t.y, 0, 0};
+  else v = {(int)t.x, (int)t.y, q.x, q.y, q.z, q.w, 0, 0};
   return v;
+}
+
+// both halves of the weight register: [block 0 | block 0] and [block 1 | block 1]
+__device__ __forceinline__ void split_halves(const v4i x, v4i& b0, v4i& b1) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x[d], (unsigned)x[d], false, false);
+    b0[d] = (int)r[0];
+    b1[d] = (int)r[1];
+  }
+}
+__device__ __forceinline__ void split_halves(const uint32_t x, uint32_t& s0, uint32_t& s1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  s0 = r[0];
+  s1 = r[1];
 }
 
 // NA: activation k-tiles in flight in registers (k-tile t is fetched NA k-tiles before it is
@@ -153,6 +169,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   for (int t = kPStageAhead; t < kPStageAhead + NA; ++t) load_a(min(t, KT - 1), abuf[t % NA]);
   v4i bq[P][kPWaveTiles];
   uint32_t sq[2][kPWaveTiles];
+  uint32_t sqd[kPWaveTiles][2];                          // current scale group, per block
 #pragma unroll
   for (int j = 0; j < P; ++j)
 #pragma unroll
@@ -173,45 +190,72 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   const int r32 = lane & 31;
   const int h = lane >> 5;
   // A operands of (k-tile kt, row block rb) from the staged slot kt % 4
+  // block b's term of this lane half (h = 0: hi, 1: lo) sits at bytes [48h + 24b, 48h + 24b + 24)
+  // of the row chunk; the scale bytes are [hi0, hi1, lo0, lo1] at 96
   struct AOps {
-    v8i hi, lo;
-    uint32_t sh, sl;
+    v8i a0, a1;
+    uint32_t s0, s1;
   };
   auto read_ops = [&](const int kt, const int rb) __attribute__((always_inline)) {
-    const uint8_t* row = sA + (kt & 3) * kPSlotBytes + rb * kPBlockBytes + r32 * kActChunk;
+    const uint8_t* row = sA + (kt & 3) * kPSlotBytes + rb * kPBlockBytes + r32 * kActChunk + 48 * h;
     AOps o;
-    o.hi = staged_operand(row, h, 0);
-    o.lo = staged_operand(row, h, 48);
-    const uint32_t s4 = *reinterpret_cast<const uint32_t*>(row + 96);
-    o.sh = s4 >> (8 * h);
-    o.sl = s4 >> (16 + 8 * h);
+    const v4i q0 = *reinterpret_cast<const v4i*>(row);
+    const v4i t01 = *reinterpret_cast<const v4i*>(row + 16);
+    const v4i q1 = *reinterpret_cast<const v4i*>(row + 32);
+    o.a0 = fp6_operand(q0, make_uint2(t01.x, t01.y), true);
+    o.a1 = fp6_operand(q1, make_uint2(t01.z, t01.w), false);
+    const uint32_t s4 = *reinterpret_cast<const uint32_t*>(row - 48 * h + 96);
+    o.s0 = s4 >> (16 * h);
+    o.s1 = s4 >> (8 + 16 * h);
     return o;
   };
-  // Operands are read one row block ahead of the matrix instructions that use them; the first
-  // block of k-tile kt + 1 is read before the barrier that ends k-tile kt (its slot was published
-  // before the previous barrier), so no k-tile starts by waiting on LDS.
+  // Software pipeline of one k-tile (kt, j = kt % 8, compile-time ring slots), in four phases of
+  // eight matrix instructions (one row block each).  Other work rides in the phases' shadows:
+  //  - operands are read one row block ahead; the next k-tile's first block is read before this
+  //    k-tile's barrier (its slot was published before the previous barrier);
+  //  - phase 0 publishes staged k-tile kt + 2, phase 1 fetches k-tile kt + 2 + NA;
+  //  - phase 2 splits the next k-tile's weight registers by block (and the next scale group);
+  //  - phase 3 refills the weight ring slot just consumed.
+  // A scheduling barrier between phases keeps each phase's work next to its matrix instructions.
   AOps nxt = read_ops(0, 0);
-  // k-tile kt, j = kt % 8 (compile-time: selects the register ring slots)
+  v4i bw[kPWaveTiles][2];
+#pragma unroll
+  for (int cb = 0; cb < kPWaveTiles; ++cb) {
+    split_halves(bq[0][cb], bw[cb][0], bw[cb][1]);
+    split_halves(sq[0][cb], sqd[cb][0], sqd[cb][1]);
+  }
   auto step = [&](const int kt, const int j) __attribute__((always_inline)) {
     constexpr int D = kPStageAhead;
-    store_a((kt + D) & 3, abuf[(j + D) % NA]);           // publish k-tile kt + D
-    load_a(min(kt + D + NA, KT - 1), abuf[(j + D) % NA]);  // fetch k-tile kt + D + NA
+    v4i bwn[kPWaveTiles][2];
+    uint32_t sqn[kPWaveTiles][2];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const AOps cur = nxt;
       nxt = rb < 3 ? read_ops(kt, rb + 1) : read_ops(min(kt + 1, KT - 1), 0);
 #pragma unroll
       for (int cb = 0; cb < kPWaveTiles; ++cb) {
-        const v8i bv = b_operand(bq[j % P][cb]);
-        acc[rb][cb] = mma_sel(j & 3, cur.hi, bv, acc[rb][cb], cur.sh, sq[(j >> 2) & 1][cb]);
-        acc[rb][cb] = mma_sel(j & 3, cur.lo, bv, acc[rb][cb], cur.sl, sq[(j >> 2) & 1][cb]);
+        acc[rb][cb] = mma_sel(j & 3, cur.a0, b_operand(bw[cb][0]), acc[rb][cb], cur.s0, sqd[cb][0]);
+        acc[rb][cb] = mma_sel(j & 3, cur.a1, b_operand(bw[cb][1]), acc[rb][cb], cur.s1, sqd[cb][1]);
       }
-    }
+      if (rb == 0) store_a((kt + D) & 3, abuf[(j + D) % NA]);                  // publish kt + D
+      if (rb == 1) load_a(min(kt + D + NA, KT - 1), abuf[(j + D) % NA]);        // fetch kt + D + NA
+      if (rb == 2) {
 #pragma unroll
-    for (int cb = 0; cb < kPWaveTiles; ++cb) bq[j % P][cb] = load_b(cb, min(kt + P, KT - 1));
-    if ((j & 3) == 3) {                                   // scale group kt/4 done: fetch group kt/4 + 2
+        for (int cb = 0; cb < kPWaveTiles; ++cb) {
+          split_halves(bq[(j + 1) % P][cb], bwn[cb][0], bwn[cb][1]);
+          // the next k-tile opens a scale group: its dwords (loaded a group ago) by block
+          if ((j & 3) == 3) split_halves(sq[((j >> 2) + 1) & 1][cb], sqn[cb][0], sqn[cb][1]);
+        }
+      }
+      if (rb == 3) {
 #pragma unroll
-      for (int cb = 0; cb < kPWaveTiles; ++cb) sq[(j >> 2) & 1][cb] = load_s(cb, min(kt / 4 + 2, g.KG - 1));
+        for (int cb = 0; cb < kPWaveTiles; ++cb) bq[j % P][cb] = load_b(cb, min(kt + P, KT - 1));
+        if ((j & 3) == 3) {                               // scale group kt/4 done: fetch group kt/4 + 2
+#pragma unroll
+          for (int cb = 0; cb < kPWaveTiles; ++cb) sq[(j >> 2) & 1][cb] = load_s(cb, min(kt / 4 + 2, g.KG - 1));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Pin this k-tile's matrix instructions before the barrier: they have no memory side effects,
     // so instruction selection would otherwise gather all of them after the unrolled loop (and keep
@@ -222,6 +266,15 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
       for (int cb = 0; cb < kPWaveTiles; ++cb) asm volatile("" : "+a"(acc[rb][cb]));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int cb = 0; cb < kPWaveTiles; ++cb) {
+      bw[cb][0] = bwn[cb][0];
+      bw[cb][1] = bwn[cb][1];
+      if ((j & 3) == 3) {
+        sqd[cb][0] = sqn[cb][0];
+        sqd[cb][1] = sqn[cb][1];
+      }
+    }
   };
   if constexpr (KTC > 0) {
 #pragma unroll
@@ -234,9 +287,9 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     }
   }
 
+  __syncthreads();                                       // every wavefront is done with the ring
   if constexpr (STAGE == 0) {
     // ---- SwiGLU, transpose through LDS, hi/lo FP6 split of each 32-value block of h ------------
-    // (the ring is free: every wavefront passed the last k-tile's barrier)
     float* ep = reinterpret_cast<float*>(sA) + wave * 32 * kPEpiStride;
     const int I = g.out_K;
     const uint32_t orb = (uint32_t)act_row_bytes(I);
