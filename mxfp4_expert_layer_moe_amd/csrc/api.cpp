@@ -43,7 +43,7 @@ struct WsLayout {
 
 size_t tile_table_bytes(const moe_dims* d, int32_t T) {
   const long long n = (long long)T * d->top_k;
-  return (size_t)tile_slots(n, d->n_experts) * tile_ints(tile_rows(n, d->n_experts)) * 4;
+  return (size_t)(tile_buffer_ints(n, d->n_experts) + 3) / 4 * 16;
 }
 
 WsLayout ws_layout(const moe_dims* d, int32_t T) {

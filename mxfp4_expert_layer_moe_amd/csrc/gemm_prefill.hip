@@ -317,18 +317,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
       __builtin_amdgcn_wave_barrier();
       const Fp6Split sp = split_fp6x32(v);
       const int m = rb * 32 + r32;
-      if (m < nrows && 2 * ublk < g.nt) {
-        uint8_t* chunk = out + (size_t)(p0 + m) * orb + (size_t)(ublk >> 1) * kActChunk;
-        const int half = ublk & 1;
-        uint2* ph = reinterpret_cast<uint2*>(chunk + 24 * half);
-        uint2* pl = reinterpret_cast<uint2*>(chunk + 48 + 24 * half);
-        ph[0] = make_uint2(sp.hi[0], sp.hi[1]); ph[1] = make_uint2(sp.hi[2], sp.hi[3]);
-        ph[2] = make_uint2(sp.hi[4], sp.hi[5]);
-        pl[0] = make_uint2(sp.lo[0], sp.lo[1]); pl[1] = make_uint2(sp.lo[2], sp.lo[3]);
-        pl[2] = make_uint2(sp.lo[4], sp.lo[5]);
-        chunk[96 + half] = (uint8_t)sp.s_hi;
-        chunk[98 + half] = (uint8_t)sp.s_lo;
-      }
+      if (m < nrows && 2 * ublk < g.nt) store_fp6_block(out + (size_t)(p0 + m) * orb, ublk, sp);
     }
   } else {
     // ---- down: scale row p by its gate weight, store fp32 ---------------------------------------

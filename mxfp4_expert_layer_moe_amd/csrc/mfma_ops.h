@@ -100,4 +100,46 @@ __device__ __forceinline__ Fp6Split split_fp6x32(const float (&v)[32]) {
   return r;
 }
 
+// Store the split block b of a packed activation row (format in moe_mxfp4.h): the chunk of k-tile
+// b / 2 holds hi codes at 24 * (b % 2), lo codes at 48 + 24 * (b % 2), scale bytes at 96 + b % 2
+// (hi) and 98 + b % 2 (lo).  Rows are 8-byte aligned, so the 24-byte code groups go out as
+// three 8-byte stores.
+__device__ __forceinline__ void store_fp6_block(uint8_t* row, int b, const Fp6Split& sp) {
+  uint8_t* chunk = row + (size_t)(b >> 1) * kActChunk;
+  const int half = b & 1;
+  uint2* ph = reinterpret_cast<uint2*>(chunk + 24 * half);
+  uint2* pl = reinterpret_cast<uint2*>(chunk + 48 + 24 * half);
+  ph[0] = make_uint2(sp.hi[0], sp.hi[1]);
+  ph[1] = make_uint2(sp.hi[2], sp.hi[3]);
+  ph[2] = make_uint2(sp.hi[4], sp.hi[5]);
+  pl[0] = make_uint2(sp.lo[0], sp.lo[1]);
+  pl[1] = make_uint2(sp.lo[2], sp.lo[3]);
+  pl[2] = make_uint2(sp.lo[4], sp.lo[5]);
+  chunk[96 + half] = (uint8_t)sp.s_hi;
+  chunk[98 + half] = (uint8_t)sp.s_lo;
+}
+
+// Split block `blk` (= row * K/32 + b) of bf16 rows [rows][K] (16-byte aligned) in one lane:
+// four 16-byte loads, the hi/lo split, the stores.  Lanes past the last block do nothing.
+__device__ __forceinline__ void pack_block_lane(const uint16_t* __restrict__ a, int K, long long nblocks,
+                                                long long blk, uint8_t* __restrict__ packed) {
+  if (blk >= nblocks) return;
+  const int nb = K / kBlock;
+  const long long row = blk / nb;
+  const int b = (int)(blk - row * nb);
+  const uint4* src = reinterpret_cast<const uint4*>(a + (size_t)row * K + (size_t)b * kBlock);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = src[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+      v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
+  store_fp6_block(packed + (size_t)row * act_row_bytes(K), b, split_fp6x32(v));
+}
+
 }  // namespace moe

@@ -61,6 +61,16 @@ __host__ __device__ inline long long tile_slots(long long n_assign, int E) {
   const int bm = tile_rows(n_assign, E);
   return (n_assign + bm - 1) / bm + (E < n_assign ? E : n_assign);
 }
+// The table buffer continues with the grouping's scratch: per-workgroup expert counts [G][E]
+// (G = workgroups of 1024 assignments) and the first tile slot of every expert [E + 1].
+constexpr int kPermChunk = 1024;   // assignments per grouping workgroup (one per thread)
+__host__ __device__ inline long long perm_groups(long long n_assign) { return (n_assign + kPermChunk - 1) / kPermChunk; }
+__host__ __device__ inline long long tile_table_ints(long long n_assign, int E) {
+  return tile_slots(n_assign, E) * tile_ints(tile_rows(n_assign, E));
+}
+__host__ __device__ inline long long tile_buffer_ints(long long n_assign, int E) {
+  return tile_table_ints(n_assign, E) + perm_groups(n_assign) * E + E + 1;
+}
 
 // ---------------------------------------------------------------------------
 // FP6 E2M3 encoding of v / 2^e (round to nearest even, saturate at 7.5).
@@ -165,18 +175,6 @@ __device__ inline void store_split32(uint8_t* row, int b, int c, const Split32& 
   }
 }
 
-// Pack block hw (= row * K/32 + b) of bf16 rows [rows][K]: one half-wavefront, lane c holds element c.
-// All 64 lanes call it; a half-wave past the last block only joins the lane exchanges.
-__device__ inline void pack_block_halfwave(const uint16_t* __restrict__ a, int K, int rows, long long hw, int c,
-                                           uint8_t* __restrict__ packed) {
-  const int nblk = K / kBlock;
-  const bool live = hw < (long long)rows * nblk;
-  const int row = live ? (int)(hw / nblk) : 0;
-  const int b = live ? (int)(hw - (long long)row * nblk) : 0;
-  const float v = live ? bf16_bits_to_float(a[(size_t)row * K + (size_t)b * kBlock + c]) : 0.0f;
-  const Split32 sp = split_block32(v, c);
-  if (live) store_split32(packed + (size_t)row * act_row_bytes(K), b, c, sp);
-}
 
 // ---------------------------------------------------------------------------
 // Host-side launchers (one translation unit each); return the launch status.

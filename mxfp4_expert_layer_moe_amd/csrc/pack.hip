@@ -7,25 +7,24 @@
 // same encoding of what hi left over.  Both terms run at the FP4 x FP6 issue
 // rate, so the expert GEMMs run two MFMAs per weight tile instead of one.
 //
-// One half-wavefront per 32-value block, one value per lane: the block maxima
-// are half-wave reductions and the 6-bit codes are gathered into 24-bit groups
-// with two lane exchanges (the same routine the gate/up epilogue uses for h).
-#include "moe_internal.h"
+// One lane per 32-value block: the lane loads its 64 bytes, finds the block
+// maxima itself and encodes the 32 values of each term with one packed
+// conversion instruction (split_fp6x32).
+#include "mfma_ops.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void pack_act_kernel(int K, int rows, const uint16_t* __restrict__ a,
+__global__ __launch_bounds__(256) void pack_act_kernel(int K, long long nblocks, const uint16_t* __restrict__ a,
                                                        uint8_t* __restrict__ packed) {
-  const long long hw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;   // half-wave = one block
-  pack_block_halfwave(a, K, rows, hw, threadIdx.x & 31, packed);
+  pack_block_lane(a, K, nblocks, (long long)blockIdx.x * blockDim.x + threadIdx.x, packed);
 }
 
 hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipStream_t s) {
-  const long long n = (long long)rows * (K / kBlock) * 32;      // threads
+  const long long n = (long long)rows * (K / kBlock);          // blocks = threads
   if (n == 0) return hipSuccess;
   const int threads = 256;
   const long long blocks = (n + threads - 1) / threads;
-  pack_act_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(K, rows, a, packed);
+  pack_act_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(K, n, a, packed);
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@
 //     ||x_t|| ||w_e|| by Cauchy-Schwarz), so the result is the float64
 //     selection at any input scale.  Gates are the softmax of the selected
 //     float64 scores.
+#include "mfma_ops.h"
 #include "permute_body.h"
 
 namespace moe {
@@ -94,7 +95,7 @@ size_t route_workspace_bytes(int T, int D, int E) {
 }
 
 // Workgroups past the logit tiles (when xpack is given) split x into the packed activation
-// format for the gate/up GEMM instead: 32 blocks of 32 values per workgroup.
+// format for the gate/up GEMM instead: one 32-value block per lane.
 __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, int D, int E, int KW,
                                                                          const uint16_t* __restrict__ x,
                                                                          const float* __restrict__ wr,
@@ -105,9 +106,9 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, i
                                                                          uint8_t* __restrict__ xpack) {
   __shared__ double red[8][32][33];          // K-partials: waves 0..7, then 8..15 added in place
   __shared__ float rsq[kLogitWaves][2][32];  // partial ||x_t||^2 (0) and ||w_e||^2 (1)
-  if ((int)blockIdx.x >= logit_wgs) {        // activation split (no barriers on this path)
-    const long long hw = (long long)(blockIdx.x - logit_wgs) * (kLogitWaves * 2) + (threadIdx.x >> 5);
-    pack_block_halfwave(x, D, T, hw, threadIdx.x & 31, xpack);
+  if ((int)blockIdx.x >= logit_wgs) {        // activation split, one block per lane (no barriers)
+    const long long blk = (long long)(blockIdx.x - logit_wgs) * (kLogitWaves * 64) + threadIdx.x;
+    pack_block_lane(x, D, (long long)T * (D / kBlock), blk, xpack);
     return;
   }
   const int tid = threadIdx.x;
@@ -414,8 +415,8 @@ static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const fl
   *xsq = reinterpret_cast<float*>(base + L.xsq);
   *wsq = reinterpret_cast<float*>(base + L.wsq);
   const int logit_wgs = ((T + kRouteTokens - 1) / kRouteTokens) * ((E + 31) / 32) * *KW;
-  const long long pack_halfwaves = xpack ? (long long)T * (D / kBlock) : 0;
-  const long long pack_wgs = (pack_halfwaves + 2 * kLogitWaves - 1) / (2 * kLogitWaves);
+  const long long pack_blocks = xpack ? (long long)T * (D / kBlock) : 0;
+  const long long pack_wgs = (pack_blocks + kLogitWaves * 64 - 1) / (kLogitWaves * 64);
   route_logits_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kLogitWaves * 64), 0, s>>>(
       T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack);
   return hipGetLastError();
