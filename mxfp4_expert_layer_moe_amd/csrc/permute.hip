@@ -68,10 +68,15 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(int n, int E, i
   const int wave = tid >> 6;
   for (int e = tid; e < E; e += kPermThreads) {
     int run = 0;
-    for (int g = 0; g < G; ++g) {
-      const int v = hist[(size_t)g * E + e];
-      hist[(size_t)g * E + e] = run;
-      run += v;
+    for (int g0 = 0; g0 < G; g0 += 8) {                 // eight independent loads per round trip
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = g0 + i < G ? hist[(size_t)(g0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (g0 + i < G) hist[(size_t)(g0 + i) * E + e] = run;
+        run += v[i];
+      }
     }
     cnt[e] = run;
   }
