@@ -13,7 +13,7 @@
 // workgroup learns everything about its rows with one load.
 //
 // Batches of up to 1024 assignments: one workgroup does everything
-// (permute_body.h).  Larger batches: three kernels over workgroups of 1024
+// (permute_body.h; 256 threads up to 256 assignments, else 1024).  Larger batches: three kernels over workgroups of 1024
 // consecutive assignments.
 //   1. count: each workgroup's expert histogram (LDS atomics, order-free);
 //   2. scan: one workgroup turns the histograms into each workgroup's first
@@ -28,14 +28,15 @@
 
 namespace moe {
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(int n, int E, int bm, int slots,
-                                                               const int32_t* __restrict__ idx,
-                                                               int32_t* __restrict__ counts,
-                                                               int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ perm,
-                                                               int32_t* __restrict__ inv,
-                                                               int32_t* __restrict__ tiles) {
-  permute_group(n, E, bm, slots, idx, counts, offsets, perm, inv, tiles);
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void permute_kernel(int n, int E, int bm, int slots,
+                                                         const int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ perm,
+                                                         int32_t* __restrict__ inv,
+                                                         int32_t* __restrict__ tiles) {
+  permute_group<THREADS>(n, E, bm, slots, idx, counts, offsets, perm, inv, tiles);
 }
 
 __global__ __launch_bounds__(kPermThreads) void perm_count_kernel(int n, int E, const int32_t* __restrict__ idx,
@@ -169,9 +170,13 @@ hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* coun
   const long long n = (long long)T * k;
   const int bm = tile_rows(n, E);
   const int slots = (int)tile_slots(n, E);
+  if (n <= 256) {
+    permute_kernel<256><<<dim3(1), dim3(256), 0, s>>>((int)n, E, bm, slots, idx, counts, offsets, perm, inv, tiles);
+    return hipGetLastError();
+  }
   if (n <= kPermChunk) {
-    permute_kernel<<<dim3(1), dim3(kPermThreads), 0, s>>>((int)n, E, bm, slots, idx, counts, offsets, perm, inv,
-                                                          tiles);
+    permute_kernel<kPermThreads><<<dim3(1), dim3(kPermThreads), 0, s>>>((int)n, E, bm, slots, idx, counts, offsets,
+                                                                        perm, inv, tiles);
     return hipGetLastError();
   }
   const int G = (int)perm_groups(n);

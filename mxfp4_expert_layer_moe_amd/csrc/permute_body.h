@@ -1,7 +1,6 @@
 // Grouping of the (token, expert) assignments by expert, executed by one
-// workgroup of kPermThreads threads (see permute.hip for the method).  Shared
-// by the stand-alone permutation kernel and the fused select + permutation
-// kernel of small batches.
+// workgroup of THREADS threads (see permute.hip for the method): the whole
+// grouping of batches of up to 1024 assignments, in one launch.
 #pragma once
 #include "moe_internal.h"
 
@@ -11,6 +10,7 @@ constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kPermRegs = 32;          // assignments held per thread per pass
 
+template <int THREADS>
 __device__ inline void permute_group(int n, int E, int bm, int slots,
                                      const int32_t* __restrict__ idx,
                                      int32_t* __restrict__ counts,
@@ -22,7 +22,7 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
   __shared__ int base[kMaxExperts];
   __shared__ int off0[kMaxExperts];
   __shared__ int tstart[kMaxExperts + 1];
-  __shared__ int wcnt[kPermWaves][kMaxExperts];
+  __shared__ int wcnt[(THREADS / 64)][kMaxExperts];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -30,11 +30,11 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   const int ti = tile_ints(bm);
 
-  for (int e = tid; e < E; e += kPermThreads) cnt[e] = 0;
+  for (int e = tid; e < E; e += THREADS) cnt[e] = 0;
   __syncthreads();
 
   // ---- histogram (integer LDS atomics: the totals do not depend on order) ----
-  for (int a = tid; a < n; a += kPermThreads) {
+  for (int a = tid; a < n; a += THREADS) {
     const int e = idx[a];
     if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
   }
@@ -80,7 +80,7 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
   __syncthreads();
   // tile headers: slot s of expert e (binary search over tstart); slots past the last tile are
   // empty.  Every header's 4th field holds the number of tiles in use.
-  for (int s = tid; s < slots; s += kPermThreads) {
+  for (int s = tid; s < slots; s += THREADS) {
     int4 h = make_int4(-1, 0, 0, tstart[E]);
     if (s < tstart[E]) {
       int lo = 0, hi = E - 1;                       // largest e with tstart[e] <= s
@@ -95,18 +95,18 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
   }
 
   // ---- stable scatter, chunk by chunk --------------------------------------
-  const int nchunks = (n + kPermThreads - 1) / kPermThreads;
+  const int nchunks = (n + THREADS - 1) / THREADS;
   for (int c0 = 0; c0 < nchunks; c0 += kPermRegs) {
     int ev[kPermRegs];
 #pragma unroll
     for (int r = 0; r < kPermRegs; ++r) {
-      const int a = (c0 + r) * kPermThreads + tid;
+      const int a = (c0 + r) * THREADS + tid;
       ev[r] = (c0 + r < nchunks && a < n) ? idx[a] : -1;
     }
 #pragma unroll
     for (int r = 0; r < kPermRegs; ++r) {
       if (c0 + r >= nchunks) break;                      // uniform
-      const int a = (c0 + r) * kPermThreads + tid;
+      const int a = (c0 + r) * THREADS + tid;
       const int e = ev[r];
       const bool valid = (unsigned)e < (unsigned)E;
       // lanes holding the same expert: intersect ballots over the id bits
@@ -117,7 +117,7 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
         same &= ((e >> bit) & 1) ? b : ~b;
       }
       const int rank = __popcll(same & lt_mask);
-      for (int e2 = tid; e2 < kPermWaves * kMaxExperts; e2 += kPermThreads) (&wcnt[0][0])[e2] = 0;
+      for (int e2 = tid; e2 < (THREADS / 64) * kMaxExperts; e2 += THREADS) (&wcnt[0][0])[e2] = 0;
       __syncthreads();
       if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
       __syncthreads();
@@ -130,9 +130,9 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
         tiles[(size_t)(tstart[e] + r / bm) * ti + 4 + r % bm] = a;
       }
       __syncthreads();
-      for (int e2 = tid; e2 < E; e2 += kPermThreads) {
+      for (int e2 = tid; e2 < E; e2 += THREADS) {
         int s = 0;
-        for (int w = 0; w < kPermWaves; ++w) s += wcnt[w][e2];
+        for (int w = 0; w < (THREADS / 64); ++w) s += wcnt[w][e2];
         base[e2] += s;
       }
       __syncthreads();

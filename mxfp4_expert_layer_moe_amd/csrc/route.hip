@@ -29,9 +29,8 @@
 //     most eps32 times that k-step's sum of |x_d w_d|, and sum_d |x_d w_d| <=
 //     ||x_t|| ||w_e|| by Cauchy-Schwarz), so the result is the float64
 //     selection at any input scale.  Gates are the softmax of the selected
-//     float64 scores.
+//     float64 scores, with the exponentials of their gaps taken in fp32.
 #include "mfma_ops.h"
-#include "permute_body.h"
 
 namespace moe {
 
@@ -332,17 +331,19 @@ __device__ __forceinline__ void select_token(int t, int T, int D, int E, int k, 
     top_k(v, cand, k, lane, taken, mx, kth);
   }
   // gates: softmax over the selected scores (mx is the largest), summed in ascending expert id
-  double ex[4];
+  // exponentials of the score gaps in fp32 (the gaps are exact differences of float64 scores);
+  // the gates are then within a few fp32 ulps of the float64 softmax
+  float ex[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) ex[c] = taken[c] ? exp(v[c] - mx) : 0.0;
-  double sum = 0.0;
+  for (int c = 0; c < 4; ++c) ex[c] = taken[c] ? expf((float)(v[c] - mx)) : 0.0f;
+  float sum = 0.0f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     uint64_t m = __ballot(taken[c]);
     while (m) {
       const int l = __ffsll((long long)m) - 1;
       m &= m - 1;
-      sum += readlane_f64(ex[c], l);
+      sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex[c]), l));
     }
   }
   int before = 0;
@@ -352,7 +353,7 @@ __device__ __forceinline__ void select_token(int t, int T, int D, int E, int k, 
     const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
     if (taken[c]) {
       out_idx[(size_t)t * k + slot] = lane + 64 * c;
-      out_w[(size_t)t * k + slot] = (float)(ex[c] / sum);
+      out_w[(size_t)t * k + slot] = ex[c] / sum;
     }
     before += __popcll(m);
   }
@@ -391,21 +392,6 @@ __global__ __launch_bounds__(256) void route_select_kernel(int T, int D, int E, 
   select_token(t, T, D, E, k, KW, max_wnorm2(E, KW, wsq), x, wr, br, logit, xsq, out_idx, out_w, out_logits);
 }
 
-// Small batches: one workgroup selects every token, then groups the assignments
-// (the selection's global writes are visible to the workgroup after the barrier).
-__global__ __launch_bounds__(kPermThreads) void route_select_permute_kernel(
-    int T, int D, int E, int k, int KW, const uint16_t* __restrict__ x, const float* __restrict__ wr,
-    const float* __restrict__ br, const double* __restrict__ logit, const float* __restrict__ xsq,
-    const float* __restrict__ wsq, int32_t* __restrict__ out_idx, float* __restrict__ out_w, int bm, int slots,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ tiles) {
-  const float wmax2 = max_wnorm2(E, KW, wsq);
-  for (int t = threadIdx.x >> 6; t < T; t += kPermWaves)
-    select_token(t, T, D, E, k, KW, wmax2, x, wr, br, logit, xsq, out_idx, out_w, nullptr);
-  __syncthreads();
-  permute_group(T * k, E, bm, slots, out_idx, counts, offsets, perm, inv, tiles);
-}
-
 static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
                                 hipStream_t s, double** logit, float** xsq, float** wsq, int* KW) {
   *KW = route_kw(T, E);
@@ -435,8 +421,6 @@ hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const flo
   return hipGetLastError();
 }
 
-constexpr int kFusedSelectMaxT = 64;         // up to here one workgroup selects and groups
-
 hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
                               int32_t* idx, float* w, void* ws, uint8_t* xpack, int32_t* counts,
                               int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s) {
@@ -446,14 +430,6 @@ hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, con
   int KW;
   hipError_t err = launch_logits(T, D, E, x, wr, ws, xpack, s, &logit, &xsq, &wsq, &KW);
   if (err != hipSuccess) return err;
-  const int n = T * k;
-  if (T <= kFusedSelectMaxT) {
-    route_select_permute_kernel<<<dim3(1), dim3(kPermThreads), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq,
-                                                                       idx, w, tile_rows(n, E),
-                                                                       (int)tile_slots(n, E), counts, offsets, perm,
-                                                                       inv, tiles);
-    return hipGetLastError();
-  }
   route_select_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq, idx, w,
                                                               nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
