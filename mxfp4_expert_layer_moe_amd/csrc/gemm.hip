@@ -58,9 +58,10 @@ __host__ __device__ inline int stage_stride(int KC) { return KC * kActChunk + 8;
 // ABUF: 2 reads the next k-tile's activations from LDS while the current one computes (costs
 // registers), 1 reads them at the start of each k-tile.  SB: with KTC, a scheduling barrier
 // after every SB k-tiles pins the refill loads in place.
-template <int STAGE, int P, int BM, int KTC, int ABUF, int SB = 1>
+// NB: 32-column weight tiles per wavefront (gate/up: the gate and up tiles of one SwiGLU pair).
+template <int STAGE, int P, int BM, int KTC, int ABUF, int SB = 1, int NB = (STAGE == 0 ? 2 : 1)>
 __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
-  constexpr int NB = STAGE == 0 ? 2 : 1;
+  static_assert(STAGE == 1 || NB == 2, "a gate/up wavefront holds one gate/up tile pair");
   static_assert(P % 4 == 0, "prefetch depth must cover whole scale groups");
   static_assert(BM <= kMTile && BM * kActChunk * P <= kAStageBytes, "a chunk of P k-tiles must fit for BM rows");
   __shared__ __attribute__((aligned(16))) uint8_t sA[kAStageBytes];
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   int sbase[NB], ssbase[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int q = STAGE == 0 ? 2 * u + nb : u;
+    const int q = NB * u + nb;
     sbase[nb] = q * g.KT * 1024;
     ssbase[nb] = q * g.KG * 256;
   }
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     }
   } else {
     // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp32
-    const int D = g.units * kNTile;
+    const int D = g.out_K;
     float wl = 0.0f;
     if (valid) wl = g.topk_w[tile[4 + i]];
     float* out = reinterpret_cast<float*>(g.out);
@@ -233,10 +234,25 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       if (8 * (r >> 2) >= nrows) break;
       const int m = 8 * (r >> 2) + 4 * half + (r & 3);
       const float wm = __shfl(wl, m);
-      if (m < nrows) out[(size_t)(p0 + m) * D + (size_t)u * kNTile + (lane & 31)] = acc[0][r] * wm;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        if (m < nrows) out[(size_t)(p0 + m) * D + (size_t)(NB * u + nb) * kNTile + (lane & 31)] = acc[nb][r] * wm;
     }
   }
 }
+
+#ifndef MOE_DECODE_DOWN_NB
+#define MOE_DECODE_DOWN_NB 1
+#endif
+#ifndef MOE_DECODE_DOWN_P
+#define MOE_DECODE_DOWN_P 16
+#endif
+#ifndef MOE_DECODE_GU_P
+#define MOE_DECODE_GU_P 8
+#endif
+constexpr int kGateUpP = MOE_DECODE_GU_P;     // gate/up weight k-tiles in flight per wavefront
+constexpr int kDownNB = MOE_DECODE_DOWN_NB;   // down-projection weight tiles per wavefront
+constexpr int kDownP = MOE_DECODE_DOWN_P;     // and k-tiles in flight
 
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
@@ -250,7 +266,7 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   g.K = stage == 0 ? D : I;
   g.KT = g.K / kKTile;
   g.KG = w_kgroups(g.K);
-  g.units = stage == 0 ? I / kNTile : D / kNTile;
+  g.units = stage == 0 ? I / kNTile : D / (kNTile * kDownNB);
   g.out_K = stage == 0 ? I : D;
   g.codes_per_expert = w_codes_per_expert(N, g.K);
   g.scales_per_expert = w_scales_per_expert(N, g.K);
@@ -263,11 +279,11 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   // the model's K = 2880 (45 k-tiles): fully unrolled k-loop
   const bool k45 = g.KT == 45 && 8 * stage_stride(45) <= kAStageBytes;   // 40384 <= 40960
   if (stage == 0) {
-    if (k45) expert_gemm_kernel<0, 8, 8, 45, 1><<<grid, dim3(256), 0, s>>>(g);
+    if (k45) expert_gemm_kernel<0, kGateUpP, 8, 45, 1><<<grid, dim3(256), 0, s>>>(g);
     else expert_gemm_kernel<0, 8, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
   } else {
-    if (k45) expert_gemm_kernel<1, 16, 8, 45, 2><<<grid, dim3(256), 0, s>>>(g);
-    else expert_gemm_kernel<1, 16, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);
+    if (k45) expert_gemm_kernel<1, kDownP, 8, 45, 2, 1, kDownNB><<<grid, dim3(256), 0, s>>>(g);
+    else expert_gemm_kernel<1, kDownP, 8, 0, 1, 1, kDownNB><<<grid, dim3(256), 0, s>>>(g);
   }
   return hipGetLastError();
 }
