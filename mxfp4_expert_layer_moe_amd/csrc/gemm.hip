@@ -113,6 +113,23 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   // weight ring: slot j holds k-tile kt with kt % P == j; scale slot s holds group (kt / 4) with (kt/4) % (P/4) == s
   v4i bq[P][NB];
   uint32_t sbq[P / 4][NB];
+  // With K known at compile time all of K is staged at once.  The staging loads (16-byte pieces,
+  // up to kPieces per thread) are issued before the weight ring, so waiting for them does not
+  // wait for the weights (loads complete in issue order).
+  constexpr int kPieces = KTC > 0 ? (BM * KTC * (kActChunk / 16) + 255) / 256 : 1;
+  uint4 stg[kPieces];
+  if constexpr (KTC > 0) {
+    __syncthreads();                                    // srow visible
+    const int n16 = KTC * (kActChunk / 16);
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      const int w = tid + 256 * q;
+      if (w < nrows * n16) {
+        const int r = w / n16, o = w - r * n16;
+        stg[q] = *reinterpret_cast<const uint4*>(g.a_packed + (size_t)srow[r] * arb + (size_t)o * 16);
+      }
+    }
+  }
   if (active) {
 #pragma unroll
     for (int j = 0; j < P; ++j)
@@ -127,6 +144,19 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
         for (int nb = 0; nb < NB; ++nb) sbq[s][nb] = load_s(nb, s);
       }
   }
+  if constexpr (KTC > 0) {
+    const int n16 = KTC * (kActChunk / 16);
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      const int w = tid + 256 * q;
+      if (w < nrows * n16) {
+        const int r = w / n16, o = w - r * n16;
+        uint2* dst = reinterpret_cast<uint2*>(sA + r * rs + o * 16);     // rows are 8-byte aligned
+        dst[0] = make_uint2(stg[q].x, stg[q].y);
+        dst[1] = make_uint2(stg[q].z, stg[q].w);
+      }
+    }
+  }
 
   v16f acc[NB];
 #pragma unroll
@@ -134,13 +164,15 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 
   for (int c0 = 0; c0 < g.KT; c0 += KC) {
     const int kcn = min(KC, g.KT - c0);
-    __syncthreads();                                    // previous chunk consumed; srow visible
-    // stage rows [0, nrows) x k-tiles [c0, c0 + kcn): contiguous chunks, 8-byte words
-    const int n8 = kcn * (kActChunk / 8);
-    for (int w = tid; w < nrows * n8; w += 256) {
-      const int r = w / n8, o = w - r * n8;
-      const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + (size_t)c0 * kActChunk + (size_t)o * 8;
-      *reinterpret_cast<uint2*>(sA + r * rs + o * 8) = *reinterpret_cast<const uint2*>(src);
+    if constexpr (KTC == 0) {
+      __syncthreads();                                  // previous chunk consumed; srow visible
+      // stage rows [0, nrows) x k-tiles [c0, c0 + kcn): contiguous chunks, 8-byte words
+      const int n8 = kcn * (kActChunk / 8);
+      for (int w = tid; w < nrows * n8; w += 256) {
+        const int r = w / n8, o = w - r * n8;
+        const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + (size_t)c0 * kActChunk + (size_t)o * 8;
+        *reinterpret_cast<uint2*>(sA + r * rs + o * 8) = *reinterpret_cast<const uint2*>(src);
+      }
     }
     __syncthreads();
     if (active) {
@@ -178,11 +210,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
           acc[nb] = mma_sel(j & 3, ah[cur], bv, acc[nb], sh[cur], sbq[j >> 2][nb]);
           acc[nb] = mma_sel(j & 3, al[cur], bv, acc[nb], sl[cur], sbq[j >> 2][nb]);
         }
-        const int kn = min(kt + P, g.KT - 1);
+        const int kn = min(kt + P, kend - 1);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) bq[j][nb] = load_b(nb, kn);
         if ((j & 3) == 3) {
-          const int grp = min((kt + P - 3) / 4, g.KG - 1);
+          const int grp = min((kt + P - 3) / 4, (kend - 1) / 4);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) sbq[j >> 2][nb] = load_s(nb, grp);
         }
