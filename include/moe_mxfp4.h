@@ -169,7 +169,9 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
  *    a_packed  packed h from the GATE_UP stage
  *    codes/scales  prepacked down weights (stage DOWN)
  *    topk_w    [T][top_k] fp32 gates; row p is scaled by topk_w[perm[p]]
- *    out       y_perm [T*top_k][d_model] fp32, row p = gate-weighted expert output
+ *    out       y_perm [T*top_k][d_model] fp16 (round to nearest even), row p =
+ *              gate-weighted expert output; its magnitude must stay below the fp16
+ *              maximum (65504)
  *  tiles is moe_permute's row-tile table for the same T.  Experts with no token
  *  have no tile (their weights are not read).
  */
@@ -180,10 +182,10 @@ moe_status moe_expert_gemm_mxfp4(const moe_dims* dims, int32_t T, moe_stage stag
 /*
  * Weighted combine: y[t] = sum over the token's slots j (ascending expert id)
  * of y_perm[inv[t*top_k + j]], summed in fp32.
- *   y_perm [T*top_k][d_model] fp32 (gate already applied);  inv from moe_permute
+ *   y_perm [T*top_k][d_model] fp16 (gate already applied);  inv from moe_permute
  *   y      out [T][d_model], fp32 (MOE_FP32) or bf16 round-to-nearest-even (MOE_BF16)
  */
-moe_status moe_combine(const moe_dims* dims, int32_t T, const float* y_perm, const int32_t* inv, void* y,
+moe_status moe_combine(const moe_dims* dims, int32_t T, const void* y_perm, const int32_t* inv, void* y,
                        moe_dtype y_dtype, hipStream_t stream);
 
 /*

@@ -60,7 +60,7 @@ WsLayout ws_layout(const moe_dims* d, int32_t T) {
   L.tiles = take(tile_table_bytes(d, T));
   L.xpack = take((size_t)T * act_row_bytes(d->d_model));
   L.hpack = take(n * act_row_bytes(d->d_ff));
-  L.yperm = take(n * (size_t)d->d_model * 4);
+  L.yperm = take(n * (size_t)d->d_model * 2);
   L.route = take(route_workspace_bytes(T, d->d_model, d->n_experts));
   L.total = o;
   return L;
@@ -170,7 +170,7 @@ moe_status moe_expert_gemm_mxfp4(const moe_dims* d, int32_t T, moe_stage stage, 
                                 out, stream));
 }
 
-moe_status moe_combine(const moe_dims* d, int32_t T, const float* y_perm, const int32_t* inv, void* y,
+moe_status moe_combine(const moe_dims* d, int32_t T, const void* y_perm, const int32_t* inv, void* y,
                        moe_dtype y_dtype, hipStream_t stream) {
   moe_status st = check_dims(d);
   if (st != MOE_OK) return st;
@@ -178,7 +178,8 @@ moe_status moe_combine(const moe_dims* d, int32_t T, const float* y_perm, const 
   if (y_dtype != MOE_BF16 && y_dtype != MOE_FP32) return MOE_EINVAL;
   if (!y_perm || !inv || !y || !aligned(y_perm, 16) || !aligned(inv, 4) || !aligned(y, 16)) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
-  return hip_status(launch_combine(T, d->d_model, d->top_k, y_perm, inv, y, y_dtype == MOE_BF16, stream));
+  return hip_status(launch_combine(T, d->d_model, d->top_k, (const _Float16*)y_perm, inv, y, y_dtype == MOE_BF16,
+                                   stream));
 }
 
 moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
@@ -207,7 +208,7 @@ moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const f
   int32_t* tiles = (int32_t*)(base + L.tiles);
   uint8_t* xpack = base + L.xpack;
   uint8_t* hpack = base + L.hpack;
-  float* yperm = (float*)(base + L.yperm);
+  _Float16* yperm = (_Float16*)(base + L.yperm);
   const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
   hipError_t e;
   if ((e = launch_route_front(T, D, E, k, (const uint16_t*)x_bf16, w_router, b_router, idx, w, base + L.route, xpack,

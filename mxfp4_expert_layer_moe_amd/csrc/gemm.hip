@@ -256,11 +256,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       if (m < nrows) store_split32(out + (size_t)(p0 + m) * orb, u, c, sp);
     }
   } else {
-    // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp32
+    // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp16
     const int D = g.out_K;
     float wl = 0.0f;
     if (valid) wl = g.topk_w[tile[4 + i]];
-    float* out = reinterpret_cast<float*>(g.out);
+    _Float16* out = reinterpret_cast<_Float16*>(g.out);
 #pragma unroll
     for (int r = 0; r < BM / 2; ++r) {
       if (8 * (r >> 2) >= nrows) break;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       const float wm = __shfl(wl, m);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        if (m < nrows) out[(size_t)(p0 + m) * D + (size_t)(NB * u + nb) * kNTile + (lane & 31)] = acc[nb][r] * wm;
+        if (m < nrows) out[(size_t)(p0 + m) * D + (size_t)(NB * u + nb) * kNTile + (lane & 31)] = (_Float16)(acc[nb][r] * wm);
     }
   }
 }

@@ -320,9 +320,9 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
       if (m < nrows && 2 * ublk < g.nt) store_fp6_block(out + (size_t)(p0 + m) * orb, ublk, sp);
     }
   } else {
-    // ---- down: scale row p by its gate weight, store fp32 ---------------------------------------
+    // ---- down: scale row p by its gate weight, store fp16 ---------------------------------------
     const int D = g.out_K;
-    float* out = reinterpret_cast<float*>(g.out);
+    _Float16* out = reinterpret_cast<_Float16*>(g.out);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       if (rb * 32 >= nrows) break;                       // uniform
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < nrows) out[(size_t)(p0 + m) * D + q * 32 + r32] = acc[rb][cb][r] * sgate[m];
+          if (m < nrows) out[(size_t)(p0 + m) * D + q * 32 + r32] = (_Float16)(acc[rb][cb][r] * sgate[m]);
         }
       }
     }

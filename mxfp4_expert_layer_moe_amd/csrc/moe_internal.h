@@ -197,7 +197,7 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
                                const uint8_t* scales, const float* topk_w, void* out, hipStream_t s);
-hipError_t launch_combine(int T, int D, int k, const float* y_perm, const int32_t* inv, void* y,
+hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, void* y,
                           int y_bf16, hipStream_t s);
 
 }  // namespace moe

@@ -69,7 +69,7 @@ class DeviceLayer:
         self.tiles = torch.empty(max(moe_tile_table_bytes(self.dims, T) // 4, 4), **i32)
         self.x_packed = torch.empty(max(moe_act_pack_bytes(D, T), 16), dtype=torch.uint8, device=device)
         self.h_packed = torch.empty(max(moe_act_pack_bytes(I, n), 16), dtype=torch.uint8, device=device)
-        self.y_perm = torch.empty((n, D), dtype=torch.float32, device=device)
+        self.y_perm = torch.empty((n, D), dtype=torch.float16, device=device)
         self.y32 = torch.empty((T, D), dtype=torch.float32, device=device)
         self.y16 = torch.empty((T, D), dtype=torch.bfloat16, device=device)
         self.ws = torch.empty(max(moe_workspace_bytes(self.dims, T), 256), dtype=torch.uint8, device=device)
