@@ -237,26 +237,38 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       }
     }
   }
-  if (!active) return;
-
   if constexpr (STAGE == 0) {
-    // SwiGLU epilogue: h = bf16(silu(clamp(g)) * clamp(u)), written as hi/lo MX6 block u of row p
+    // SwiGLU epilogue: h = bf16(silu(clamp(g)) * clamp(u)), then a transpose through LDS (the
+    // staged rows are free once every wavefront is past its k-loop) so that lane m holds the 32
+    // values of row m's block and splits them into hi/lo FP6 with the packed conversions.
+    __syncthreads();
+    if (!active) return;
+    constexpr int kEpStride = 36;                        // floats per row: 8 rows on 8 bank groups
+    static_assert(4 * BM * kEpStride * 4 <= kAStageBytes, "transpose fits the staging buffer");
+    float* ep = reinterpret_cast<float*>(sA) + wave * BM * kEpStride;
     const int I = g.out_K;
     const size_t orb = act_row_bytes(I);
     uint8_t* out = reinterpret_cast<uint8_t*>(g.out);
     const int c = lane & 31;
-    // register r holds rows 8(r/4) + {0..7}; tiles of BM rows only fill r < BM/2, and row
-    // groups at or past nrows are skipped (uniform per wavefront)
+    // register r holds rows 8(r/4) + 4(l/32) + r%4; tiles of BM rows only fill r < BM/2
 #pragma unroll
     for (int r = 0; r < BM / 2; ++r) {
-      if (8 * (r >> 2) >= nrows) break;
       const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-      const float h = swiglu_bf16(acc[0][r], acc[1][r], g.limit);
-      const Split32 sp = split_block32(h, c);
-      if (m < nrows) store_split32(out + (size_t)(p0 + m) * orb, u, c, sp);
+      ep[m * kEpStride + c] = swiglu_bf16(acc[0][r], acc[1][r], g.limit);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < BM && lane < nrows) {
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(ep + lane * kEpStride + 4 * q);
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+      store_fp6_block(out + (size_t)(p0 + lane) * orb, u, split_fp6x32(v));
     }
   } else {
     // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp16
+    if (!active) return;
     const int D = g.out_K;
     float wl = 0.0f;
     if (valid) wl = g.topk_w[tile[4 + i]];

@@ -72,29 +72,6 @@ __host__ __device__ inline long long tile_buffer_ints(long long n_assign, int E)
   return tile_table_ints(n_assign, E) + perm_groups(n_assign) * E + E + 1;
 }
 
-// ---------------------------------------------------------------------------
-// FP6 E2M3 encoding of v / 2^e (round to nearest even, saturate at 7.5).
-// Returns the 6-bit code; *dec receives the decoded value times 2^e.
-// ---------------------------------------------------------------------------
-__device__ inline uint32_t e2m3_encode(float v, float inv_scale, float scale, float* dec) {
-  float a = fabsf(v) * inv_scale;        // exact: inv_scale is a power of two
-  float c;
-  if (a < 2.0f) {
-    c = __builtin_rintf(a * 8.0f);                    // codes 0..16 (16 == 2.0)
-  } else if (a < 4.0f) {
-    c = 16.0f + __builtin_rintf((a - 2.0f) * 4.0f);   // codes 16..24
-  } else {
-    c = 24.0f + __builtin_rintf((fminf(a, 7.5f) - 4.0f) * 2.0f);   // codes 24..31
-  }
-  uint32_t code = (uint32_t)c;
-  float mag = code < 16 ? (float)code * 0.125f
-                        : (code < 24 ? 2.0f + (float)(code - 16) * 0.25f : 4.0f + (float)(code - 24) * 0.5f);
-  float val = mag * scale;
-  bool neg = v < 0.0f;
-  *dec = neg ? -val : val;
-  return code | (neg && code ? 32u : 0u);
-}
-
 // Shared exponent of a block whose largest magnitude is amax: floor(log2 amax) - 2,
 // returned as the E8M0 byte, clamped to [1, 253] so that both the scale and its
 // inverse are normal fp32 numbers; amax == 0 gives 127.
@@ -106,7 +83,6 @@ __device__ inline uint32_t e2m3_scale_byte(float amax) {
 }
 
 __device__ inline float e8m0_to_float(uint32_t b) { return __uint_as_float(b << 23); }
-__device__ inline float e8m0_to_inv(uint32_t b) { return __uint_as_float((254u - b) << 23); }
 
 __device__ inline float bf16_round(float v) {
   uint32_t u = __float_as_uint(v);
@@ -124,56 +100,7 @@ __device__ inline float swiglu_bf16(float g, float u, float limit) {
   return bf16_round(gv * __builtin_amdgcn_rcpf(1.0f + e) * uv);
 }
 
-__device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__device__ inline float half_wave_max(float v) {
-#pragma unroll
-  for (int d = 1; d < 32; d <<= 1) v = fmaxf(v, __shfl_xor(v, d));
-  return v;
-}
-
-// Split one 32-value block held one value per lane of a half-wavefront (lane c of
-// the half holds element c) into hi/lo E2M3 terms.  All 64 lanes must call it.
-// vh / vl: the 24-bit little-endian code group of elements 4*(c/4)..+3 (valid in
-// every lane of the group); s_hi / s_lo: the E8M0 scale bytes of the block.
-struct Split32 {
-  uint32_t vh, vl, s_hi, s_lo;
-};
-
-__device__ inline Split32 split_block32(float v, int c) {
-  Split32 r;
-  r.s_hi = e2m3_scale_byte(half_wave_max(fabsf(v)));
-  float d;
-  const uint32_t c_hi = e2m3_encode(v, e8m0_to_inv(r.s_hi), e8m0_to_float(r.s_hi), &d);
-  const float res = v - d;
-  r.s_lo = e2m3_scale_byte(half_wave_max(fabsf(res)));
-  const uint32_t c_lo = e2m3_encode(res, e8m0_to_inv(r.s_lo), e8m0_to_float(r.s_lo), &d);
-  uint32_t vh = c_hi << (6 * (c & 3));
-  uint32_t vl = c_lo << (6 * (c & 3));
-  vh |= __shfl_xor(vh, 1);
-  vl |= __shfl_xor(vl, 1);
-  vh |= __shfl_xor(vh, 2);
-  vl |= __shfl_xor(vl, 2);
-  r.vh = vh;
-  r.vl = vl;
-  return r;
-}
-
-// Store block b of a packed row from lane c of the half-wave that split it.
-__device__ inline void store_split32(uint8_t* row, int b, int c, const Split32& s) {
-  uint8_t* chunk = row + (size_t)(b >> 1) * kActChunk;
-  const int half = b & 1;
-  if ((c & 3) == 0) {
-    uint8_t* ph = chunk + half * 24 + 3 * (c >> 2);
-    uint8_t* pl = chunk + 48 + half * 24 + 3 * (c >> 2);
-    ph[0] = (uint8_t)s.vh; ph[1] = (uint8_t)(s.vh >> 8); ph[2] = (uint8_t)(s.vh >> 16);
-    pl[0] = (uint8_t)s.vl; pl[1] = (uint8_t)(s.vl >> 8); pl[2] = (uint8_t)(s.vl >> 16);
-  }
-  if (c == 0) {
-    chunk[96 + half] = (uint8_t)s.s_hi;
-    chunk[98 + half] = (uint8_t)s.s_lo;
-  }
-}
 
 
 // ---------------------------------------------------------------------------
