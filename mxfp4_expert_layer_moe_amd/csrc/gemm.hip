@@ -83,6 +83,9 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   const int half = lane >> 5;
   const bool valid = i < nrows;
   if (tid < nrows) srow[tid] = STAGE == 0 ? tile[4 + tid] / g.k : p0 + tid;
+  // down: each row's gate weight topk_w[perm[p]], fetched now so it is there for the epilogue
+  float wl = 0.0f;
+  if (STAGE == 1 && valid) wl = g.topk_w[tile[4 + i]];
 
   // K chunk staged at once: everything if it fits, else a multiple of the prefetch depth
   int KC = KTC > 0 ? KTC : g.KT;
@@ -270,8 +273,6 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp16
     if (!active) return;
     const int D = g.out_K;
-    float wl = 0.0f;
-    if (valid) wl = g.topk_w[tile[4 + i]];
     _Float16* out = reinterpret_cast<_Float16*>(g.out);
 #pragma unroll
     for (int r = 0; r < BM / 2; ++r) {

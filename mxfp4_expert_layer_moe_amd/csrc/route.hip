@@ -19,6 +19,13 @@
 //     of 16-term partial sums.  The 16 K-partials of a workgroup are summed in
 //     LDS in a fixed order and its float64 tile is written to the workspace,
 //     with the squared norms of the x rows and w rows.
+//  route_select_small (batches of at most 32 tokens and 32 experts, i.e.
+//     decode): one workgroup sums the partial tiles into an LDS logit table,
+//     then selects with one lane per token (the token's 32 scores sit in its
+//     registers), the same rules and arithmetic as below, and for the layer
+//     forward groups the assignments by expert in the same workgroup.  The
+//     logit kernel splits K sixteen ways at these sizes, so its work spreads
+//     over sixteen compute units.
 //  route_select: one wavefront per token.  Sums the KW partial tiles in a
 //     fixed order (deterministic), adds the bias, takes the top-k by
 //     wave-wide arg-max (larger logit first, lower id on ties).  If any other
@@ -68,7 +75,11 @@ __device__ double score_f64(const uint16_t* __restrict__ xr, const float* __rest
 constexpr int kLogitWaves = 16;
 constexpr int kLogitBatch = 4;                 // k-steps whose loads are issued together
 
+static bool route_small(int T, int E) { return T <= 32 && E <= 32; }
+constexpr int kSmallKW = 16;
+
 static int route_kw(int T, int E) {
+  if (route_small(T, E)) return kSmallKW;
   const int tiles = ((T + kRouteTokens - 1) / kRouteTokens) * ((E + 31) / 32);
   return tiles <= 64 ? 4 : (tiles <= 256 ? 2 : 1);
 }
@@ -93,49 +104,27 @@ size_t route_workspace_bytes(int T, int D, int E) {
   return T > 0 ? route_ws_layout(T, E).total : 0;
 }
 
-// Workgroups past the logit tiles (when xpack is given) split x into the packed activation
-// format for the gate/up GEMM instead: one 32-value block per lane.
-__global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, int D, int E, int KW,
-                                                                         const uint16_t* __restrict__ x,
-                                                                         const float* __restrict__ wr,
-                                                                         double* __restrict__ logit,
-                                                                         float* __restrict__ xsq,
-                                                                         float* __restrict__ wsq,
-                                                                         int logit_wgs,
-                                                                         uint8_t* __restrict__ xpack) {
-  __shared__ double red[8][32][33];          // K-partials: waves 0..7, then 8..15 added in place
-  __shared__ float rsq[kLogitWaves][2][32];  // partial ||x_t||^2 (0) and ||w_e||^2 (1)
-  if ((int)blockIdx.x >= logit_wgs) {        // activation split, one block per lane (no barriers)
-    const long long blk = (long long)(blockIdx.x - logit_wgs) * (kLogitWaves * 64) + threadIdx.x;
-    pack_block_lane(x, D, (long long)T * (D / kBlock), blk, xpack);
-    return;
-  }
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nte = (E + 31) / 32;
-  const int kw = blockIdx.x % KW;
-  const int nt = (blockIdx.x / KW) % nte;
-  const int tt = blockIdx.x / (KW * nte);
-  const int epad = nte * 32;
+// One wavefront's share of a (32-token, 32-expert) logit tile: the k-steps s_first, s_first +
+// s_stride, ... (16 K values each), BATCH of them loaded before their matrix instructions.
+// Lane l: token row / expert row l % 32, K half l / 32.  Returns the float64 tile partial in the
+// MFMA layout and the lane's partial squared norms of its x row (xs) and w row (sq).
+template <int BATCH>
+__device__ __forceinline__ void logit_steps(int T, int D, int E, const uint16_t* __restrict__ x,
+                                            const float* __restrict__ wr, int tok, int e, int half, int s_first,
+                                            int s_stride, double (&accd)[16], float& sq, float& xs) {
   const int nsteps = D / 16;
-  const int kstride = kLogitWaves * KW;
-  const int row = lane & 31;
-  const int half = lane >> 5;
-  const int e = nt * 32 + row;
-  const int tok = tt * kRouteTokens + row;
   const uint16_t* xa = x + (size_t)tok * D + 8 * half;
   const float* wb = wr + (size_t)e * D + 8 * half;
-  double accd[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) accd[r] = 0.0;
-  float sq = 0.0f, xs = 0.0f;
-  for (int s0 = kw * kLogitWaves + wave; s0 < nsteps; s0 += kLogitBatch * kstride) {
-    uint4 xu[kLogitBatch];
-    float4 wa[kLogitBatch], wc[kLogitBatch];
+  sq = 0.0f;
+  xs = 0.0f;
+  for (int s0 = s_first; s0 < nsteps; s0 += BATCH * s_stride) {
+    uint4 xu[BATCH];
+    float4 wa[BATCH], wc[BATCH];
 #pragma unroll
-    for (int b = 0; b < kLogitBatch; ++b) {
-      const int s = s0 + b * kstride;
+    for (int b = 0; b < BATCH; ++b) {
+      const int s = s0 + b * s_stride;
       xu[b] = make_uint4(0, 0, 0, 0);
       wa[b] = make_float4(0.f, 0.f, 0.f, 0.f);
       wc[b] = wa[b];
@@ -148,8 +137,8 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, i
       }
     }
 #pragma unroll
-    for (int b = 0; b < kLogitBatch; ++b) {
-      if (s0 + b * kstride >= nsteps) break;             // uniform
+    for (int b = 0; b < BATCH; ++b) {
+      if (s0 + b * s_stride >= nsteps) break;             // uniform
       const uint32_t uw[4] = {xu[b].x, xu[b].y, xu[b].z, xu[b].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -179,13 +168,19 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, i
       for (int r = 0; r < 16; ++r) accd[r] += (double)t[r];
     }
   }
+}
+
+// Fixed-order sum of the 16 wavefronts' partial tiles: slot s = p_s + p_(s+8) is left in
+// red[s] (the caller adds slots 0..7 in order); the squared-norm partials go to rsq.
+__device__ __forceinline__ void reduce_partials(const double (&accd)[16], float sq, float xs,
+                                                double (&red)[8][32][33], float (&rsq)[kLogitWaves][2][32],
+                                                int wave, int half, int row) {
   sq += __shfl_xor(sq, 32);
   xs += __shfl_xor(xs, 32);
   if (half == 0) {
     rsq[wave][0][row] = xs;
     rsq[wave][1][row] = sq;
   }
-  // fixed-order reduction of the 16 K-partials: slot s = p_s + p_(s+8), then sum of the 8 slots
   if (wave < 8) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * half + (r & 3)][row] = accd[r];
@@ -196,6 +191,42 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, i
     for (int r = 0; r < 16; ++r) red[wave - 8][8 * (r >> 2) + 4 * half + (r & 3)][row] += accd[r];
   }
   __syncthreads();
+}
+
+// Workgroups past the logit tiles (when xpack is given) split x into the packed activation
+// format for the gate/up GEMM instead: one 32-value block per lane.
+__global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, int D, int E, int KW,
+                                                                         const uint16_t* __restrict__ x,
+                                                                         const float* __restrict__ wr,
+                                                                         double* __restrict__ logit,
+                                                                         float* __restrict__ xsq,
+                                                                         float* __restrict__ wsq,
+                                                                         int logit_wgs,
+                                                                         uint8_t* __restrict__ xpack) {
+  __shared__ double red[8][32][33];          // K-partials: waves 0..7, then 8..15 added in place
+  __shared__ float rsq[kLogitWaves][2][32];  // partial ||x_t||^2 (0) and ||w_e||^2 (1)
+  if ((int)blockIdx.x >= logit_wgs) {        // activation split, one block per lane (no barriers)
+    const long long blk = (long long)(blockIdx.x - logit_wgs) * (kLogitWaves * 64) + threadIdx.x;
+    pack_block_lane(x, D, (long long)T * (D / kBlock), blk, xpack);
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nte = (E + 31) / 32;
+  const int kw = blockIdx.x % KW;
+  const int nt = (blockIdx.x / KW) % nte;
+  const int tt = blockIdx.x / (KW * nte);
+  const int epad = nte * 32;
+  const int kstride = kLogitWaves * KW;
+  const int row = lane & 31;
+  const int half = lane >> 5;
+  const int e = nt * 32 + row;
+  const int tok = tt * kRouteTokens + row;
+  double accd[16];
+  float sq, xs;
+  logit_steps<kLogitBatch>(T, D, E, x, wr, tok, e, half, kw * kLogitWaves + wave, kstride, accd, sq, xs);
+  reduce_partials(accd, sq, xs, red, rsq, wave, half, row);
   double* lt = logit + ((size_t)kw * T + (size_t)tt * kRouteTokens) * epad + nt * 32;
   for (int j = tid; j < 32 * 32; j += kLogitWaves * 64) {
     const int m = j >> 5, c = j & 31;
@@ -392,6 +423,176 @@ __global__ __launch_bounds__(256) void route_select_kernel(int T, int D, int E, 
   select_token(t, T, D, E, k, KW, max_wnorm2(E, KW, wsq), x, wr, br, logit, xsq, out_idx, out_w, out_logits);
 }
 
+// ---- batches of at most 32 tokens and 32 experts --------------------------------------
+
+// Inclusive prefix sum over each half (32 lanes) of the wavefront: shifts by 1, 2, 4, 8 inside
+// rows of 16 lanes (DPP row_shr, zero shifted in), then lane 15 of rows 0 and 2 added into
+// rows 1 and 3 (DPP row_bcast:15).
+__device__ __forceinline__ int half_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  return v;
+}
+
+// One workgroup, one thread per (token t, expert e) pair: t = thread / 32, e = thread % 32, so a
+// wavefront holds two tokens, one per half.  Partial tiles -> scores in LDS; each pair's rank
+// among its token's live experts (higher score first, lower id first on equal scores) selects
+// the top k; the same band test, exact re-scoring and gate arithmetic as select_token; then
+// (perm given) the grouping by expert straight from the per-token selection masks: the
+// position of (t, e) in expert e's segment is the number of earlier tokens that chose e.
+__global__ __launch_bounds__(1024) void route_select_small_kernel(
+    int T, int D, int E, int k, const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ br, const double* __restrict__ logit, const float* __restrict__ xsq,
+    const float* __restrict__ wsq, int32_t* __restrict__ out_idx, float* __restrict__ out_w,
+    float* __restrict__ out_logits, int bm, int slots, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int32_t* __restrict__ tiles) {
+  __shared__ __align__(16) double lt[32][34];  // [token][expert] scores (bias included)
+  __shared__ float xn2[32], wn2[32];
+  __shared__ double kth[32], top[32];         // k-th and largest selected score per token
+  __shared__ float ex_l[32][33];              // gate numerators
+  __shared__ uint32_t smask[32];              // selected experts per token (bit e)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int t = tid >> 5, e = tid & 31;
+  const int hshift = lane & 32;               // this token's half of the wavefront ballots
+  const bool live = t < T && e < E;
+  {
+    // the kSmallKW partials in order, then the bias; every load is issued before the sums
+    if (live) {
+      double p[kSmallKW];
+#pragma unroll
+      for (int q = 0; q < kSmallKW; ++q) p[q] = logit[((size_t)q * T + t) * 32 + e];
+      const float b = br[e];
+      double s = 0.0;
+#pragma unroll
+      for (int q = 0; q < kSmallKW; ++q) s += p[q];
+      const double v = s + (double)b;
+      lt[t][e] = v;
+      if (out_logits) out_logits[(size_t)t * E + e] = (float)v;
+    }
+    if (tid < 64) {
+      const int r = tid & 31;
+      const bool in = tid < 32 ? r < T : r < E;
+      float p[kSmallKW];
+#pragma unroll
+      for (int q = 0; q < kSmallKW; ++q)
+        p[q] = !in ? 0.0f : (tid < 32 ? xsq[(size_t)q * T + r] : wsq[(size_t)q * 32 + r]);
+      float v = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kSmallKW; ++q) v += p[q];
+      (tid < 32 ? xn2 : wn2)[r] = v;
+    }
+  }
+  __syncthreads();
+  // rank among the live experts of the token
+  const double v0 = live ? lt[t][e] : 0.0;
+  int rank = 0;
+  {
+    const double2* row = reinterpret_cast<const double2*>(&lt[t < T ? t : 0][0]);
+#pragma unroll
+    for (int j2 = 0; j2 < 16; ++j2) {
+      const double2 w = row[j2];                          // one 16-byte read per two experts
+      const int j = 2 * j2;
+      rank += (j < E && (w.x > v0 || (w.x == v0 && j < e))) ? 1 : 0;
+      rank += (j + 1 < E && (w.y > v0 || (w.y == v0 && j + 1 < e))) ? 1 : 0;
+    }
+  }
+  bool sel = live && rank < k;
+  if (sel && rank == k - 1) kth[t] = v0;
+  __syncthreads();
+  // band test: any other live expert within the band of the k-th score flags the token
+  float wmax2 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) wmax2 = fmaxf(wmax2, wn2[j]);             // zero past E
+  bool cand = false;
+  if (live) {
+    const double band = kBandRel * sqrt((double)xn2[t] * (double)wmax2);
+    cand = sel || v0 >= kth[t] - band;
+  }
+  const uint32_t cm = (uint32_t)(__ballot(cand) >> hshift);
+  // flagged tokens of this wavefront: re-score every candidate exactly (the whole wavefront
+  // per score), then rank again among the candidates
+  double v = v0;
+  for (int h = 0; h < 2; ++h) {                          // uniform
+    const int th = 2 * (tid >> 6) + h;
+    uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)cm, 32 * h);
+    if (th >= T || __popc(m) <= k) continue;
+    while (m) {
+      const int j = __ffs(m) - 1;
+      m &= m - 1;
+      const double sc = score_f64(x + (size_t)th * D, wr + (size_t)j * D, (double)br[j], D, lane);
+      if (lane == 0) lt[th][j] = sc;
+    }
+  }
+  if (live && __popc(cm) > k) {
+    v = cand ? lt[t][e] : -INFINITY;
+    rank = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const double w = lt[t][j];
+      rank += (((cm >> j) & 1u) && (w > v || (w == v && j < e))) ? 1 : 0;
+    }
+    sel = cand && rank < k;
+  }
+  if (sel && rank == 0) top[t] = v;
+  const uint32_t sm = (uint32_t)(__ballot(sel) >> hshift);
+  if (live && e == 0) smask[t] = sm;
+  __syncthreads();
+  // gates: softmax over the selected scores, exponentials of the gaps in fp32, summed in
+  // ascending expert id; slots in ascending expert id
+  float g = 0.0f;
+  if (sel) {
+    g = expf((float)(v - top[t]));
+    ex_l[t][e] = g;
+  }
+  __syncthreads();
+  if (sel) {
+    float sum = 0.0f;
+    for (uint32_t m = sm; m; m &= m - 1) sum += ex_l[t][__ffs(m) - 1];
+    const int slot = __popc(sm & ((1u << e) - 1u));
+    out_idx[(size_t)t * k + slot] = e;
+    out_w[(size_t)t * k + slot] = g / sum;
+  }
+  if (!perm) return;
+  // grouping: tokens before t that chose e, and the total per expert
+  int before = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int bit = j < T ? (int)((smask[j] >> e) & 1u) : 0;
+    total += bit;
+    before += j < t ? bit : 0;
+  }
+  // exclusive scans over the 32 experts of this half-wavefront: segment offsets, first tiles
+  const int ntl = (total + bm - 1) / bm;
+  const int inc = half_scan(total), tinc = half_scan(ntl);
+  const int off = inc - total, tst = tinc - ntl;
+  const int used = __shfl(tinc, 31, 32);                 // tiles in use
+  const int n = T * k;
+  if (sel && off + before < n && tst + before / bm < slots) {   // always true; keeps stores in bounds
+    const int slot = __popc(sm & ((1u << e) - 1u));
+    const int a = t * k + slot, pos = off + before;
+    perm[pos] = a;
+    inv[a] = pos;
+    tiles[(size_t)(tst + before / bm) * tile_ints(bm) + 4 + before % bm] = a;
+  }
+  // totals, offsets and the headers of expert e's tiles from the first half-wavefront; the
+  // headers of the empty slots past the last tile from everyone
+  if (tid < 32 && e < E) {
+    counts[e] = total;
+    offsets[e] = off;
+    if (e == E - 1) offsets[E] = n;
+    for (int i = 0; i < ntl && tst + i < slots; ++i)
+      *reinterpret_cast<int4*>(tiles + (size_t)(tst + i) * tile_ints(bm)) =
+          make_int4(e, off + i * bm, min(bm, total - i * bm), used);
+  }
+  for (int sl = used + tid; sl < slots; sl += 1024)
+    *reinterpret_cast<int4*>(tiles + (size_t)sl * tile_ints(bm)) = make_int4(-1, 0, 0, used);
+}
+
 static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
                                 hipStream_t s, double** logit, float** xsq, float** wsq, int* KW) {
   *KW = route_kw(T, E);
@@ -416,6 +617,12 @@ hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const flo
   int KW;
   hipError_t err = launch_logits(T, D, E, x, wr, ws, nullptr, s, &logit, &xsq, &wsq, &KW);
   if (err != hipSuccess) return err;
+  if (route_small(T, E)) {
+    route_select_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(T, D, E, k, x, wr, br, logit, xsq, wsq, idx, w,
+                                                             logits, 0, 0, nullptr, nullptr, nullptr, nullptr,
+                                                             nullptr);
+    return hipGetLastError();
+  }
   route_select_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq, idx, w,
                                                               logits);
   return hipGetLastError();
@@ -430,6 +637,13 @@ hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, con
   int KW;
   hipError_t err = launch_logits(T, D, E, x, wr, ws, xpack, s, &logit, &xsq, &wsq, &KW);
   if (err != hipSuccess) return err;
+  if (route_small(T, E)) {
+    const long long n = (long long)T * k;
+    route_select_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(T, D, E, k, x, wr, br, logit, xsq, wsq, idx, w,
+                                                             nullptr, tile_rows(n, E), (int)tile_slots(n, E),
+                                                             counts, offsets, perm, inv, tiles);
+    return hipGetLastError();
+  }
   route_select_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq, idx, w,
                                                               nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
