@@ -53,19 +53,17 @@ constexpr int kPStagePieces = kPrefillRows * kPPieces; // 896 pieces per staged 
 constexpr int kPSlotBytes = 1024 * 16;                 // 896 pieces + 128 dummy (4 unconditional per thread)
 constexpr int kPStageAhead = 2;                        // k-tile kt + 2 is written to LDS during k-tile kt
 constexpr int kPEpiStride = 68;                        // floats per row of the transposed h block
+constexpr int kPOutStride = 136;                       // halves per row of the transposed y block
 static_assert(kPSlots * kPSlotBytes >= 4 * 32 * kPEpiStride * 4, "h transposition fits the ring");
+static_assert(kPSlots * kPSlotBytes / 4 >= 32 * kPOutStride * 2, "y transposition fits a wavefront's quarter");
 
 // Matrix-instruction pairing.  Each 64-wide k-tile holds two 32-value blocks b = 0, 1 of the
 // activation, each stored as hi + lo FP6 terms.  One MFMA per block: lanes 0-31 supply the hi term
 // and lanes 32-63 the lo term of block b as the instruction's two K halves, and the weight operand
 // holds block b in both halves, so the instruction sums (hi + lo) * w over the block.  A lane half's
-// 24-byte term then starts at the same offset pattern in both halves (no per-lane reordering).
-__device__ __forceinline__ v8i fp6_operand(v4i q, uint2 t, bool q_first) {
-  v8i v;
-  if (q_first) v = {q.x, q.y, q.z, q.w, (int)t.x, (int)t.y, 0, 0};
-  else v = {(int)t.x, (int)t.y, q.x, q.y, q.z, q.w, 0, 0};
-  return v;
-}
+// two 24-byte terms are the 48 contiguous bytes at 48h of the row chunk: read as twelve dwords,
+// block 0's operand is dwords 0-5 and block 1's dwords 6-11 (register sub-ranges, no copies).
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 // both halves of the weight register: [block 0 | block 0] and [block 1 | block 1]
 __device__ __forceinline__ void split_halves(const v4i x, v4i& b0, v4i& b1) {
@@ -106,16 +104,18 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   const int slot = item / g.ngroups;
   const int cgrp = item - slot * g.ngroups;
   const int32_t* tile = g.tiles + (size_t)slot * tile_ints(kPrefillRows);
+  // the header and the row ids in one round trip (a slot always holds 128 id entries)
+  const int a_id = tile[4 + (tid & (kPrefillRows - 1))];
   const int4 hdr = *reinterpret_cast<const int4*>(tile);
   const int e = __builtin_amdgcn_readfirstlane(hdr.x);
   const int p0 = __builtin_amdgcn_readfirstlane(hdr.y);
   const int nrows = __builtin_amdgcn_readfirstlane(hdr.z);
 
-  if (tid < kPrefillRows) {
-    const int r = min(tid, nrows - 1);                   // rows past the tile repeat its last row
-    const int a = tile[4 + r];
-    srow[tid] = STAGE == 0 ? a / g.k : p0 + r;
-    if constexpr (STAGE == 1) sgate[tid] = g.topk_w[a];
+  // down: each row's gate weight, loaded now and waited for only in the epilogue
+  float wrow = 0.0f;
+  if (tid < nrows) {
+    srow[tid] = STAGE == 0 ? a_id / g.k : p0 + tid;
+    if constexpr (STAGE == 1) wrow = g.topk_w[a_id];
   }
   __syncthreads();
 
@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   for (int i = 0; i < 4; ++i) {
     const int q = min(tid + 256 * i, kPStagePieces - 1); // the dummy pieces re-read a real one
     const int row = q / kPPieces;
-    aoff[i] = (uint32_t)srow[row] * g.arb + (uint32_t)(q - row * kPPieces) * 16u;
+    // rows past the tile repeat its last row
+    aoff[i] = (uint32_t)srow[min(row, nrows - 1)] * g.arb + (uint32_t)(q - row * kPPieces) * 16u;
   }
   auto load_a = [&](const int kt, v4i (&buf)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -191,22 +192,21 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   const int h = lane >> 5;
   // A operands of (k-tile kt, row block rb) from the staged slot kt % 4
   // block b's term of this lane half (h = 0: hi, 1: lo) sits at bytes [48h + 24b, 48h + 24b + 24)
-  // of the row chunk; the scale bytes are [hi0, hi1, lo0, lo1] at 96
+  // of the row chunk; the scale bytes are [hi0, hi1, lo0, lo1] at 96, so the half's two scales are
+  // the 16 bits at 96 + 2h (byte b for block b, chosen by the instruction's A-scale byte select).
+  // Loads only: nothing waits for them until the operands are used a phase later.
   struct AOps {
-    v8i a0, a1;
-    uint32_t s0, s1;
+    v16i q;
+    uint32_t s;
   };
   auto read_ops = [&](const int kt, const int rb) __attribute__((always_inline)) {
-    const uint8_t* row = sA + (kt & 3) * kPSlotBytes + rb * kPBlockBytes + r32 * kActChunk + 48 * h;
+    const uint8_t* row = sA + (kt & 3) * kPSlotBytes + rb * kPBlockBytes + r32 * kActChunk;
     AOps o;
-    const v4i q0 = *reinterpret_cast<const v4i*>(row);
-    const v4i t01 = *reinterpret_cast<const v4i*>(row + 16);
-    const v4i q1 = *reinterpret_cast<const v4i*>(row + 32);
-    o.a0 = fp6_operand(q0, make_uint2(t01.x, t01.y), true);
-    o.a1 = fp6_operand(q1, make_uint2(t01.z, t01.w), false);
-    const uint32_t s4 = *reinterpret_cast<const uint32_t*>(row - 48 * h + 96);
-    o.s0 = s4 >> (16 * h);
-    o.s1 = s4 >> (8 + 16 * h);
+    const v4i q0 = *reinterpret_cast<const v4i*>(row + 48 * h);
+    const v4i q1 = *reinterpret_cast<const v4i*>(row + 48 * h + 16);
+    const v4i q2 = *reinterpret_cast<const v4i*>(row + 48 * h + 32);
+    o.q = v16i{q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w, q2.x, q2.y, q2.z, q2.w, 0, 0, 0, 0};
+    o.s = *reinterpret_cast<const uint16_t*>(row + 96 + 2 * h);
     return o;
   };
   // Software pipeline of one k-tile (kt, j = kt % 8, compile-time ring slots), in four phases of
@@ -232,10 +232,12 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     for (int rb = 0; rb < 4; ++rb) {
       const AOps cur = nxt;
       nxt = rb < 3 ? read_ops(kt, rb + 1) : read_ops(min(kt + 1, KT - 1), 0);
+      const v8i a0 = __builtin_shufflevector(cur.q, cur.q, 0, 1, 2, 3, 4, 5, 6, 7);
+      const v8i a1 = __builtin_shufflevector(cur.q, cur.q, 6, 7, 8, 9, 10, 11, 12, 13);
 #pragma unroll
       for (int cb = 0; cb < kPWaveTiles; ++cb) {
-        acc[rb][cb] = mma_sel(j & 3, cur.a0, b_operand(bw[cb][0]), acc[rb][cb], cur.s0, sqd[cb][0]);
-        acc[rb][cb] = mma_sel(j & 3, cur.a1, b_operand(bw[cb][1]), acc[rb][cb], cur.s1, sqd[cb][1]);
+        acc[rb][cb] = mma_sel_a<0>(j & 3, a0, b_operand(bw[cb][0]), acc[rb][cb], cur.s, sqd[cb][0]);
+        acc[rb][cb] = mma_sel_a<1>(j & 3, a1, b_operand(bw[cb][1]), acc[rb][cb], cur.s, sqd[cb][1]);
       }
       if (rb == 0) store_a((kt + D) & 3, abuf[(j + D) % NA]);                  // publish kt + D
       if (rb == 1) load_a(min(kt + D + NA, KT - 1), abuf[(j + D) % NA]);        // fetch kt + D + NA
@@ -320,22 +322,35 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
       if (m < nrows && 2 * ublk < g.nt) store_fp6_block(out + (size_t)(p0 + m) * orb, ublk, sp);
     }
   } else {
-    // ---- down: scale row p by its gate weight, store fp16 ---------------------------------------
+    // ---- down: scale row p by its gate weight, fp16, transpose through LDS, 16-byte row stores --
+    if (tid < kPrefillRows) sgate[tid] = wrow;
+    __syncthreads();
     const int D = g.out_K;
-    _Float16* out = reinterpret_cast<_Float16*>(g.out);
+    uint8_t* out = reinterpret_cast<uint8_t*>(g.out);
+    _Float16* ep = reinterpret_cast<_Float16*>(sA + wave * (kPSlots * kPSlotBytes / 4));
+    const int c0 = (cgrp * kPGroupTiles + wave * kPWaveTiles) * 32;   // first column of the wavefront
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       if (rb * 32 >= nrows) break;                       // uniform
 #pragma unroll
-      for (int cb = 0; cb < kPWaveTiles; ++cb) {
-        const int q = cgrp * kPGroupTiles + wave * kPWaveTiles + cb;
-        if (q >= g.nt) break;                            // uniform
+      for (int cb = 0; cb < kPWaveTiles; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < nrows) out[(size_t)(p0 + m) * D + q * 32 + r32] = (_Float16)(acc[rb][cb][r] * sgate[m]);
+          const int m = 8 * (r >> 2) + 4 * h + (r & 3);
+          ep[m * kPOutStride + cb * 32 + r32] = (_Float16)(acc[rb][cb][r] * sgate[rb * 32 + m]);
         }
+      __builtin_amdgcn_wave_barrier();
+      // 32 rows x 128 columns = 512 pieces of 8 values; piece = row * 16 + column / 8
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pc = lane + 64 * i;
+        const int row = pc >> 4, c8 = (pc & 15) * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + row * kPOutStride + c8);
+        const int m = rb * 32 + row;
+        if (m < nrows && c0 + c8 < D)
+          *reinterpret_cast<uint4*>(out + ((size_t)(p0 + m) * D + c0 + c8) * 2) = v;
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }

@@ -35,6 +35,22 @@ __device__ inline v16f mma_fp6_fp4(v8i a, v8i b, v16f c, uint32_t sa, uint32_t s
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 4, 0, sa, OB, sb);
 }
 
+// scaled MFMA whose A scale is byte OA of sa (the per-lane scale register holds several bytes)
+template <int OA, int OB>
+__device__ inline v16f mma_fp6_fp4_sel(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 4, OA, sa, OB, sb);
+}
+
+template <int OA>
+__device__ inline v16f mma_sel_a(int ob, v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  switch (ob) {
+    case 0: return mma_fp6_fp4_sel<OA, 0>(a, b, c, sa, sb);
+    case 1: return mma_fp6_fp4_sel<OA, 1>(a, b, c, sa, sb);
+    case 2: return mma_fp6_fp4_sel<OA, 2>(a, b, c, sa, sb);
+    default: return mma_fp6_fp4_sel<OA, 3>(a, b, c, sa, sb);
+  }
+}
+
 // ob is a compile-time constant after unrolling, so the switch folds away
 __device__ inline v16f mma_sel(int ob, v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
   switch (ob) {
