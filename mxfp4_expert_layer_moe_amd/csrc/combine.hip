@@ -5,39 +5,59 @@
 // NN2 + 0.3 NN4).  The gate is already applied by the down-projection epilogue,
 // so this kernel gathers the k fp16 rows of each token (positions inv[t*k + j])
 // and sums them in fp32 in slot order (ascending expert id): no atomics, the
-// same bits on every run.  HBM-bound: reads k rows, writes one.
+// same bits on every run.  HBM-bound: reads k rows, writes one.  A thread owns 8
+// columns of a token and issues the index and row loads of 4 slots at a time, so
+// a token's gather costs two memory round trips per 4 slots.
 #include "moe_internal.h"
 
 namespace moe {
 
+constexpr int kCombineCols = 8;        // columns per thread: one 16-byte fp16 load per row
+constexpr int kCombineBatch = 4;       // slots whose index and row loads are issued together
+
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(int T, int D, int k, const _Float16* __restrict__ y_perm,
                                                       const int32_t* __restrict__ inv, void* __restrict__ y) {
-  const int d4 = D / 4;
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const int d8 = D / kCombineCols;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (long long)T * d4) return;
-  const int t = (int)(gid / d4);
-  const int c = (int)(gid - (long long)t * d4) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int p = inv[(size_t)t * k + j];
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    const h4 v = *reinterpret_cast<const h4*>(y_perm + (size_t)p * D + c);
-    acc.x += (float)v.x; acc.y += (float)v.y; acc.z += (float)v.z; acc.w += (float)v.w;
+  if (gid >= (long long)T * d8) return;
+  const int t = (int)(gid / d8);
+  const int c = (int)(gid - (long long)t * d8) * kCombineCols;
+  float acc[kCombineCols];
+#pragma unroll
+  for (int i = 0; i < kCombineCols; ++i) acc[i] = 0.0f;
+  for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+    int p[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) p[u] = j0 + u < k ? inv[(size_t)t * k + j0 + u] : 0;
+    h8 v[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      if (j0 + u < k) v[u] = *reinterpret_cast<const h8*>(y_perm + (size_t)p[u] * D + c);
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)                 // slot order
+      if (j0 + u < k) {
+#pragma unroll
+        for (int i = 0; i < kCombineCols; ++i) acc[i] += (float)v[u][i];
+      }
   }
   if (BF16_OUT) {
-    const uint32_t b0 = __float_as_uint(bf16_round(acc.x)) >> 16, b1 = __float_as_uint(bf16_round(acc.y)) >> 16;
-    const uint32_t b2 = __float_as_uint(bf16_round(acc.z)) >> 16, b3 = __float_as_uint(bf16_round(acc.w)) >> 16;
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)t * D + c) =
-        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    uint32_t w[kCombineCols / 2];
+#pragma unroll
+    for (int i = 0; i < kCombineCols / 2; ++i)
+      w[i] = (__float_as_uint(bf16_round(acc[2 * i])) >> 16) | (__float_as_uint(bf16_round(acc[2 * i + 1])) & 0xFFFF0000u);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + (size_t)t * D + c) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * D + c) = acc;
+    float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * D + c);
+    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
 hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, void* y, int y_bf16,
                           hipStream_t s) {
-  const long long n = (long long)T * (D / 4);
+  const long long n = (long long)T * (D / kCombineCols);
   if (n == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (y_bf16)
