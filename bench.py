@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--stats-report", nargs=2, metavar=("STATS_CSV", "OUT_TXT"),
                    help="summarise a rocprofv3 --stats kernel table as text, then exit")
     p.add_argument("--command", default="", help="the command that made the profile (for the reports)")
+    p.add_argument("--no-block", action="store_true", help="skip the timing of the pre-norm block forward")
     return p.parse_args()
 
 
@@ -218,6 +219,23 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
 
+    # ---- the pre-norm block around the layer, y = x + MoE(RMSNorm(x)), same steps -----
+    block = None
+    if not args.no_block:
+        for s in range(args.warmup):
+            layer.block_forward(weights=copies[s % L])
+        torch.cuda.synchronize()
+        eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eb0.record(stream)
+        for s in range(args.steps):
+            layer.block_forward(weights=copies[s % L])
+        eb1.record(stream)
+        torch.cuda.synchronize()
+        b_ms = eb0.elapsed_time(eb1) / args.steps
+        block = {"what": "RMSNorm -> MoE layer -> residual add (moe_block_forward)",
+                 "ms_per_step": round(b_ms, 5), "tokens_per_s": round(T / (b_ms * 1e-3), 1),
+                 "extra_ms_over_layer": round(b_ms - ms_step, 5)}
+
     # ---- dominant kernel alone: gate/up expert GEMM, per-launch HIP events -----
     layer.route(logits=False)
     layer.permute()
@@ -279,6 +297,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if block is not None:
+        out["block"] = block
     if args.copy_mib > 0:                     # counter calibration: plain copies of known size, untimed
         n = args.copy_mib * 2 ** 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda")

@@ -189,6 +189,34 @@ moe_status moe_combine(const moe_dims* dims, int32_t T, const void* y_perm, cons
                        moe_dtype y_dtype, hipStream_t stream);
 
 /*
+ * Weighted combine plus the residual stream: y[t] = fp32(residual[t]) + (the
+ * moe_combine sum of token t), one fp32 addition after the slot-order sum; the
+ * bf16 output is its round to nearest even.  This is the end of the MoE half of
+ * a pre-norm transformer block, y = x + MoE(RMSNorm(x)) (the block maps
+ * [N x d_model] to [N x d_model]: "gpt-oss architecture walk-through",
+ * section "Transformer Blocks").
+ *   residual_bf16 [T][d_model] bf16, 16-byte aligned (the block input x)
+ *   other arguments as moe_combine
+ */
+moe_status moe_combine_residual(const moe_dims* dims, int32_t T, const void* y_perm, const int32_t* inv,
+                                const void* residual_bf16, void* y, moe_dtype y_dtype, hipStream_t stream);
+
+/*
+ * RMSNorm of the rows of x ("From GPT-2 to gpt-oss", section 7, Figures 11-12:
+ * divide by the root mean square, multiply by a learned per-channel scale, no
+ * mean and no bias; rms_norm_eps = 1e-5 in the model cards' config tables):
+ *   r_t = 1 / sqrt(sum_d x[t,d]^2 / d_model + eps)
+ *   xn[t,d] = bf16((x[t,d] * r_t) * gamma[d])
+ * computed in float64 (eps widened from fp32) and rounded once, to nearest
+ * even, from float64.
+ *   x_bf16  [T][d_model] bf16, 16-byte aligned
+ *   gamma   [d_model] fp32 scale, 16-byte aligned;  eps > 0 and finite
+ *   xn_bf16 out [T][d_model] bf16, 16-byte aligned; must not overlap x_bf16
+ */
+moe_status moe_rmsnorm(const moe_dims* dims, int32_t T, const void* x_bf16, const float* gamma, float eps,
+                       void* xn_bf16, hipStream_t stream);
+
+/*
  * The whole layer: route -> permute -> pack x -> gate/up + SwiGLU -> down ->
  * combine, enqueued on `stream` with no host synchronisation.
  *   ws / ws_bytes: device scratch of at least moe_workspace_bytes(dims, T)
@@ -197,6 +225,19 @@ moe_status moe_combine(const moe_dims* dims, int32_t T, const void* y_perm, cons
 moe_status moe_forward(const moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
                        const float* b_router, const moe_weights* weights, void* y, moe_dtype y_dtype,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The MoE half of a pre-norm transformer block: y = x + MoE(RMSNorm(x)), i.e.
+ * moe_rmsnorm -> the moe_forward steps on the normalised rows ->
+ * moe_combine_residual with x.  The bits equal those of that sequence of step
+ * calls.  ws: at least moe_block_workspace_bytes(dims, T) bytes, 256-byte
+ * aligned (the normalised rows, then moe_forward's workspace); contents
+ * undefined after the call.  gamma / eps as moe_rmsnorm.
+ */
+size_t moe_block_workspace_bytes(const moe_dims* dims, int32_t T);
+moe_status moe_block_forward(const moe_dims* dims, int32_t T, const void* x_bf16, const float* gamma, float eps,
+                             const float* w_router, const float* b_router, const moe_weights* weights, void* y,
+                             moe_dtype y_dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- host-only helpers (off the hot path; no HIP calls) ---------------- */
 

@@ -24,7 +24,8 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN = 0, 1
 EXPORTS = ("moe_status_str", "moe_act_pack_bytes", "moe_prepacked_codes_bytes", "moe_prepacked_scales_bytes",
            "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes", "moe_route", "moe_permute",
            "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine", "moe_forward", "moe_mxfp4_quantize",
-           "moe_mxfp4_prepack")
+           "moe_mxfp4_prepack", "moe_combine_residual", "moe_rmsnorm", "moe_block_workspace_bytes",
+           "moe_block_forward")
 
 
 class MoeError(RuntimeError):
@@ -62,7 +63,8 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_prepacked_codes_bytes", "moe_prepacked_scales_bytes"):
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, ctypes.c_int]
-        for name in ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes"):
+        for name in ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes",
+                     "moe_block_workspace_bytes"):
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, i32]
         L.moe_route.argtypes = [dp, i32, vp, f32p, f32p, i32p, f32p, f32p, vp, sz, vp]
@@ -71,10 +73,15 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_gemm_mxfp4.argtypes = [dp, i32, ctypes.c_int, vp, i32p, vp, vp, f32p, vp, vp]
         L.moe_combine.argtypes = [dp, i32, f32p, i32p, vp, ctypes.c_int, vp]
         L.moe_forward.argtypes = [dp, i32, vp, f32p, f32p, ctypes.POINTER(moe_weights), vp, ctypes.c_int, vp, sz, vp]
+        L.moe_combine_residual.argtypes = [dp, i32, vp, i32p, vp, vp, ctypes.c_int, vp]
+        L.moe_rmsnorm.argtypes = [dp, i32, vp, f32p, ctypes.c_float, vp, vp]
+        L.moe_block_forward.argtypes = [dp, i32, vp, f32p, ctypes.c_float, f32p, f32p, ctypes.POINTER(moe_weights),
+                                        vp, ctypes.c_int, vp, sz, vp]
         L.moe_mxfp4_quantize.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
         L.moe_mxfp4_prepack.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp]
         for name in ("moe_route", "moe_permute", "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine",
-                     "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_prepack"):
+                     "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_prepack", "moe_combine_residual",
+                     "moe_rmsnorm", "moe_block_forward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -165,6 +172,28 @@ def moe_forward(d, T, x, w_router, b_router, weights: moe_weights, y, y_dtype, w
         ws_bytes = ws.numel() * ws.element_size()
     _check(lib().moe_forward(ctypes.byref(d), T, _p(x), _p(w_router), _p(b_router), ctypes.byref(weights), _p(y),
                              y_dtype, _p(ws), ws_bytes, _s(stream)), "moe_forward")
+
+
+def moe_combine_residual(d, T, y_perm, inv, residual, y, y_dtype, stream=None):
+    _check(lib().moe_combine_residual(ctypes.byref(d), T, _p(y_perm), _p(inv), _p(residual), _p(y), y_dtype,
+                                      _s(stream)), "moe_combine_residual")
+
+
+def moe_rmsnorm(d, T, x, gamma, eps, xn, stream=None):
+    _check(lib().moe_rmsnorm(ctypes.byref(d), T, _p(x), _p(gamma), float(eps), _p(xn), _s(stream)), "moe_rmsnorm")
+
+
+def moe_block_workspace_bytes(d: moe_dims, T: int) -> int:
+    return lib().moe_block_workspace_bytes(ctypes.byref(d), T)
+
+
+def moe_block_forward(d, T, x, gamma, eps, w_router, b_router, weights: moe_weights, y, y_dtype, ws, ws_bytes=None,
+                      stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().moe_block_forward(ctypes.byref(d), T, _p(x), _p(gamma), float(eps), _p(w_router), _p(b_router),
+                                   ctypes.byref(weights), _p(y), y_dtype, _p(ws), ws_bytes, _s(stream)),
+           "moe_block_forward")
 
 
 def moe_mxfp4_quantize(w: np.ndarray):

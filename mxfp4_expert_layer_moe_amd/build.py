@@ -15,7 +15,8 @@ LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe_mxfp4.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "pack.hip", "gemm.hip", "gemm_prefill.hip", "combine.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "pack.hip", "gemm.hip", "gemm_prefill.hip", "combine.hip",
+           "norm.hip"]
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled: plain fp32 VALU only
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -66,6 +66,56 @@ WsLayout ws_layout(const moe_dims* d, int32_t T) {
   return L;
 }
 
+moe_status check_forward(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                         const float* b_router, const moe_weights* wts, const void* y, moe_dtype y_dtype,
+                         const void* ws) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (y_dtype != MOE_BF16 && y_dtype != MOE_FP32) return MOE_EINVAL;
+  if (!x_bf16 || !w_router || !b_router || !wts || !y || !ws) return MOE_EINVAL;
+  if (!wts->gu_codes || !wts->gu_scales || !wts->dn_codes || !wts->dn_scales) return MOE_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(b_router, 4) || !aligned(y, 16) ||
+      !aligned(ws, kAlignWs) || !aligned(wts->gu_codes, 16) || !aligned(wts->dn_codes, 16) ||
+      !aligned(wts->gu_scales, 4) || !aligned(wts->dn_scales, 4))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// normalised rows of the block forward, at the start of its workspace
+size_t block_xn_bytes(const moe_dims* d, int32_t T) {
+  return round_up((size_t)T * d->d_model * 2, kAlignWs);
+}
+
+// The layer on activations x (already validated; ws holds ws_layout(d, T).total bytes); with a
+// residual, the combine adds it to the output.
+moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const uint16_t* residual,
+                        const float* w_router, const float* b_router, const moe_weights* wts, void* y,
+                        moe_dtype y_dtype, uint8_t* base, hipStream_t stream) {
+  const WsLayout L = ws_layout(d, T);
+  int32_t* idx = (int32_t*)(base + L.idx);
+  float* w = (float*)(base + L.w);
+  int32_t* counts = (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* perm = (int32_t*)(base + L.perm);
+  int32_t* inv = (int32_t*)(base + L.inv);
+  int32_t* tiles = (int32_t*)(base + L.tiles);
+  uint8_t* xpack = base + L.xpack;
+  uint8_t* hpack = base + L.hpack;
+  _Float16* yperm = (_Float16*)(base + L.yperm);
+  const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
+  if (launch_route_front(T, D, E, k, x, w_router, b_router, idx, w, base + L.route, xpack, counts, offsets, perm,
+                         inv, tiles, stream))
+    return MOE_EHIP;
+  if (launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, tiles, wts->gu_codes, wts->gu_scales, nullptr, hpack,
+                  stream))
+    return MOE_EHIP;
+  if (launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, tiles, wts->dn_codes, wts->dn_scales, w, yperm, stream))
+    return MOE_EHIP;
+  if (launch_combine(T, D, k, yperm, inv, residual, y, y_dtype == MOE_BF16, stream)) return MOE_EHIP;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,50 +228,64 @@ moe_status moe_combine(const moe_dims* d, int32_t T, const void* y_perm, const i
   if (y_dtype != MOE_BF16 && y_dtype != MOE_FP32) return MOE_EINVAL;
   if (!y_perm || !inv || !y || !aligned(y_perm, 16) || !aligned(inv, 4) || !aligned(y, 16)) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
-  return hip_status(launch_combine(T, d->d_model, d->top_k, (const _Float16*)y_perm, inv, y, y_dtype == MOE_BF16,
-                                   stream));
+  return hip_status(launch_combine(T, d->d_model, d->top_k, (const _Float16*)y_perm, inv, nullptr, y,
+                                   y_dtype == MOE_BF16, stream));
+}
+
+moe_status moe_combine_residual(const moe_dims* d, int32_t T, const void* y_perm, const int32_t* inv,
+                                const void* residual_bf16, void* y, moe_dtype y_dtype, hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (y_dtype != MOE_BF16 && y_dtype != MOE_FP32) return MOE_EINVAL;
+  if (!y_perm || !inv || !residual_bf16 || !y || !aligned(y_perm, 16) || !aligned(inv, 4) ||
+      !aligned(residual_bf16, 16) || !aligned(y, 16))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_combine(T, d->d_model, d->top_k, (const _Float16*)y_perm, inv,
+                                   (const uint16_t*)residual_bf16, y, y_dtype == MOE_BF16, stream));
+}
+
+moe_status moe_rmsnorm(const moe_dims* d, int32_t T, const void* x_bf16, const float* gamma, float eps,
+                       void* xn_bf16, hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (!x_bf16 || !gamma || !xn_bf16 || !(eps > 0.0f) || !isfinite(eps)) return MOE_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(gamma, 16) || !aligned(xn_bf16, 16)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_rmsnorm(T, d->d_model, (const uint16_t*)x_bf16, gamma, eps, (uint16_t*)xn_bf16, stream));
 }
 
 moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
                        const float* b_router, const moe_weights* wts, void* y, moe_dtype y_dtype, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
-  moe_status st = check_dims(d);
+  moe_status st = check_forward(d, T, x_bf16, w_router, b_router, wts, y, y_dtype, ws);
   if (st != MOE_OK) return st;
-  if ((st = check_T(d, T)) != MOE_OK) return st;
-  if (y_dtype != MOE_BF16 && y_dtype != MOE_FP32) return MOE_EINVAL;
-  if (!x_bf16 || !w_router || !b_router || !wts || !y || !ws) return MOE_EINVAL;
-  if (!wts->gu_codes || !wts->gu_scales || !wts->dn_codes || !wts->dn_scales) return MOE_EINVAL;
-  if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(b_router, 4) || !aligned(y, 16) ||
-      !aligned(ws, kAlignWs) || !aligned(wts->gu_codes, 16) || !aligned(wts->dn_codes, 16) ||
-      !aligned(wts->gu_scales, 4) || !aligned(wts->dn_scales, 4))
-    return MOE_EINVAL;
-  const WsLayout L = ws_layout(d, T);
-  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (ws_bytes < ws_layout(d, T).total) return MOE_EWORKSPACE;
   if (T == 0) return MOE_OK;
-  uint8_t* base = (uint8_t*)ws;
-  int32_t* idx = (int32_t*)(base + L.idx);
-  float* w = (float*)(base + L.w);
-  int32_t* counts = (int32_t*)(base + L.counts);
-  int32_t* offsets = (int32_t*)(base + L.offsets);
-  int32_t* perm = (int32_t*)(base + L.perm);
-  int32_t* inv = (int32_t*)(base + L.inv);
-  int32_t* tiles = (int32_t*)(base + L.tiles);
-  uint8_t* xpack = base + L.xpack;
-  uint8_t* hpack = base + L.hpack;
-  _Float16* yperm = (_Float16*)(base + L.yperm);
-  const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
-  hipError_t e;
-  if ((e = launch_route_front(T, D, E, k, (const uint16_t*)x_bf16, w_router, b_router, idx, w, base + L.route, xpack,
-                              counts, offsets, perm, inv, tiles, stream)))
-    return MOE_EHIP;
-  if ((e = launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, tiles, wts->gu_codes, wts->gu_scales, nullptr,
-                       hpack, stream)))
-    return MOE_EHIP;
-  if ((e = launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, tiles, wts->dn_codes, wts->dn_scales, w, yperm,
-                       stream)))
-    return MOE_EHIP;
-  if ((e = launch_combine(T, D, k, yperm, inv, y, y_dtype == MOE_BF16, stream))) return MOE_EHIP;
-  return MOE_OK;
+  return forward_impl(d, T, (const uint16_t*)x_bf16, nullptr, w_router, b_router, wts, y, y_dtype,
+                      (uint8_t*)ws, stream);
+}
+
+size_t moe_block_workspace_bytes(const moe_dims* d, int32_t T) {
+  if (check_dims(d) != MOE_OK || check_T(d, T) != MOE_OK) return 0;
+  return block_xn_bytes(d, T) + ws_layout(d, T).total;
+}
+
+moe_status moe_block_forward(const moe_dims* d, int32_t T, const void* x_bf16, const float* gamma, float eps,
+                             const float* w_router, const float* b_router, const moe_weights* wts, void* y,
+                             moe_dtype y_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_forward(d, T, x_bf16, w_router, b_router, wts, y, y_dtype, ws);
+  if (st != MOE_OK) return st;
+  if (!gamma || !aligned(gamma, 16) || !(eps > 0.0f) || !isfinite(eps)) return MOE_EINVAL;
+  const size_t xn_bytes = block_xn_bytes(d, T);
+  if (ws_bytes < xn_bytes + ws_layout(d, T).total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  uint16_t* xn = (uint16_t*)ws;
+  if (launch_rmsnorm(T, d->d_model, (const uint16_t*)x_bf16, gamma, eps, xn, stream)) return MOE_EHIP;
+  return forward_impl(d, T, xn, (const uint16_t*)x_bf16, w_router, b_router, wts, y, y_dtype,
+                      (uint8_t*)ws + xn_bytes, stream);
 }
 
 // ---- host-only ---------------------------------------------------------------

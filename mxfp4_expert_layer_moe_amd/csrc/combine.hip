@@ -8,6 +8,11 @@
 // same bits on every run.  HBM-bound: reads k rows, writes one.  A thread owns 8
 // columns of a token and issues the index and row loads of 4 slots at a time, so
 // a token's gather costs two memory round trips per 4 slots.
+//
+// With a residual (the MoE half of a pre-norm transformer block, y = x + MoE(xn):
+// the block's input and output are both [N x D], "gpt-oss architecture
+// walk-through", section "Transformer Blocks"), the bf16 residual row is added
+// to the slot-order sum with one more fp32 addition.
 #include "moe_internal.h"
 
 namespace moe {
@@ -15,9 +20,10 @@ namespace moe {
 constexpr int kCombineCols = 8;        // columns per thread: one 16-byte fp16 load per row
 constexpr int kCombineBatch = 4;       // slots whose index and row loads are issued together
 
-template <bool BF16_OUT>
+template <bool BF16_OUT, bool RESIDUAL>
 __global__ __launch_bounds__(256) void combine_kernel(int T, int D, int k, const _Float16* __restrict__ y_perm,
-                                                      const int32_t* __restrict__ inv, void* __restrict__ y) {
+                                                      const int32_t* __restrict__ inv,
+                                                      const uint16_t* __restrict__ residual, void* __restrict__ y) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   const int d8 = D / kCombineCols;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -42,6 +48,15 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int D, int k, const
         for (int i = 0; i < kCombineCols; ++i) acc[i] += (float)v[u][i];
       }
   }
+  if constexpr (RESIDUAL) {
+    const uint4 r = *reinterpret_cast<const uint4*>(residual + (size_t)t * D + c);
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < kCombineCols / 2; ++i) {
+      acc[2 * i] = __uint_as_float(rw[i] << 16) + acc[2 * i];
+      acc[2 * i + 1] = __uint_as_float(rw[i] & 0xFFFF0000u) + acc[2 * i + 1];
+    }
+  }
   if (BF16_OUT) {
     uint32_t w[kCombineCols / 2];
 #pragma unroll
@@ -55,15 +70,18 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int D, int k, const
   }
 }
 
-hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, void* y, int y_bf16,
-                          hipStream_t s) {
+hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, const uint16_t* residual,
+                          void* y, int y_bf16, hipStream_t s) {
   const long long n = (long long)T * (D / kCombineCols);
   if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
-  if (y_bf16)
-    combine_kernel<true><<<dim3(blocks), dim3(256), 0, s>>>(T, D, k, y_perm, inv, y);
-  else
-    combine_kernel<false><<<dim3(blocks), dim3(256), 0, s>>>(T, D, k, y_perm, inv, y);
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (residual) {
+    if (y_bf16) combine_kernel<true, true><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, residual, y);
+    else combine_kernel<false, true><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, residual, y);
+  } else {
+    if (y_bf16) combine_kernel<true, false><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, nullptr, y);
+    else combine_kernel<false, false><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, nullptr, y);
+  }
   return hipGetLastError();
 }
 

@@ -124,7 +124,9 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
                                const uint8_t* scales, const float* topk_w, void* out, hipStream_t s);
-hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, void* y,
-                          int y_bf16, hipStream_t s);
+hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, const uint16_t* residual,
+                          void* y, int y_bf16, hipStream_t s);
+hipError_t launch_rmsnorm(int T, int D, const uint16_t* x, const float* gamma, float eps, uint16_t* xn,
+                          hipStream_t s);
 
 }  // namespace moe

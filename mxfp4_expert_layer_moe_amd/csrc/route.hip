@@ -52,20 +52,35 @@ __device__ inline double wave_sum_f64(double v) {
   return v;
 }
 
-// Exact float64 score of expert row wre for token row xr (bf16): 8-wide chunks per lane.
+// Exact float64 score of expert row wre for token row xr (bf16): 8-wide chunks per lane, the
+// loads of kScoreBatch chunks issued together (all of a 3072-wide row), summed in chunk order.
+constexpr int kScoreBatch = 6;
 __device__ double score_f64(const uint16_t* __restrict__ xr, const float* __restrict__ wre, double bias, int D,
                             int lane) {
   double acc = 0.0;
-  for (int c = lane; c < D / 8; c += 64) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(xr + 8 * c);
-    const float4 w0 = *reinterpret_cast<const float4*>(wre + 8 * c);
-    const float4 w1 = *reinterpret_cast<const float4*>(wre + 8 * c + 4);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    const float wf[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  const int nc = D / 8;
+  for (int c0 = lane; c0 < nc; c0 += 64 * kScoreBatch) {
+    uint4 xv[kScoreBatch];
+    float4 w0[kScoreBatch], w1[kScoreBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc += (double)__uint_as_float(xw[i] << 16) * (double)wf[2 * i];
-      acc += (double)__uint_as_float(xw[i] & 0xFFFF0000u) * (double)wf[2 * i + 1];
+    for (int b = 0; b < kScoreBatch; ++b) {
+      const int c = c0 + 64 * b;
+      if (c < nc) {
+        xv[b] = *reinterpret_cast<const uint4*>(xr + 8 * c);
+        w0[b] = *reinterpret_cast<const float4*>(wre + 8 * c);
+        w1[b] = *reinterpret_cast<const float4*>(wre + 8 * c + 4);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kScoreBatch; ++b) {
+      if (c0 + 64 * b >= nc) break;
+      const uint32_t xw[4] = {xv[b].x, xv[b].y, xv[b].z, xv[b].w};
+      const float wf[8] = {w0[b].x, w0[b].y, w0[b].z, w0[b].w, w1[b].x, w1[b].y, w1[b].z, w1[b].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc += (double)__uint_as_float(xw[i] << 16) * (double)wf[2 * i];
+        acc += (double)__uint_as_float(xw[i] & 0xFFFF0000u) * (double)wf[2 * i + 1];
+      }
     }
   }
   return wave_sum_f64(acc) + bias;
@@ -455,6 +470,7 @@ __global__ __launch_bounds__(1024) void route_select_small_kernel(
   __shared__ double kth[32], top[32];         // k-th and largest selected score per token
   __shared__ float ex_l[32][33];              // gate numerators
   __shared__ uint32_t smask[32];              // selected experts per token (bit e)
+  __shared__ uint32_t fmask[32];              // candidates of the flagged tokens (0: not flagged)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int t = tid >> 5, e = tid & 31;
@@ -514,21 +530,31 @@ __global__ __launch_bounds__(1024) void route_select_small_kernel(
     cand = sel || v0 >= kth[t] - band;
   }
   const uint32_t cm = (uint32_t)(__ballot(cand) >> hshift);
-  // flagged tokens of this wavefront: re-score every candidate exactly (the whole wavefront
-  // per score), then rank again among the candidates
+  const bool flagged = live && __popc(cm) > k;
+  // flagged tokens: re-score every (token, candidate) pair exactly, the pairs dealt to the 16
+  // wavefronts in token-then-expert order (one wavefront per score), then rank again among the
+  // candidates.  The whole section is skipped when no token is flagged.
   double v = v0;
-  for (int h = 0; h < 2; ++h) {                          // uniform
-    const int th = 2 * (tid >> 6) + h;
-    uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)cm, 32 * h);
-    if (th >= T || __popc(m) <= k) continue;
-    while (m) {
-      const int j = __ffs(m) - 1;
-      m &= m - 1;
-      const double sc = score_f64(x + (size_t)th * D, wr + (size_t)j * D, (double)br[j], D, lane);
-      if (lane == 0) lt[th][j] = sc;
+  if (__syncthreads_or(flagged)) {
+    if (e == 0) fmask[t] = flagged ? cm : 0u;
+    __syncthreads();
+    const int wave = tid >> 6;
+    int i = 0;
+    for (int tt = 0; tt < T; ++tt) {
+      uint32_t m = fmask[tt];                            // uniform
+      while (m) {
+        const int j = __ffs(m) - 1;
+        m &= m - 1;
+        if ((i & 15) == wave) {
+          const double sc = score_f64(x + (size_t)tt * D, wr + (size_t)j * D, (double)br[j], D, lane);
+          if (lane == 0) lt[tt][j] = sc;
+        }
+        ++i;
+      }
     }
+    __syncthreads();
   }
-  if (live && __popc(cm) > k) {
+  if (flagged) {
     v = cand ? lt[t][e] : -INFINITY;
     rank = 0;
 #pragma unroll

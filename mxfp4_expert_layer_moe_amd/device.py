@@ -9,9 +9,10 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_FP32, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, dims, moe_act_pack_bytes, moe_combine,
-               moe_expert_gemm_mxfp4, moe_forward, moe_mxfp4_prepack, moe_pack_act, moe_permute, moe_route,
-               moe_route_workspace_bytes, moe_tile_table_bytes, moe_weights, moe_workspace_bytes)
+from . import (MOE_BF16, MOE_FP32, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, dims, moe_act_pack_bytes,
+               moe_block_forward, moe_block_workspace_bytes, moe_combine, moe_combine_residual,
+               moe_expert_gemm_mxfp4, moe_forward, moe_mxfp4_prepack, moe_pack_act, moe_permute, moe_rmsnorm,
+               moe_route, moe_route_workspace_bytes, moe_tile_table_bytes, moe_weights, moe_workspace_bytes)
 
 
 def _u8(a: np.ndarray, device) -> torch.Tensor:
@@ -75,18 +76,24 @@ class DeviceLayer:
         self.ws = torch.empty(max(moe_workspace_bytes(self.dims, T), 256), dtype=torch.uint8, device=device)
         self.route_ws = torch.empty(max(moe_route_workspace_bytes(self.dims, T), 256), dtype=torch.uint8,
                                     device=device)
+        # the pre-norm block around the layer: RMSNorm scale, normalised rows, block workspace
+        gamma = inp.norm_weight if getattr(inp, "norm_weight", None) is not None else np.ones(D, np.float32)
+        self.gamma = torch.from_numpy(np.ascontiguousarray(gamma, dtype=np.float32)).to(device)
+        self.eps = float(getattr(inp, "norm_eps", 1e-5))
+        self.xn = torch.empty((T, D), dtype=torch.bfloat16, device=device)
+        self.block_ws = None
 
     # ---- step by step (the C entry points in order) ---------------------------
-    def route(self, logits=True, stream=None):
-        moe_route(self.dims, self.T, self.x, self.w_router, self.b_router, self.topk_idx, self.topk_w,
-                  self.logits if logits else None, self.route_ws, None, stream)
+    def route(self, logits=True, stream=None, x=None):
+        moe_route(self.dims, self.T, self.x if x is None else x, self.w_router, self.b_router, self.topk_idx,
+                  self.topk_w, self.logits if logits else None, self.route_ws, None, stream)
 
     def permute(self, stream=None):
         moe_permute(self.dims, self.T, self.topk_idx, self.counts, self.offsets, self.perm, self.inv, self.tiles,
                     stream)
 
-    def pack_x(self, stream=None):
-        moe_pack_act(self.D, self.T, self.x, self.x_packed, stream)
+    def pack_x(self, stream=None, x=None):
+        moe_pack_act(self.D, self.T, self.x if x is None else x, self.x_packed, stream)
 
     def gate_up(self, weights: DeviceWeights | None = None, stream=None):
         w = weights or self.weights
@@ -98,9 +105,12 @@ class DeviceLayer:
         moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_DOWN, self.h_packed, self.tiles, w.dn_codes,
                               w.dn_scales, self.topk_w, self.y_perm, stream)
 
-    def combine(self, bf16=False, stream=None):
-        moe_combine(self.dims, self.T, self.y_perm, self.inv, self.y16 if bf16 else self.y32,
-                    MOE_BF16 if bf16 else MOE_FP32, stream)
+    def combine(self, bf16=False, stream=None, residual=None):
+        y, dt = (self.y16, MOE_BF16) if bf16 else (self.y32, MOE_FP32)
+        if residual is None:
+            moe_combine(self.dims, self.T, self.y_perm, self.inv, y, dt, stream)
+        else:
+            moe_combine_residual(self.dims, self.T, self.y_perm, self.inv, residual, y, dt, stream)
 
     def steps(self, bf16=False, stream=None):
         self.route(stream=stream)
@@ -109,6 +119,29 @@ class DeviceLayer:
         self.gate_up(stream=stream)
         self.down(stream=stream)
         self.combine(bf16, stream)
+
+    # ---- the pre-norm block: y = x + MoE(RMSNorm(x)) --------------------------
+    def rmsnorm(self, stream=None):
+        moe_rmsnorm(self.dims, self.T, self.x, self.gamma, self.eps, self.xn, stream)
+
+    def block_steps(self, bf16=False, stream=None):
+        self.rmsnorm(stream)
+        self.route(stream=stream, x=self.xn)
+        self.permute(stream)
+        self.pack_x(stream, x=self.xn)
+        self.gate_up(stream=stream)
+        self.down(stream=stream)
+        self.combine(bf16, stream, residual=self.x)
+
+    def block_forward(self, bf16=False, weights: DeviceWeights | None = None, stream=None):
+        w = weights or self.weights
+        if self.block_ws is None:
+            self.block_ws = torch.empty(max(moe_block_workspace_bytes(self.dims, self.T), 256), dtype=torch.uint8,
+                                        device=self.device)
+        y, dt = (self.y16, MOE_BF16) if bf16 else (self.y32, MOE_FP32)
+        moe_block_forward(self.dims, self.T, self.x, self.gamma, self.eps, self.w_router, self.b_router, w.struct(),
+                          y, dt, self.block_ws, None, stream)
+        return y
 
     def forward(self, bf16=False, weights: DeviceWeights | None = None, stream=None):
         w = weights or self.weights

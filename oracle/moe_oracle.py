@@ -24,12 +24,25 @@ pages describe the layer:
      specification;
   6. combine: the weighted sum of the selected experts' outputs.
 
+Around the layer, the MoE half of a pre-norm transformer block (block_forward):
+  0. RMSNorm of the block input: divide by the root mean square, multiply by a
+     learned per-channel scale, no mean, no bias [From GPT-2 to gpt-oss,
+     section 7 "RMSNorm replaces LayerNorm", Fig. 11-12]; eps = rms_norm_eps =
+     1e-5 [model card config tables]; every transformer block holds two such
+     normalisations [walk-through, "Transformer Blocks"];
+  7. residual: the block output adds the MoE output to the block input (the
+     block maps [N x 2880] to [N x 2880]; residual/shortcut connections are
+     named in the From-GPT-2 page's width-versus-depth discussion).
+
 Readings where the pages are silent (each one is listed in the design notes):
 router = linear map with bias; softmax over the k selected logits; exact
 ties go to the lower expert id; the k slots of a token are stored in
 ascending expert id; the permutation is stable by token within an expert;
 the clamp applies to both gate and up pre-activations before silu(g) * u;
-h is rounded to bf16 (round to nearest even) before the down projection.
+h is rounded to bf16 (round to nearest even) before the down projection;
+the normalised activations are rounded once to bf16 (the expert path takes
+bf16 activations), the RMS in float64 with eps widened from its fp32 value;
+the residual block is pre-norm, y = x + MoE(RMSNorm(x)).
 
 Parity status: every function here is pinned by the CPU tests
 (exhaustive decode table, closed forms, the 0.7/0.3 example, brute force
@@ -223,6 +236,42 @@ def forward(inp, tokens=None, override_idx: dict | None = None) -> dict:
     y = combine(w, z_perm, inv, tokens, k)
     return dict(logits=logits, idx=idx, flagged=flagged, gap=gap, w=w, counts=counts,
                 offsets=offsets, perm=perm, inv=inv, tokens=tokens, h=h_all, z=z_all, y=y)
+
+
+# ----------------------------------------------------------------------------
+# The block around the layer: RMSNorm before it, the residual after it
+# ----------------------------------------------------------------------------
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of the rows of x [From GPT-2 to gpt-oss, section 7, Fig. 12]:
+    x / sqrt(mean over the row of x^2 + eps), times the per-channel scale gamma,
+    rounded to bf16.  float64 throughout; eps is the fp32 value the layer is given."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=1)
+    r = 1.0 / np.sqrt(ms + float(np.float32(eps)))
+    return round_to_bf16((x * r[:, None]) * np.asarray(gamma, dtype=np.float64)[None, :])
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of float64 values that are already bf16 values (exact)."""
+    return (np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def block_forward(inp, tokens=None, override_idx: dict | None = None) -> dict:
+    """The MoE half of a pre-norm transformer block: y = x + MoE(RMSNorm(x)).
+
+    inp additionally carries norm_weight (gamma, fp32 [D]) and norm_eps.  Returns
+    forward()'s dict computed on the normalised rows, with xn (float64 [T][D],
+    bf16 values), y_moe (the layer output) and y = x + y_moe for the evaluated
+    tokens."""
+    import dataclasses
+    x = bf16_to_f64(inp.x_bf16)
+    xn = rms_norm(x, inp.norm_weight, inp.norm_eps)
+    inner = dataclasses.replace(inp, x_bf16=f64_to_bf16_bits(xn))
+    o = forward(inner, tokens=tokens, override_idx=override_idx)
+    o["xn"] = xn
+    o["y_moe"] = o["y"]
+    o["y"] = x[o["tokens"]] + o["y_moe"]
+    return o
 
 
 # ----------------------------------------------------------------------------

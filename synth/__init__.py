@@ -8,6 +8,7 @@ expert evaluation) and imports neither the oracle nor the HIP library.
 """
 from .gen import (  # noqa: F401
     CONFIGS,
+    RMS_NORM_EPS,
     SWIGLU_LIMIT,
     LayerInputs,
     bf16_bits_to_f32,

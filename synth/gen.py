@@ -10,6 +10,8 @@ with one 8-bit E8M0 scale per 32 consecutive values along the reduction axis
 
 Distributions (the same for every workload):
   * x ~ N(0, 1) drawn in fp32, rounded to bf16 (round to nearest even);
+  * RMSNorm scale gamma ~ 1 + N(0, 0.1), fp32, and eps = 1e-5 (model cards'
+    rms_norm_eps), for the pre-norm block around the layer;
   * router weight ~ N(0, 0.02), router bias ~ N(0, 0.01), both fp32;
   * expert gate / up / down weights ~ N(0, 0.02) in fp32, then encoded to
     MXFP4 with the OCP Microscaling v1.0 conversion rule (shared exponent
@@ -36,9 +38,10 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 SWIGLU_LIMIT = 7.0
+RMS_NORM_EPS = 1e-5
 
 # Substream tags.
-_TAG_X, _TAG_WR, _TAG_BR, _TAG_GATE, _TAG_UP, _TAG_DOWN, _TAG_PERM = range(7)
+_TAG_X, _TAG_WR, _TAG_BR, _TAG_GATE, _TAG_UP, _TAG_DOWN, _TAG_PERM, _TAG_NORM = range(8)
 
 # Router-bias exponent of the skewed workload: expert popularity p(r) ~ r^-1.2
 # for popularity rank r = 1..E.  The bias is beta * ln p(r) (up to a constant
@@ -74,6 +77,8 @@ class LayerInputs:
     dn_codes: np.ndarray    # uint8 [E][D][I/2]
     dn_scales: np.ndarray   # uint8 [E][D][I/32]
     desc: dict
+    norm_weight: np.ndarray | None = None   # float32 [D]: RMSNorm scale of the block
+    norm_eps: float = RMS_NORM_EPS
 
     @property
     def x_f32(self) -> np.ndarray:
@@ -204,8 +209,9 @@ def make_inputs(cfg: int | dict = 0, *, T: int | None = None, x_scale: float = 1
             for res in ex.map(lambda e: _expert_weights(s, e, D, I), range(Ew)):
                 store(res)
     c["x_scale"] = x_scale
+    gamma = np.float32(1.0) + _rng(s, _TAG_NORM).standard_normal(D, dtype=np.float32) * np.float32(0.1)
     return LayerInputs(Tn, D, E, k, I, SWIGLU_LIMIT, x_bf16, wr, br,
-                       gu_codes, gu_scales, dn_codes, dn_scales, c)
+                       gu_codes, gu_scales, dn_codes, dn_scales, c, gamma, RMS_NORM_EPS)
 
 
 def zipf_popularity(E: int) -> np.ndarray:

@@ -293,3 +293,62 @@ def test_workload_routing_has_no_near_ties(cfg):
     assert flagged.sum() <= 2
     if cfg == 1:
         assert (counts > 0).sum() >= 28          # near-uniform load at decode
+
+
+# --------------------------------------------------------------------------- RMSNorm and residual block
+def test_rms_norm_hand_computed_row():
+    """[3, 4, 0, 0]: mean square 25/4, RMS 2.5, so 1.2 and 1.6; bf16 keeps 8 significant bits
+    (1.0011001|1001.. and 1.1001100|1100.. both round up): 1.203125 and 1.6015625."""
+    got = oracle.rms_norm(np.array([[3.0, 4.0, 0.0, 0.0]]), np.ones(4), 0.0)
+    assert got.tolist() == [[1.203125, 1.6015625, 0.0, 0.0]]
+
+
+def test_rms_norm_divides_by_the_mean_not_the_sum():
+    """Fifteen ones and a seven: sum of squares 64 over 16 channels, mean 4, RMS 2 (exact)."""
+    x = np.array([[1.0] * 15 + [7.0]])
+    assert oracle.rms_norm(x, np.ones(16), 0.0).tolist() == [[0.5] * 15 + [3.5]]
+
+
+def test_rms_norm_eps_is_added_to_the_mean_square():
+    """Constant rows of 1/8 with eps = 3/64 (exact in fp32): sqrt(1/64 + 3/64) = 1/4, output 1/2."""
+    x = np.full((3, 64), 0.125)
+    assert np.all(oracle.rms_norm(x, np.ones(64), 3.0 / 64.0) == 0.5)
+
+
+def test_rms_norm_scale_is_per_channel():
+    """A constant row has RMS equal to its value, so with eps = 0 the output is gamma itself."""
+    gamma = np.array([1.0, 2.0, 0.5, -1.0, 0.25, 3.0, -0.75, 1.5])
+    assert np.array_equal(oracle.rms_norm(np.full((2, 8), 2.0), gamma, 0.0), np.tile(gamma, (2, 1)))
+
+
+def test_rms_norm_is_invariant_to_power_of_two_scaling_and_has_unit_rms():
+    """RMSNorm(2^j x) = RMSNorm(x) bit for bit when eps = 0 (every step scales exactly); the
+    normalised rows have mean square 1 up to the bf16 rounding (relative 2^-8)."""
+    x = synth.bf16_bits_to_f32(synth.make_inputs(0).x_bf16).astype(np.float64)
+    base = oracle.rms_norm(x, np.ones(x.shape[1]), 0.0)
+    for j in (-7, -1, 3, 20):
+        assert np.array_equal(oracle.rms_norm(x * 2.0 ** j, np.ones(x.shape[1]), 0.0), base)
+    assert np.allclose(np.mean(base ** 2, axis=1), 1.0, rtol=2.0 ** -7)
+
+
+def test_block_with_zero_experts_returns_its_input():
+    """All-zero expert weights (code 0 is +0): the MoE output is 0 and the block output is x."""
+    inp = synth.make_inputs(0)
+    inp.gu_codes[:] = 0
+    inp.dn_codes[:] = 0
+    o = oracle.block_forward(inp)
+    assert np.all(o["y_moe"] == 0.0)
+    assert np.array_equal(o["y"], oracle.bf16_to_f64(inp.x_bf16))
+
+
+def test_block_is_the_layer_on_the_normalised_rows_plus_the_input():
+    """block_forward = forward on bf16(RMSNorm(x)) (itself pinned by the dense brute force),
+    plus x."""
+    import dataclasses
+    inp = synth.make_inputs(dict(T=9, D=64, E=4, k=2, I=64, seed=7))
+    o = oracle.block_forward(inp)
+    xn = oracle.rms_norm(oracle.bf16_to_f64(inp.x_bf16), inp.norm_weight, inp.norm_eps)
+    inner = dataclasses.replace(inp, x_bf16=synth.f32_to_bf16_bits(xn.astype(np.float32)))
+    ref = np.array(brute.brute_layer(inner)["y"])
+    assert np.abs(o["y_moe"] - ref).max() <= 1e-12 * np.abs(ref).max()
+    assert np.array_equal(o["y"], oracle.bf16_to_f64(inp.x_bf16) + o["y_moe"])
