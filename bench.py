@@ -50,6 +50,7 @@ def parse():
                    help="summarise a rocprofv3 --stats kernel table as text, then exit")
     p.add_argument("--command", default="", help="the command that made the profile (for the reports)")
     p.add_argument("--no-block", action="store_true", help="skip the timing of the pre-norm block forward")
+    p.add_argument("--no-act4", action="store_true", help="skip the timing of the MXFP4-activation variant")
     return p.parse_args()
 
 
@@ -236,6 +237,22 @@ def main():
                  "ms_per_step": round(b_ms, 5), "tokens_per_s": round(T / (b_ms * 1e-3), 1),
                  "extra_ms_over_layer": round(b_ms - ms_step, 5)}
 
+    # ---- the activation-quantized variant (MXFP4 activations), same steps ---------
+    act4 = None
+    if not args.no_act4:
+        for s in range(args.warmup):
+            layer.forward_act4(weights=copies[s % L])
+        torch.cuda.synchronize()
+        e40, e41 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e40.record(stream)
+        for s in range(args.steps):
+            layer.forward_act4(weights=copies[s % L])
+        e41.record(stream)
+        torch.cuda.synchronize()
+        a_ms = e40.elapsed_time(e41) / args.steps
+        act4 = {"what": "MXFP4 activations into the expert GEMMs (moe_forward_act4; a lower-precision contract)",
+                "ms_per_step": round(a_ms, 5), "tokens_per_s": round(T / (a_ms * 1e-3), 1)}
+
     # ---- dominant kernel alone: gate/up expert GEMM, per-launch HIP events -----
     layer.route(logits=False)
     layer.permute()
@@ -299,6 +316,8 @@ def main():
     }
     if block is not None:
         out["block"] = block
+    if act4 is not None:
+        out["act4"] = act4
     if args.copy_mib > 0:                     # counter calibration: plain copies of known size, untimed
         n = args.copy_mib * 2 ** 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda")

@@ -47,6 +47,16 @@
  * A block's 32 codes are 6-bit fields packed little-endian (element i at bits
  * 6i..6i+5); E2M3 = sign | 2 exponent bits (bias 1) | 3 mantissa bits.
  *
+ * MXFP4 activation pack format (the activation-quantized entry points, *_act4)
+ * ----------------------------------------------------------------------------
+ * Activations quantized to MXFP4 with the OCP MX v1.0 conversion: per 32-value
+ * block, shared exponent floor(log2 amax) - 2 as an E8M0 byte, elements rounded
+ * to the nearest E2M1 value (ties to the even code), saturating at +-6; an
+ * all-zero block gets scale byte 0.  A row of K values is (K/64) chunks of 48
+ * bytes (moe_act4_pack_bytes): [0,16) codes of block 2kt (element i in nibble i,
+ * low nibble first), [16,32) codes of block 2kt+1, [32] [33] their scales,
+ * [34,48) unused.
+ *
  * Prepacked weight format
  * -----------------------
  * moe_mxfp4_prepack reorders canonical MXFP4 bytes (codes [E][N][K/2], even K
@@ -225,6 +235,31 @@ moe_status moe_rmsnorm(const moe_dims* dims, int32_t T, const void* x_bf16, cons
 moe_status moe_forward(const moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
                        const float* b_router, const moe_weights* weights, void* y, moe_dtype y_dtype,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The activation-quantized variant (W4A4): the expert GEMMs take their
+ * activations as MXFP4 (format above) and run one FP4 x FP4 scaled matrix
+ * instruction per weight tile, the full MXFP4 rate of the matrix cores (the
+ * pages: the hardware supports MXFP4; "From GPT-2 to gpt-oss", section
+ * "MXFP4").  The router and the permutation are those of the default path (on
+ * the bf16 x); x is quantized for the gate/up GEMM and h = bf16(silu(clamp g) *
+ * clamp u) is quantized in the gate/up epilogue for the down GEMM.  The result
+ * is not the W4A16 layer of moe_forward: it is a different, lower-precision
+ * contract.
+ *   moe_pack_act4:               bf16 rows -> MXFP4 rows
+ *   moe_expert_gemm_mxfp4_act4:  as moe_expert_gemm_mxfp4 with MXFP4 activations
+ *                                (stage GATE_UP writes h in the MXFP4 format)
+ *   moe_forward_act4:            the whole layer; ws of moe_workspace_bytes_act4
+ */
+size_t moe_act4_pack_bytes(int32_t K, int32_t rows);
+moe_status moe_pack_act4(int32_t K, int32_t rows, const void* a_bf16, void* a_packed4, hipStream_t stream);
+moe_status moe_expert_gemm_mxfp4_act4(const moe_dims* dims, int32_t T, moe_stage stage, const void* a_packed4,
+                                      const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
+                                      const float* topk_w, void* out, hipStream_t stream);
+size_t moe_workspace_bytes_act4(const moe_dims* dims, int32_t T);
+moe_status moe_forward_act4(const moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                            const float* b_router, const moe_weights* weights, void* y, moe_dtype y_dtype,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * The MoE half of a pre-norm transformer block: y = x + MoE(RMSNorm(x)), i.e.

@@ -25,7 +25,8 @@ EXPORTS = ("moe_status_str", "moe_act_pack_bytes", "moe_prepacked_codes_bytes", 
            "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes", "moe_route", "moe_permute",
            "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine", "moe_forward", "moe_mxfp4_quantize",
            "moe_mxfp4_prepack", "moe_combine_residual", "moe_rmsnorm", "moe_block_workspace_bytes",
-           "moe_block_forward")
+           "moe_block_forward", "moe_act4_pack_bytes", "moe_pack_act4", "moe_expert_gemm_mxfp4_act4",
+           "moe_workspace_bytes_act4", "moe_forward_act4")
 
 
 class MoeError(RuntimeError):
@@ -64,7 +65,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, ctypes.c_int]
         for name in ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes",
-                     "moe_block_workspace_bytes"):
+                     "moe_block_workspace_bytes", "moe_workspace_bytes_act4"):
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, i32]
         L.moe_route.argtypes = [dp, i32, vp, f32p, f32p, i32p, f32p, f32p, vp, sz, vp]
@@ -74,6 +75,12 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [dp, i32, f32p, i32p, vp, ctypes.c_int, vp]
         L.moe_forward.argtypes = [dp, i32, vp, f32p, f32p, ctypes.POINTER(moe_weights), vp, ctypes.c_int, vp, sz, vp]
         L.moe_combine_residual.argtypes = [dp, i32, vp, i32p, vp, vp, ctypes.c_int, vp]
+        L.moe_act4_pack_bytes.restype = sz
+        L.moe_act4_pack_bytes.argtypes = [i32, i32]
+        L.moe_pack_act4.argtypes = [i32, i32, vp, vp, vp]
+        L.moe_expert_gemm_mxfp4_act4.argtypes = [dp, i32, ctypes.c_int, vp, i32p, vp, vp, f32p, vp, vp]
+        L.moe_forward_act4.argtypes = [dp, i32, vp, f32p, f32p, ctypes.POINTER(moe_weights), vp, ctypes.c_int, vp,
+                                       sz, vp]
         L.moe_rmsnorm.argtypes = [dp, i32, vp, f32p, ctypes.c_float, vp, vp]
         L.moe_block_forward.argtypes = [dp, i32, vp, f32p, ctypes.c_float, f32p, f32p, ctypes.POINTER(moe_weights),
                                         vp, ctypes.c_int, vp, sz, vp]
@@ -81,7 +88,8 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp4_prepack.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp]
         for name in ("moe_route", "moe_permute", "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine",
                      "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_prepack", "moe_combine_residual",
-                     "moe_rmsnorm", "moe_block_forward"):
+                     "moe_rmsnorm", "moe_block_forward", "moe_pack_act4", "moe_expert_gemm_mxfp4_act4",
+                     "moe_forward_act4"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -194,6 +202,30 @@ def moe_block_forward(d, T, x, gamma, eps, w_router, b_router, weights: moe_weig
     _check(lib().moe_block_forward(ctypes.byref(d), T, _p(x), _p(gamma), float(eps), _p(w_router), _p(b_router),
                                    ctypes.byref(weights), _p(y), y_dtype, _p(ws), ws_bytes, _s(stream)),
            "moe_block_forward")
+
+
+def moe_act4_pack_bytes(K: int, rows: int) -> int:
+    return lib().moe_act4_pack_bytes(K, rows)
+
+
+def moe_pack_act4(K, rows, a, a_packed4, stream=None):
+    _check(lib().moe_pack_act4(K, rows, _p(a), _p(a_packed4), _s(stream)), "moe_pack_act4")
+
+
+def moe_expert_gemm_mxfp4_act4(d, T, stage, a_packed4, tiles, codes, scales, topk_w, out, stream=None):
+    _check(lib().moe_expert_gemm_mxfp4_act4(ctypes.byref(d), T, stage, _p(a_packed4), _p(tiles), _p(codes),
+                                            _p(scales), _p(topk_w), _p(out), _s(stream)), "moe_expert_gemm_mxfp4_act4")
+
+
+def moe_workspace_bytes_act4(d: moe_dims, T: int) -> int:
+    return lib().moe_workspace_bytes_act4(ctypes.byref(d), T)
+
+
+def moe_forward_act4(d, T, x, w_router, b_router, weights: moe_weights, y, y_dtype, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().moe_forward_act4(ctypes.byref(d), T, _p(x), _p(w_router), _p(b_router), ctypes.byref(weights),
+                                  _p(y), y_dtype, _p(ws), ws_bytes, _s(stream)), "moe_forward_act4")
 
 
 def moe_mxfp4_quantize(w: np.ndarray):

@@ -46,7 +46,7 @@ size_t tile_table_bytes(const moe_dims* d, int32_t T) {
   return (size_t)(tile_buffer_ints(n, d->n_experts) + 3) / 4 * 16;
 }
 
-WsLayout ws_layout(const moe_dims* d, int32_t T) {
+WsLayout ws_layout(const moe_dims* d, int32_t T, int af = kActSplit6) {
   WsLayout L;
   const size_t n = (size_t)T * d->top_k;
   size_t o = 0;
@@ -58,8 +58,8 @@ WsLayout ws_layout(const moe_dims* d, int32_t T) {
   L.perm = take(n * 4);
   L.inv = take(n * 4);
   L.tiles = take(tile_table_bytes(d, T));
-  L.xpack = take((size_t)T * act_row_bytes(d->d_model));
-  L.hpack = take(n * act_row_bytes(d->d_ff));
+  L.xpack = take((size_t)T * act_row_bytes_af(af, d->d_model));
+  L.hpack = take(n * act_row_bytes_af(af, d->d_ff));
   L.yperm = take(n * (size_t)d->d_model * 2);
   L.route = take(route_workspace_bytes(T, d->d_model, d->n_experts));
   L.total = o;
@@ -91,8 +91,8 @@ size_t block_xn_bytes(const moe_dims* d, int32_t T) {
 // residual, the combine adds it to the output.
 moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const uint16_t* residual,
                         const float* w_router, const float* b_router, const moe_weights* wts, void* y,
-                        moe_dtype y_dtype, uint8_t* base, hipStream_t stream) {
-  const WsLayout L = ws_layout(d, T);
+                        moe_dtype y_dtype, uint8_t* base, hipStream_t stream, int af = kActSplit6) {
+  const WsLayout L = ws_layout(d, T, af);
   int32_t* idx = (int32_t*)(base + L.idx);
   float* w = (float*)(base + L.w);
   int32_t* counts = (int32_t*)(base + L.counts);
@@ -105,12 +105,13 @@ moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const u
   _Float16* yperm = (_Float16*)(base + L.yperm);
   const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
   if (launch_route_front(T, D, E, k, x, w_router, b_router, idx, w, base + L.route, xpack, counts, offsets, perm,
-                         inv, tiles, stream))
+                         inv, tiles, stream, af))
     return MOE_EHIP;
   if (launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, tiles, wts->gu_codes, wts->gu_scales, nullptr, hpack,
-                  stream))
+                  stream, af))
     return MOE_EHIP;
-  if (launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, tiles, wts->dn_codes, wts->dn_scales, w, yperm, stream))
+  if (launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, tiles, wts->dn_codes, wts->dn_scales, w, yperm, stream,
+                  af))
     return MOE_EHIP;
   if (launch_combine(T, D, k, yperm, inv, residual, y, y_dtype == MOE_BF16, stream)) return MOE_EHIP;
   return MOE_OK;
@@ -202,9 +203,22 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
   return hip_status(launch_pack(K, rows, (const uint16_t*)a_bf16, (uint8_t*)a_packed, stream));
 }
 
-moe_status moe_expert_gemm_mxfp4(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed,
-                                 const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
-                                 const float* topk_w, void* out, hipStream_t stream) {
+size_t moe_act4_pack_bytes(int32_t K, int32_t rows) {
+  if (K <= 0 || K % kKTile || rows < 0) return 0;
+  return (size_t)rows * act4_row_bytes(K);
+}
+
+moe_status moe_pack_act4(int32_t K, int32_t rows, const void* a_bf16, void* a_packed4, hipStream_t stream) {
+  if (K <= 0 || rows < 0) return MOE_EINVAL;
+  if (K % kKTile) return MOE_EUNSUPPORTED;
+  if (!a_bf16 || !a_packed4 || !aligned(a_bf16, 16) || !aligned(a_packed4, 16)) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  return hip_status(launch_pack(K, rows, (const uint16_t*)a_bf16, (uint8_t*)a_packed4, stream, kActFp4));
+}
+
+static moe_status expert_gemm(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed,
+                              const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
+                              const float* topk_w, void* out, hipStream_t stream, int af) {
   moe_status st = check_dims(d);
   if (st != MOE_OK) return st;
   if ((st = check_T(d, T)) != MOE_OK) return st;
@@ -217,7 +231,19 @@ moe_status moe_expert_gemm_mxfp4(const moe_dims* d, int32_t T, moe_stage stage, 
   if (T == 0) return MOE_OK;
   return hip_status(launch_gemm(stage == MOE_STAGE_GATE_UP ? 0 : 1, T, d->d_model, d->d_ff, d->n_experts,
                                 d->top_k, d->swiglu_limit, (const uint8_t*)a_packed, tiles, codes, scales, topk_w,
-                                out, stream));
+                                out, stream, af));
+}
+
+moe_status moe_expert_gemm_mxfp4(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed,
+                                 const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
+                                 const float* topk_w, void* out, hipStream_t stream) {
+  return expert_gemm(d, T, stage, a_packed, tiles, codes, scales, topk_w, out, stream, kActSplit6);
+}
+
+moe_status moe_expert_gemm_mxfp4_act4(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed4,
+                                      const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
+                                      const float* topk_w, void* out, hipStream_t stream) {
+  return expert_gemm(d, T, stage, a_packed4, tiles, codes, scales, topk_w, out, stream, kActFp4);
 }
 
 moe_status moe_combine(const moe_dims* d, int32_t T, const void* y_perm, const int32_t* inv, void* y,
@@ -266,6 +292,22 @@ moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const f
   if (T == 0) return MOE_OK;
   return forward_impl(d, T, (const uint16_t*)x_bf16, nullptr, w_router, b_router, wts, y, y_dtype,
                       (uint8_t*)ws, stream);
+}
+
+size_t moe_workspace_bytes_act4(const moe_dims* d, int32_t T) {
+  if (check_dims(d) != MOE_OK || check_T(d, T) != MOE_OK) return 0;
+  return ws_layout(d, T, kActFp4).total;
+}
+
+moe_status moe_forward_act4(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                            const float* b_router, const moe_weights* wts, void* y, moe_dtype y_dtype, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_forward(d, T, x_bf16, w_router, b_router, wts, y, y_dtype, ws);
+  if (st != MOE_OK) return st;
+  if (ws_bytes < ws_layout(d, T, kActFp4).total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  return forward_impl(d, T, (const uint16_t*)x_bf16, nullptr, w_router, b_router, wts, y, y_dtype,
+                      (uint8_t*)ws, stream, kActFp4);
 }
 
 size_t moe_block_workspace_bytes(const moe_dims* d, int32_t T) {

@@ -16,6 +16,9 @@
 // dword, byte `opsel`.  Result: lane l, register r holds row 8(r/4)+4(l/32)+r%4,
 // column l%32.
 //
+// The activation-quantized variant (AF = kActFp4) takes A as MXFP4 (one FP4 x FP4 instruction per
+// weight tile, 48-byte chunks per k-tile) and quantizes h to MXFP4 in the gate/up epilogue.
+//
 // Work decomposition: grid.y walks the row tiles of every expert (the row-tile
 // table written by the permutation; empty slots exit), and
 // grid.x walks output units: a gate/up pair of 32-column tiles (stage 0) or
@@ -50,7 +53,7 @@ __device__ inline v8i a_operand_lds(const uint8_t* p) {      // 24 bytes, 8-byte
 // Staged rows in LDS: the packed row's chunks for k-tiles [c0, c0 + KC), row stride KC * 112 + 8
 // bytes.  The 8-byte pad keeps the rows of one read on different banks (KC * 112 alone is a
 // multiple of the 128-byte bank cycle for every even KC).
-__host__ __device__ inline int stage_stride(int KC) { return KC * kActChunk + 8; }
+__host__ __device__ inline int stage_stride(int KC, int chunk = kActChunk) { return KC * chunk + 8; }
 
 // KTC: the number of 64-wide k-tiles when known at compile time (K = 2880 gives 45), else 0.
 // With KTC the whole K range is staged at once and the k-loop is fully unrolled, so the
@@ -59,11 +62,13 @@ __host__ __device__ inline int stage_stride(int KC) { return KC * kActChunk + 8;
 // registers), 1 reads them at the start of each k-tile.  SB: with KTC, a scheduling barrier
 // after every SB k-tiles pins the refill loads in place.
 // NB: 32-column weight tiles per wavefront (gate/up: the gate and up tiles of one SwiGLU pair).
-template <int STAGE, int P, int BM, int KTC, int ABUF, int SB = 1, int NB = (STAGE == 0 ? 2 : 1)>
+template <int STAGE, int P, int BM, int KTC, int ABUF, int SB = 1, int NB = (STAGE == 0 ? 2 : 1),
+          int AF = kActSplit6>
 __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
+  constexpr int CH = AF == kActFp4 ? kAct4Chunk : kActChunk;     // packed bytes per row and k-tile
   static_assert(STAGE == 1 || NB == 2, "a gate/up wavefront holds one gate/up tile pair");
   static_assert(P % 4 == 0, "prefetch depth must cover whole scale groups");
-  static_assert(BM <= kMTile && BM * kActChunk * P <= kAStageBytes, "a chunk of P k-tiles must fit for BM rows");
+  static_assert(BM <= kMTile && BM * CH * P <= kAStageBytes, "a chunk of P k-tiles must fit for BM rows");
   __shared__ __attribute__((aligned(16))) uint8_t sA[kAStageBytes];
   __shared__ int srow[BM];
 
@@ -89,9 +94,9 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 
   // K chunk staged at once: everything if it fits, else a multiple of the prefetch depth
   int KC = KTC > 0 ? KTC : g.KT;
-  if (KTC == 0 && nrows * stage_stride(KC) > kAStageBytes) KC = ((kAStageBytes / nrows - 8) / kActChunk) / P * P;
-  const int rs = stage_stride(KC);
-  const size_t arb = act_row_bytes(g.K);
+  if (KTC == 0 && nrows * stage_stride(KC, CH) > kAStageBytes) KC = ((kAStageBytes / nrows - 8) / CH) / P * P;
+  const int rs = stage_stride(KC, CH);
+  const size_t arb = act_row_bytes_af(AF, g.K);
 
   // this expert's weights as buffer resources; tile q starts at q*KT k-tiles (codes) / q*KG groups (scales)
   const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(g.codes + (size_t)e * g.codes_per_expert,
@@ -119,11 +124,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   // With K known at compile time all of K is staged at once.  The staging loads (16-byte pieces,
   // up to kPieces per thread) are issued before the weight ring, so waiting for them does not
   // wait for the weights (loads complete in issue order).
-  constexpr int kPieces = KTC > 0 ? (BM * KTC * (kActChunk / 16) + 255) / 256 : 1;
+  constexpr int kPieces = KTC > 0 ? (BM * KTC * (CH / 16) + 255) / 256 : 1;
   uint4 stg[kPieces];
   if constexpr (KTC > 0) {
     __syncthreads();                                    // srow visible
-    const int n16 = KTC * (kActChunk / 16);
+    const int n16 = KTC * (CH / 16);
 #pragma unroll
     for (int q = 0; q < kPieces; ++q) {
       const int w = tid + 256 * q;
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       }
   }
   if constexpr (KTC > 0) {
-    const int n16 = KTC * (kActChunk / 16);
+    const int n16 = KTC * (CH / 16);
 #pragma unroll
     for (int q = 0; q < kPieces; ++q) {
       const int w = tid + 256 * q;
@@ -170,10 +175,10 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     if constexpr (KTC == 0) {
       __syncthreads();                                  // previous chunk consumed; srow visible
       // stage rows [0, nrows) x k-tiles [c0, c0 + kcn): contiguous chunks, 8-byte words
-      const int n8 = kcn * (kActChunk / 8);
+      const int n8 = kcn * (CH / 8);
       for (int w = tid; w < nrows * n8; w += 256) {
         const int r = w / n8, o = w - r * n8;
-        const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + (size_t)c0 * kActChunk + (size_t)o * 8;
+        const uint8_t* src = g.a_packed + (size_t)srow[r] * arb + (size_t)c0 * CH + (size_t)o * 8;
         *reinterpret_cast<uint2*>(sA + r * rs + o * 8) = *reinterpret_cast<const uint2*>(src);
       }
     }
@@ -183,11 +188,21 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       const int kend = c0 + kcn;
       // A operands of k-tile kt from LDS; rows past nrows read stale bytes and are masked to zero
       auto lds_a = [&](const int kt, v8i& hi, v8i& lo, uint32_t& sh, uint32_t& sl) {
-        const uint8_t* chunk = arow + (kt - c0) * kActChunk;
-        hi = a_operand_lds(chunk + half * 24);
-        lo = a_operand_lds(chunk + 48 + half * 24);
-        sh = chunk[96 + half];
-        sl = chunk[98 + half];
+        const uint8_t* chunk = arow + (kt - c0) * CH;
+        if constexpr (AF == kActFp4) {
+          // the lane's block: 16 bytes of E2M1 codes and its scale byte (lo is unused)
+          const uint2* q = reinterpret_cast<const uint2*>(chunk + half * 16);
+          const uint2 a = q[0], b = q[1];
+          hi = v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, 0, 0, 0, 0};
+          lo = hi;
+          sh = chunk[32 + half];
+          sl = sh;
+        } else {
+          hi = a_operand_lds(chunk + half * 24);
+          lo = a_operand_lds(chunk + 48 + half * 24);
+          sh = chunk[96 + half];
+          sl = chunk[98 + half];
+        }
         const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
         hi = valid ? hi : z;
         lo = valid ? lo : z;
@@ -210,8 +225,12 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const v8i bv = b_operand(bq[j][nb]);
-          acc[nb] = mma_sel(j & 3, ah[cur], bv, acc[nb], sh[cur], sbq[j >> 2][nb]);
-          acc[nb] = mma_sel(j & 3, al[cur], bv, acc[nb], sl[cur], sbq[j >> 2][nb]);
+          if constexpr (AF == kActFp4) {
+            acc[nb] = mma4_sel(j & 3, ah[cur], bv, acc[nb], sh[cur], sbq[j >> 2][nb]);
+          } else {
+            acc[nb] = mma_sel(j & 3, ah[cur], bv, acc[nb], sh[cur], sbq[j >> 2][nb]);
+            acc[nb] = mma_sel(j & 3, al[cur], bv, acc[nb], sl[cur], sbq[j >> 2][nb]);
+          }
         }
         const int kn = min(kt + P, kend - 1);
 #pragma unroll
@@ -250,7 +269,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     static_assert(4 * BM * kEpStride * 4 <= kAStageBytes, "transpose fits the staging buffer");
     float* ep = reinterpret_cast<float*>(sA) + wave * BM * kEpStride;
     const int I = g.out_K;
-    const size_t orb = act_row_bytes(I);
+    const size_t orb = act_row_bytes_af(AF, I);
     uint8_t* out = reinterpret_cast<uint8_t*>(g.out);
     const int c = lane & 31;
     // register r holds rows 8(r/4) + 4(l/32) + r%4; tiles of BM rows only fill r < BM/2
@@ -267,7 +286,8 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
         const float4 f = *reinterpret_cast<const float4*>(ep + lane * kEpStride + 4 * q);
         v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
       }
-      store_fp6_block(out + (size_t)(p0 + lane) * orb, u, split_fp6x32(v));
+      if constexpr (AF == kActFp4) store_fp4_block(out + (size_t)(p0 + lane) * orb, u, quant_fp4x32(v));
+      else store_fp6_block(out + (size_t)(p0 + lane) * orb, u, split_fp6x32(v));
     }
   } else {
     // down epilogue: scale row p by its gate weight topk_w[perm[p]], store fp16
@@ -301,7 +321,7 @@ constexpr int kDownP = MOE_DECODE_DOWN_P;     // and k-tiles in flight
 
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
-                       void* out, hipStream_t s) {
+                       void* out, hipStream_t s, int af) {
   if (T == 0) return hipSuccess;
   GemmArgs g;
   g.T = T; g.k = k; g.E = E; g.limit = limit;
@@ -318,11 +338,21 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   const long long n_assign = (long long)T * k;
   // batches with many rows per expert (128-row tiles) go to the prefill kernel
   if (tile_rows(n_assign, E) != 8)
-    return launch_gemm_prefill(stage, T, D, I, E, k, limit, a_packed, tiles, codes, scales, topk_w, out, s);
+    return launch_gemm_prefill(stage, T, D, I, E, k, limit, a_packed, tiles, codes, scales, topk_w, out, s, af);
   // decode-sized batches (8-row tiles whose activations fit LDS whole)
   const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));
   // the model's K = 2880 (45 k-tiles): fully unrolled k-loop
   const bool k45 = g.KT == 45 && 8 * stage_stride(45) <= kAStageBytes;   // 40384 <= 40960
+  if (af == kActFp4) {
+    if (stage == 0) {
+      if (k45) expert_gemm_kernel<0, kGateUpP, 8, 45, 1, 1, 2, kActFp4><<<grid, dim3(256), 0, s>>>(g);
+      else expert_gemm_kernel<0, 8, 8, 0, 1, 1, 2, kActFp4><<<grid, dim3(256), 0, s>>>(g);
+    } else {
+      if (k45) expert_gemm_kernel<1, kDownP, 8, 45, 2, 1, kDownNB, kActFp4><<<grid, dim3(256), 0, s>>>(g);
+      else expert_gemm_kernel<1, kDownP, 8, 0, 1, 1, kDownNB, kActFp4><<<grid, dim3(256), 0, s>>>(g);
+    }
+    return hipGetLastError();
+  }
   if (stage == 0) {
     if (k45) expert_gemm_kernel<0, kGateUpP, 8, 45, 1><<<grid, dim3(256), 0, s>>>(g);
     else expert_gemm_kernel<0, 8, 8, 0, 1><<<grid, dim3(256), 0, s>>>(g);

@@ -27,6 +27,10 @@
 //  - Gate/up epilogue: SwiGLU in registers, then a transpose of the h tile
 //    through LDS. Each lane then holds one 32-value block of an h row and
 //    splits it into hi/lo FP6 with the packed conversion instructions.
+//  - The activation-quantized variant (AF = kActFp4) stages 48-byte MXFP4
+//    chunks and issues one FP4 x FP4 instruction per weight tile in the plain
+//    operand layout (lanes 0-31 block 0, lanes 32-63 block 1, weights as
+//    loaded); its gate/up epilogue quantizes h to MXFP4.
 #include "mfma_ops.h"
 
 namespace moe {
@@ -47,9 +51,6 @@ struct PrefillArgs {
 constexpr int kPWaveTiles = 4;                         // 32-column weight tiles per wavefront
 constexpr int kPGroupTiles = 4 * kPWaveTiles;          // per workgroup
 constexpr int kPSlots = 4;                             // staged k-tiles in the LDS ring
-constexpr int kPPieces = kActChunk / 16;               // 16-byte pieces per row chunk (7)
-constexpr int kPBlockBytes = 32 * kActChunk;           // one 32-row block of a staged k-tile
-constexpr int kPStagePieces = kPrefillRows * kPPieces; // 896 pieces per staged k-tile
 constexpr int kPSlotBytes = 1024 * 16;                 // 896 pieces + 128 dummy (4 unconditional per thread)
 constexpr int kPStageAhead = 2;                        // k-tile kt + 2 is written to LDS during k-tile kt
 constexpr int kPEpiStride = 68;                        // floats per row of the transposed h block
@@ -82,9 +83,14 @@ __device__ __forceinline__ void split_halves(const uint32_t x, uint32_t& s0, uin
 
 // NA: activation k-tiles in flight in registers (k-tile t is fetched NA k-tiles before it is
 // written to LDS); P: weight k-tiles in flight per wavefront.  Both divide 8.
-template <int STAGE, int KTC, int NA, int P>
+template <int STAGE, int KTC, int NA, int P, int AF = kActSplit6>
 __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g) {
   static_assert(8 % NA == 0 && 8 % P == 0 && P >= 4, "ring depths divide the 8-step unroll");
+  constexpr bool F4 = AF == kActFp4;
+  constexpr int CH = F4 ? kAct4Chunk : kActChunk;        // packed bytes per row and k-tile
+  constexpr int NPC = F4 ? 2 : 4;                         // staged 16-byte pieces per thread per k-tile
+  constexpr int kStagePieces = kPrefillRows * (CH / 16);  // 384 or 896 (the rest re-read a real one)
+  constexpr int kBlockBytes = 32 * CH;                    // one 32-row block of a staged k-tile
   __shared__ __attribute__((aligned(16))) uint8_t sA[kPSlots * kPSlotBytes];
   __shared__ int srow[kPrefillRows];
   __shared__ float sgate[kPrefillRows];
@@ -121,22 +127,22 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
 
   // ---- activation staging: thread tid moves pieces tid + 256 i (i < 4) of every k-tile ----------
   const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(g.a_packed, g.a_bytes);
-  uint32_t aoff[4];
+  uint32_t aoff[NPC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = min(tid + 256 * i, kPStagePieces - 1); // the dummy pieces re-read a real one
-    const int row = q / kPPieces;
+  for (int i = 0; i < NPC; ++i) {
+    const int q = min(tid + 256 * i, kStagePieces - 1);  // the dummy pieces re-read a real one
+    const int row = q / (CH / 16);
     // rows past the tile repeat its last row
-    aoff[i] = (uint32_t)srow[min(row, nrows - 1)] * g.arb + (uint32_t)(q - row * kPPieces) * 16u;
+    aoff[i] = (uint32_t)srow[min(row, nrows - 1)] * g.arb + (uint32_t)(q - row * (CH / 16)) * 16u;
   }
-  auto load_a = [&](const int kt, v4i (&buf)[4]) __attribute__((always_inline)) {
+  auto load_a = [&](const int kt, v4i (&buf)[NPC]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, aoff[i], kt * kActChunk, 0);
+    for (int i = 0; i < NPC; ++i) buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, aoff[i], kt * CH, 0);
   };
-  auto store_a = [&](const int s, const v4i (&buf)[4]) __attribute__((always_inline)) {
+  auto store_a = [&](const int s, const v4i (&buf)[NPC]) __attribute__((always_inline)) {
     uint8_t* dst = sA + s * kPSlotBytes + tid * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i*>(dst + i * 4096) = buf[i];
+    for (int i = 0; i < NPC; ++i) *reinterpret_cast<v4i*>(dst + i * 4096) = buf[i];
   };
 
   // ---- weights: this wavefront's four 32-column tiles of expert e -----------------------------
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   // ---- prologue: k-tiles 0, 1 staged; the next NA in registers; weight ring filled -------------
   // Every load index is clamped to the last k-tile, so no load or store depends on K: a k-tile
   // past the end is staged into a slot nobody reads.  Register set t % NA holds k-tile t.
-  v4i abuf[NA][4];
+  v4i abuf[NA][NPC];
   load_a(0, abuf[0 % NA]);
   store_a(0, abuf[0 % NA]);
   load_a(min(1, KT - 1), abuf[1 % NA]);
@@ -200,8 +206,14 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     uint32_t s;
   };
   auto read_ops = [&](const int kt, const int rb) __attribute__((always_inline)) {
-    const uint8_t* row = sA + (kt & 3) * kPSlotBytes + rb * kPBlockBytes + r32 * kActChunk;
+    const uint8_t* row = sA + (kt & 3) * kPSlotBytes + rb * kBlockBytes + r32 * CH;
     AOps o;
+    if constexpr (F4) {                                   // the lane's block: 16 bytes and a scale byte
+      const v4i q0 = *reinterpret_cast<const v4i*>(row + 16 * h);
+      o.q = v16i{q0.x, q0.y, q0.z, q0.w, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      o.s = row[32 + h];
+      return o;
+    }
     const v4i q0 = *reinterpret_cast<const v4i*>(row + 48 * h);
     const v4i q1 = *reinterpret_cast<const v4i*>(row + 48 * h + 16);
     const v4i q2 = *reinterpret_cast<const v4i*>(row + 48 * h + 32);
@@ -219,10 +231,12 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   // A scheduling barrier between phases keeps each phase's work next to its matrix instructions.
   AOps nxt = read_ops(0, 0);
   v4i bw[kPWaveTiles][2];
+  if constexpr (!F4) {
 #pragma unroll
-  for (int cb = 0; cb < kPWaveTiles; ++cb) {
-    split_halves(bq[0][cb], bw[cb][0], bw[cb][1]);
-    split_halves(sq[0][cb], sqd[cb][0], sqd[cb][1]);
+    for (int cb = 0; cb < kPWaveTiles; ++cb) {
+      split_halves(bq[0][cb], bw[cb][0], bw[cb][1]);
+      split_halves(sq[0][cb], sqd[cb][0], sqd[cb][1]);
+    }
   }
   auto step = [&](const int kt, const int j) __attribute__((always_inline)) {
     constexpr int D = kPStageAhead;
@@ -232,16 +246,23 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     for (int rb = 0; rb < 4; ++rb) {
       const AOps cur = nxt;
       nxt = rb < 3 ? read_ops(kt, rb + 1) : read_ops(min(kt + 1, KT - 1), 0);
-      const v8i a0 = __builtin_shufflevector(cur.q, cur.q, 0, 1, 2, 3, 4, 5, 6, 7);
-      const v8i a1 = __builtin_shufflevector(cur.q, cur.q, 6, 7, 8, 9, 10, 11, 12, 13);
+      if constexpr (F4) {
+        const v8i a = __builtin_shufflevector(cur.q, cur.q, 0, 1, 2, 3, 12, 13, 14, 15);
 #pragma unroll
-      for (int cb = 0; cb < kPWaveTiles; ++cb) {
-        acc[rb][cb] = mma_sel_a<0>(j & 3, a0, b_operand(bw[cb][0]), acc[rb][cb], cur.s, sqd[cb][0]);
-        acc[rb][cb] = mma_sel_a<1>(j & 3, a1, b_operand(bw[cb][1]), acc[rb][cb], cur.s, sqd[cb][1]);
+        for (int cb = 0; cb < kPWaveTiles; ++cb)
+          acc[rb][cb] = mma4_sel(j & 3, a, b_operand(bq[j % P][cb]), acc[rb][cb], cur.s, sq[(j >> 2) & 1][cb]);
+      } else {
+        const v8i a0 = __builtin_shufflevector(cur.q, cur.q, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v8i a1 = __builtin_shufflevector(cur.q, cur.q, 6, 7, 8, 9, 10, 11, 12, 13);
+#pragma unroll
+        for (int cb = 0; cb < kPWaveTiles; ++cb) {
+          acc[rb][cb] = mma_sel_a<0>(j & 3, a0, b_operand(bw[cb][0]), acc[rb][cb], cur.s, sqd[cb][0]);
+          acc[rb][cb] = mma_sel_a<1>(j & 3, a1, b_operand(bw[cb][1]), acc[rb][cb], cur.s, sqd[cb][1]);
+        }
       }
       if (rb == 0) store_a((kt + D) & 3, abuf[(j + D) % NA]);                  // publish kt + D
       if (rb == 1) load_a(min(kt + D + NA, KT - 1), abuf[(j + D) % NA]);        // fetch kt + D + NA
-      if (rb == 2) {
+      if (!F4 && rb == 2) {
 #pragma unroll
         for (int cb = 0; cb < kPWaveTiles; ++cb) {
           split_halves(bq[(j + 1) % P][cb], bwn[cb][0], bwn[cb][1]);
@@ -269,7 +290,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int cb = 0; cb < kPWaveTiles; ++cb) {
+    for (int cb = 0; cb < (F4 ? 0 : kPWaveTiles); ++cb) {
       bw[cb][0] = bwn[cb][0];
       bw[cb][1] = bwn[cb][1];
       if ((j & 3) == 3) {
@@ -294,7 +315,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     // ---- SwiGLU, transpose through LDS, hi/lo FP6 split of each 32-value block of h ------------
     float* ep = reinterpret_cast<float*>(sA) + wave * 32 * kPEpiStride;
     const int I = g.out_K;
-    const uint32_t orb = (uint32_t)act_row_bytes(I);
+    const uint32_t orb = (uint32_t)act_row_bytes_af(AF, I);
     uint8_t* out = reinterpret_cast<uint8_t*>(g.out);
     const int uu = lane >> 5;                            // after the transpose: block of this lane
     const int ublk = cgrp * (kPGroupTiles / 2) + wave * (kPWaveTiles / 2) + uu;
@@ -317,9 +338,14 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
         v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
       }
       __builtin_amdgcn_wave_barrier();
-      const Fp6Split sp = split_fp6x32(v);
       const int m = rb * 32 + r32;
-      if (m < nrows && 2 * ublk < g.nt) store_fp6_block(out + (size_t)(p0 + m) * orb, ublk, sp);
+      if constexpr (F4) {
+        const Fp4Block q4 = quant_fp4x32(v);
+        if (m < nrows && 2 * ublk < g.nt) store_fp4_block(out + (size_t)(p0 + m) * orb, ublk, q4);
+      } else {
+        const Fp6Split sp = split_fp6x32(v);
+        if (m < nrows && 2 * ublk < g.nt) store_fp6_block(out + (size_t)(p0 + m) * orb, ublk, sp);
+      }
     }
   } else {
     // ---- down: scale row p by its gate weight, fp16, transpose through LDS, 16-byte row stores --
@@ -366,7 +392,7 @@ constexpr int kPP = MOE_PREFILL_P;
 
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
-                               const uint8_t* scales, const float* topk_w, void* out, hipStream_t s) {
+                               const uint8_t* scales, const float* topk_w, void* out, hipStream_t s, int af) {
   PrefillArgs g;
   const int K = stage == 0 ? D : I;
   const int N = stage == 0 ? 2 * I : D;
@@ -378,7 +404,7 @@ hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, flo
   g.out_K = stage == 0 ? I : D;
   g.limit = limit;
   g.a_packed = a_packed;
-  g.arb = (uint32_t)act_row_bytes(K);
+  g.arb = (uint32_t)act_row_bytes_af(af, K);
   g.a_bytes = (uint32_t)((size_t)(stage == 0 ? T : (long long)T * k) * g.arb);
   g.tiles = tiles;
   g.topk_w = topk_w;
@@ -395,6 +421,16 @@ hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, flo
   else expert_gemm_prefill_kernel<1, 0, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
   return hipGetLastError();
 #endif
+  if (af == kActFp4) {
+    if (stage == 0) {
+      if (g.KT == 45) expert_gemm_prefill_kernel<0, 45, kPNA, kPP, kActFp4><<<grid, dim3(256), 0, s>>>(g);
+      else expert_gemm_prefill_kernel<0, 0, kPNA, kPP, kActFp4><<<grid, dim3(256), 0, s>>>(g);
+    } else {
+      if (g.KT == 45) expert_gemm_prefill_kernel<1, 45, kPNA, kPP, kActFp4><<<grid, dim3(256), 0, s>>>(g);
+      else expert_gemm_prefill_kernel<1, 0, kPNA, kPP, kActFp4><<<grid, dim3(256), 0, s>>>(g);
+    }
+    return hipGetLastError();
+  }
   if (stage == 0) {
     if (g.KT == 45) expert_gemm_prefill_kernel<0, 45, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
     else expert_gemm_prefill_kernel<0, 0, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);

@@ -51,6 +51,21 @@ __device__ inline v16f mma_sel_a(int ob, v8i a, v8i b, v16f c, uint32_t sa, uint
   }
 }
 
+// scaled MFMA with both operands FP4 E2M1 (A scale byte 0 of sa, B scale byte OB of sb)
+template <int OB>
+__device__ inline v16f mma_fp4_fp4(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, OB, sb);
+}
+
+__device__ inline v16f mma4_sel(int ob, v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  switch (ob) {
+    case 0: return mma_fp4_fp4<0>(a, b, c, sa, sb);
+    case 1: return mma_fp4_fp4<1>(a, b, c, sa, sb);
+    case 2: return mma_fp4_fp4<2>(a, b, c, sa, sb);
+    default: return mma_fp4_fp4<3>(a, b, c, sa, sb);
+  }
+}
+
 // ob is a compile-time constant after unrolling, so the switch folds away
 __device__ inline v16f mma_sel(int ob, v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
   switch (ob) {
@@ -135,10 +150,65 @@ __device__ __forceinline__ void store_fp6_block(uint8_t* row, int b, const Fp6Sp
   chunk[98 + half] = (uint8_t)sp.s_lo;
 }
 
-// Split block `blk` (= row * K/32 + b) of bf16 rows [rows][K] (16-byte aligned) in one lane:
-// four 16-byte loads, the hi/lo split, the stores.  Lanes past the last block do nothing.
+// ---------------------------------------------------------------------------
+// MXFP4 quantization of one 32-value block held by one lane (OCP MX v1.0 conversion): shared
+// exponent E = floor(log2 amax) - 2 (the E2M1 emax), clamped to the E8M0 range, byte E + 127;
+// each element v / 2^E rounded to the nearest E2M1 value (ties to the even code), magnitudes
+// past 6 saturate; an all-zero block gets scale byte 0 and zero codes.  Codes: element i in
+// nibble i of the 16 bytes (low nibble first), bit 3 the sign.
+// ---------------------------------------------------------------------------
+struct Fp4Block {
+  uint4 codes;
+  uint32_t scale;
+};
+
+__device__ __forceinline__ uint32_t e2m1_code(float v, float inv) {
+  const float q = fabsf(v) * inv;
+  float c;
+  if (q < 2.0f) c = rintf(q * 2.0f);                         // 0, 0.5, ..., 2 -> codes 0..4
+  else if (q < 4.0f) c = 4.0f + rintf(q - 2.0f);              // 2, 3, 4 -> codes 4..6
+  else c = 6.0f + rintf(fminf(q, 6.0f) * 0.5f - 2.0f);         // 4, 6 -> codes 6, 7
+  return (uint32_t)c | (v < 0.0f ? 8u : 0u);
+}
+
+__device__ __forceinline__ Fp4Block quant_fp4x32(const float (&v)[32]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  Fp4Block r;
+  if (amax == 0.0f) {
+    r.codes = make_uint4(0, 0, 0, 0);
+    r.scale = 0;
+    return r;
+  }
+  int E = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 2;
+  E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  r.scale = (uint32_t)(E + 127);
+  const float inv = ldexpf(1.0f, -E);
+  uint32_t w[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x |= e2m1_code(v[8 * d + j], inv) << (4 * j);
+    w[d] = x;
+  }
+  r.codes = make_uint4(w[0], w[1], w[2], w[3]);
+  return r;
+}
+
+// Store quantized block b of an MXFP4-packed activation row (format in moe_internal.h).
+__device__ __forceinline__ void store_fp4_block(uint8_t* row, int b, const Fp4Block& q) {
+  uint8_t* chunk = row + (size_t)(b >> 1) * kAct4Chunk;
+  *reinterpret_cast<uint4*>(chunk + 16 * (b & 1)) = q.codes;
+  chunk[32 + (b & 1)] = (uint8_t)q.scale;
+}
+
+// Pack block `blk` (= row * K/32 + b) of bf16 rows [rows][K] (16-byte aligned) in one lane:
+// four 16-byte loads, then the hi/lo FP6 split (af = kActSplit6) or the MXFP4 quantization
+// (af = kActFp4), the stores.  Lanes past the last block do nothing.
 __device__ __forceinline__ void pack_block_lane(const uint16_t* __restrict__ a, int K, long long nblocks,
-                                                long long blk, uint8_t* __restrict__ packed) {
+                                                long long blk, uint8_t* __restrict__ packed, int af = kActSplit6) {
   if (blk >= nblocks) return;
   const int nb = K / kBlock;
   const long long row = blk / nb;
@@ -155,7 +225,8 @@ __device__ __forceinline__ void pack_block_lane(const uint16_t* __restrict__ a, 
       v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
   }
-  store_fp6_block(packed + (size_t)row * act_row_bytes(K), b, split_fp6x32(v));
+  if (af == kActFp4) store_fp4_block(packed + (size_t)row * act4_row_bytes(K), b, quant_fp4x32(v));
+  else store_fp6_block(packed + (size_t)row * act_row_bytes(K), b, split_fp6x32(v));
 }
 
 }  // namespace moe

@@ -31,6 +31,22 @@ __host__ __device__ inline int act_ktiles(int K) { return K / kKTile; }
 __host__ __device__ inline size_t act_row_bytes(int K) { return (size_t)act_ktiles(K) * kActChunk; }
 
 // ---------------------------------------------------------------------------
+// Packed MXFP4 activation rows (the activation-quantized variant): per 64-wide
+// k-tile kt a 48-byte chunk:
+//   [0,16) E2M1 codes of block 2kt (element i in nibble i, low nibble first)
+//   [16,32) codes of block 2kt+1   [32] [33] E8M0 scales of the two blocks   [34,48) unused
+// ---------------------------------------------------------------------------
+constexpr int kAct4Chunk = 48;
+__host__ __device__ inline size_t act4_row_bytes(int K) { return (size_t)act_ktiles(K) * kAct4Chunk; }
+// activation formats of the expert GEMMs
+constexpr int kActSplit6 = 0;      // bf16 as hi + lo FP6 terms (the default)
+constexpr int kActFp4 = 1;         // MXFP4 activations
+__host__ __device__ inline int act_chunk(int af) { return af == kActFp4 ? kAct4Chunk : kActChunk; }
+__host__ __device__ inline size_t act_row_bytes_af(int af, int K) {
+  return af == kActFp4 ? act4_row_bytes(K) : act_row_bytes(K);
+}
+
+// ---------------------------------------------------------------------------
 // Prepacked weights: for each expert, for each output tile q of 32 rows, for
 // each k-tile kt of 64: 64 lanes x 16 B of codes (lane l = row l%32 of the
 // tile, K block l/32 of the k-tile).  Scales: for each (q, group of 4 k-tiles)
@@ -113,17 +129,19 @@ hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const flo
 // selection and the grouping into one workgroup.
 hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
                               int32_t* idx, float* w, void* ws, uint8_t* xpack, int32_t* counts,
-                              int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s);
+                              int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s,
+                              int af = kActSplit6);
 size_t route_workspace_bytes(int T, int D, int E);
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s);
-hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipStream_t s);
+hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipStream_t s, int af = kActSplit6);
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
-                       void* out, hipStream_t s);
+                       void* out, hipStream_t s, int af = kActSplit6);
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
-                               const uint8_t* scales, const float* topk_w, void* out, hipStream_t s);
+                               const uint8_t* scales, const float* topk_w, void* out, hipStream_t s,
+                               int af = kActSplit6);
 hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, const uint16_t* residual,
                           void* y, int y_bf16, hipStream_t s);
 hipError_t launch_rmsnorm(int T, int D, const uint16_t* x, const float* gamma, float eps, uint16_t* xn,

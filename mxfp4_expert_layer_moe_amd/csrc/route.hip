@@ -217,12 +217,12 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, i
                                                                          float* __restrict__ xsq,
                                                                          float* __restrict__ wsq,
                                                                          int logit_wgs,
-                                                                         uint8_t* __restrict__ xpack) {
+                                                                         uint8_t* __restrict__ xpack, int af) {
   __shared__ double red[8][32][33];          // K-partials: waves 0..7, then 8..15 added in place
   __shared__ float rsq[kLogitWaves][2][32];  // partial ||x_t||^2 (0) and ||w_e||^2 (1)
   if ((int)blockIdx.x >= logit_wgs) {        // activation split, one block per lane (no barriers)
     const long long blk = (long long)(blockIdx.x - logit_wgs) * (kLogitWaves * 64) + threadIdx.x;
-    pack_block_lane(x, D, (long long)T * (D / kBlock), blk, xpack);
+    pack_block_lane(x, D, (long long)T * (D / kBlock), blk, xpack, af);
     return;
   }
   const int tid = threadIdx.x;
@@ -620,6 +620,7 @@ __global__ __launch_bounds__(1024) void route_select_small_kernel(
 }
 
 static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
+                                int af,
                                 hipStream_t s, double** logit, float** xsq, float** wsq, int* KW) {
   *KW = route_kw(T, E);
   const RouteWs L = route_ws_layout(T, E);
@@ -631,7 +632,7 @@ static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const fl
   const long long pack_blocks = xpack ? (long long)T * (D / kBlock) : 0;
   const long long pack_wgs = (pack_blocks + kLogitWaves * 64 - 1) / (kLogitWaves * 64);
   route_logits_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kLogitWaves * 64), 0, s>>>(
-      T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack);
+      T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
   return hipGetLastError();
 }
 
@@ -641,7 +642,7 @@ hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const flo
   double* logit;
   float *xsq, *wsq;
   int KW;
-  hipError_t err = launch_logits(T, D, E, x, wr, ws, nullptr, s, &logit, &xsq, &wsq, &KW);
+  hipError_t err = launch_logits(T, D, E, x, wr, ws, nullptr, kActSplit6, s, &logit, &xsq, &wsq, &KW);
   if (err != hipSuccess) return err;
   if (route_small(T, E)) {
     route_select_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(T, D, E, k, x, wr, br, logit, xsq, wsq, idx, w,
@@ -656,12 +657,13 @@ hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const flo
 
 hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
                               int32_t* idx, float* w, void* ws, uint8_t* xpack, int32_t* counts,
-                              int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s) {
+                              int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s,
+                              int af) {
   if (T == 0) return hipSuccess;
   double* logit;
   float *xsq, *wsq;
   int KW;
-  hipError_t err = launch_logits(T, D, E, x, wr, ws, xpack, s, &logit, &xsq, &wsq, &KW);
+  hipError_t err = launch_logits(T, D, E, x, wr, ws, xpack, af, s, &logit, &xsq, &wsq, &KW);
   if (err != hipSuccess) return err;
   if (route_small(T, E)) {
     const long long n = (long long)T * k;

@@ -9,10 +9,11 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_FP32, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, dims, moe_act_pack_bytes,
+from . import (MOE_BF16, MOE_FP32, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, dims, moe_act4_pack_bytes, moe_act_pack_bytes,
                moe_block_forward, moe_block_workspace_bytes, moe_combine, moe_combine_residual,
-               moe_expert_gemm_mxfp4, moe_forward, moe_mxfp4_prepack, moe_pack_act, moe_permute, moe_rmsnorm,
-               moe_route, moe_route_workspace_bytes, moe_tile_table_bytes, moe_weights, moe_workspace_bytes)
+               moe_expert_gemm_mxfp4, moe_expert_gemm_mxfp4_act4, moe_forward, moe_forward_act4, moe_mxfp4_prepack,
+               moe_pack_act, moe_pack_act4, moe_permute, moe_rmsnorm, moe_route, moe_route_workspace_bytes,
+               moe_tile_table_bytes, moe_weights, moe_workspace_bytes, moe_workspace_bytes_act4)
 
 
 def _u8(a: np.ndarray, device) -> torch.Tensor:
@@ -82,6 +83,8 @@ class DeviceLayer:
         self.eps = float(getattr(inp, "norm_eps", 1e-5))
         self.xn = torch.empty((T, D), dtype=torch.bfloat16, device=device)
         self.block_ws = None
+        # the activation-quantized variant (MXFP4 activations), allocated on first use
+        self.x_packed4 = self.h_packed4 = self.ws4 = None
 
     # ---- step by step (the C entry points in order) ---------------------------
     def route(self, logits=True, stream=None, x=None):
@@ -119,6 +122,35 @@ class DeviceLayer:
         self.gate_up(stream=stream)
         self.down(stream=stream)
         self.combine(bf16, stream)
+
+    # ---- the activation-quantized variant (MXFP4 activations) -----------------
+    def _act4_buffers(self):
+        if self.x_packed4 is None:
+            T, k, D, I = self.T, self.k, self.D, self.I
+            u8 = dict(dtype=torch.uint8, device=self.device)
+            self.x_packed4 = torch.empty(max(moe_act4_pack_bytes(D, T), 16), **u8)
+            self.h_packed4 = torch.empty(max(moe_act4_pack_bytes(I, T * k), 16), **u8)
+            self.ws4 = torch.empty(max(moe_workspace_bytes_act4(self.dims, T), 256), **u8)
+
+    def steps_act4(self, bf16=False, stream=None):
+        self._act4_buffers()
+        w = self.weights
+        self.route(stream=stream)
+        self.permute(stream)
+        moe_pack_act4(self.D, self.T, self.x, self.x_packed4, stream)
+        moe_expert_gemm_mxfp4_act4(self.dims, self.T, MOE_STAGE_GATE_UP, self.x_packed4, self.tiles, w.gu_codes,
+                                   w.gu_scales, None, self.h_packed4, stream)
+        moe_expert_gemm_mxfp4_act4(self.dims, self.T, MOE_STAGE_DOWN, self.h_packed4, self.tiles, w.dn_codes,
+                                   w.dn_scales, self.topk_w, self.y_perm, stream)
+        self.combine(bf16, stream)
+
+    def forward_act4(self, bf16=False, weights: DeviceWeights | None = None, stream=None):
+        self._act4_buffers()
+        w = weights or self.weights
+        y, dt = (self.y16, MOE_BF16) if bf16 else (self.y32, MOE_FP32)
+        moe_forward_act4(self.dims, self.T, self.x, self.w_router, self.b_router, w.struct(), y, dt, self.ws4, None,
+                         stream)
+        return y
 
     # ---- the pre-norm block: y = x + MoE(RMSNorm(x)) --------------------------
     def rmsnorm(self, stream=None):

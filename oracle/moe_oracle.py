@@ -166,17 +166,47 @@ def swiglu(g: np.ndarray, u: np.ndarray, limit: float) -> np.ndarray:
     return silu(g) * u
 
 
-def expert_ffn(xr: np.ndarray, gu_codes, gu_scales, dn_codes, dn_scales, limit: float):
-    """One expert on rows xr [M][D]: returns (h [M][I] bf16-rounded f64, z [M][D] f64)."""
+def expert_ffn(xr: np.ndarray, gu_codes, gu_scales, dn_codes, dn_scales, limit: float, act4: bool = False):
+    """One expert on rows xr [M][D]: returns (h [M][I] bf16-rounded f64, z [M][D] f64).
+
+    act4: the activation-quantized variant; the rows entering each projection (x, then h) are
+    quantized to MXFP4 first (mxfp4_quantize_rows), and the returned h is that quantized h."""
     w_gu = mxfp4_decode(gu_codes, gu_scales)        # [2I][D]
     I = w_gu.shape[0] // 2
-    g = xr @ w_gu[:I].T
-    u = xr @ w_gu[I:].T
+    xa = mxfp4_quantize_rows(xr) if act4 else xr
+    g = xa @ w_gu[:I].T
+    u = xa @ w_gu[I:].T
     del w_gu
     h = round_to_bf16(swiglu(g, u, limit))
+    if act4:
+        h = mxfp4_quantize_rows(h)
     w_dn = mxfp4_decode(dn_codes, dn_scales)        # [D][I]
     z = h @ w_dn.T
     return h, z
+
+
+def mxfp4_quantize_rows(v: np.ndarray) -> np.ndarray:
+    """MXFP4 values of rows [R][K] (K % 32 == 0) under the OCP MX v1.0 conversion, float64.
+
+    Per 32-value block: shared exponent E = floor(log2 amax) - 2 (2 is the largest E2M1
+    exponent), clamped to [-127, 127]; each element v / 2^E goes to the nearest E2M1 magnitude,
+    ties to the one with the even code, magnitudes past 6 to 6; an all-zero block stays zero."""
+    v = np.asarray(v, dtype=np.float64)
+    R, K = v.shape
+    b = v.reshape(R, K // 32, 32)
+    amax = np.abs(b).max(axis=-1, keepdims=True)
+    _, ex = np.frexp(amax)                          # amax = m 2^ex, m in [0.5, 1): floor(log2) = ex - 1
+    E = np.clip(ex - 1 - 2, -127, 127)
+    q = np.abs(b) / np.ldexp(1.0, E)
+    d = np.abs(q[..., None] - E2M1_MAGNITUDE)      # distance to every grid value
+    best = d.min(axis=-1, keepdims=True)
+    even = np.arange(8) % 2 == 0
+    # the nearest value; of two equally near (always neighbours, one code even) the even code
+    pick = np.where(((d == best) & even).any(axis=-1), np.argmax((d == best) & even, axis=-1),
+                    np.argmax(d == best, axis=-1))
+    out = np.sign(b) * E2M1_MAGNITUDE[pick] * np.ldexp(1.0, E)
+    out[np.broadcast_to(amax == 0, b.shape)] = 0.0
+    return out.reshape(R, K)
 
 
 # ----------------------------------------------------------------------------
@@ -190,7 +220,7 @@ def combine(w: np.ndarray, z_perm: np.ndarray, inv: np.ndarray, tokens: np.ndarr
     return y
 
 
-def forward(inp, tokens=None, override_idx: dict | None = None) -> dict:
+def forward(inp, tokens=None, override_idx: dict | None = None, act4: bool = False) -> dict:
     """Evaluate the layer.
 
     inp: object with T, D, E, k, I, swiglu_limit, x_bf16, w_router, b_router,
@@ -200,6 +230,8 @@ def forward(inp, tokens=None, override_idx: dict | None = None) -> dict:
     these tokens (all tokens when None).
     override_idx: {token: k expert ids} replacing the oracle's own selection
     for those tokens (used for near-tie tokens only).
+    act4: the activation-quantized variant (MXFP4 activations into both expert
+    projections; routing on the unquantized x).
 
     Returns a dict with logits, idx, flagged, gap, w, counts, offsets, perm,
     inv, tokens, and for the evaluated tokens: h (by position p), z (by
@@ -226,7 +258,7 @@ def forward(inp, tokens=None, override_idx: dict | None = None) -> dict:
             continue
         rows = x[perm[seg] // k]
         h, z = expert_ffn(rows, inp.gu_codes[e], inp.gu_scales[e], inp.dn_codes[e],
-                          inp.dn_scales[e], inp.swiglu_limit)
+                          inp.dn_scales[e], inp.swiglu_limit, act4=act4)
         for i, p in enumerate(seg):
             h_all[int(p)] = h[i]
             z_all[int(p)] = z[i]

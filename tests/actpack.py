@@ -44,3 +44,33 @@ def decode(buf, K: int, rows: int):
 def decode_sum(buf, K: int, rows: int) -> np.ndarray:
     hi, lo = decode(buf, K, rows)
     return hi + lo
+
+
+# ---- MXFP4 activation rows (the activation-quantized entry points) -------------------------
+# Per row, K/64 chunks of 48 bytes: [0,16) E2M1 codes of block 2kt (element i in nibble i, low
+# nibble first), [16,32) codes of block 2kt+1, [32],[33] their E8M0 scale bytes.
+def e2m1_table() -> np.ndarray:
+    t = np.zeros(16)
+    for c in range(16):
+        s = -1.0 if c & 8 else 1.0
+        e, m = (c >> 1) & 3, c & 1
+        t[c] = s * (m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2.0))
+    return t
+
+
+_E2M1 = e2m1_table()
+
+
+def row4_bytes(K: int) -> int:
+    return K // 64 * 48
+
+
+def decode4(buf, K: int, rows: int) -> np.ndarray:
+    """buf: uint8 array (at least rows*row4_bytes(K)) -> float64 [rows][K]."""
+    kt = K // 64
+    a = np.asarray(buf, dtype=np.uint8)[: rows * row4_bytes(K)].reshape(rows, kt, 48)
+    codes = a[:, :, :32].reshape(rows, kt, 2, 16)
+    c = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(rows, kt, 2, 32)
+    sbyte = a[:, :, 32:34].astype(np.int64)
+    val = _E2M1[c] * np.ldexp(1.0, sbyte - 127)[..., None]
+    return val.reshape(rows, K)

@@ -58,8 +58,31 @@ def decode_matrix(codes, scales):
     return out
 
 
-def expert_dense(xrow, Wg, Wu, Wd, limit):
-    """One SwiGLU expert on one token: returns (h list, z list)."""
+def mxfp4_quantize(row):
+    """OCP MX v1.0 conversion of a row to MXFP4 values, block by block of 32: the shared exponent
+    is floor(log2 amax) minus E2M1's largest exponent (2); each element goes to the E2M1 value
+    nearest to v / 2^E (searched over all sixteen codes), an exact tie to the even code, so past
+    6 it stays at 6; an all-zero block stays zero."""
+    out = []
+    for b0 in range(0, len(row), 32):
+        blk = row[b0:b0 + 32]
+        amax = max(abs(v) for v in blk)
+        if amax == 0.0:
+            out.extend([0.0] * len(blk))
+            continue
+        E = max(-127, min(127, math.floor(math.log2(amax)) - 2))
+        for v in blk:
+            q = v / 2.0 ** E
+            best = min(range(16), key=lambda c: (abs(e2m1_value(c) - q), c & 1, c))
+            out.append(e2m1_value(best) * 2.0 ** E)
+    return out
+
+
+def expert_dense(xrow, Wg, Wu, Wd, limit, act4=False):
+    """One SwiGLU expert on one token: returns (h list, z list).  act4: the rows entering each
+    projection are quantized to MXFP4 first."""
+    if act4:
+        xrow = mxfp4_quantize(xrow)
     h = []
     for i in range(len(Wg)):
         g = sum(a * b for a, b in zip(xrow, Wg[i]))
@@ -67,11 +90,13 @@ def expert_dense(xrow, Wg, Wu, Wd, limit):
         g = min(max(g, -limit), limit)
         u = min(max(u, -limit), limit)
         h.append(bf16_round(g / (1.0 + math.exp(-g)) * u))
+    if act4:
+        h = mxfp4_quantize(h)
     z = [sum(a * b for a, b in zip(h, Wd[n])) for n in range(len(Wd))]
     return h, z
 
 
-def brute_layer(inp):
+def brute_layer(inp, act4=False):
     """Dense evaluation of the layer; returns dict(logits, idx, w, y) as Python lists."""
     T, D, E, k, I = inp.T, inp.D, inp.E, inp.k, inp.I
     x = [[bf16_bits_value(int(b)) for b in row] for row in inp.x_bf16]
@@ -93,7 +118,7 @@ def brute_layer(inp):
         gate = [ex[e] / s if e in ex else 0.0 for e in range(E)]
         y = [0.0] * D
         for e in range(E):                       # every expert, ascending id
-            _, z = expert_dense(x[t], *experts[e], inp.swiglu_limit)
+            _, z = expert_dense(x[t], *experts[e], inp.swiglu_limit, act4=act4)
             y = [a + gate[e] * b for a, b in zip(y, z)]
         logits.append(lt)
         idx_all.append(sel)

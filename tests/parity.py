@@ -53,10 +53,10 @@ def rne_bf16_bits(y32: np.ndarray) -> np.ndarray:
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def oracle_with_adoption(inp, gpu_idx: np.ndarray, tokens=None):
+def oracle_with_adoption(inp, gpu_idx: np.ndarray, tokens=None, act4: bool = False):
     """Oracle run; for near-tie tokens whose GPU selection differs, adopt the GPU's set when every
     expert it picked scores within 1e-6 of the oracle's k-th largest logit."""
-    o = oracle.forward(inp, tokens=tokens)
+    o = oracle.forward(inp, tokens=tokens, act4=act4)
     flagged = np.nonzero(o["flagged"])[0]
     adopt = {}
     for t in flagged:
@@ -66,7 +66,7 @@ def oracle_with_adoption(inp, gpu_idx: np.ndarray, tokens=None):
             if np.all(o["logits"][t, gpu_idx[t]] >= kth - oracle.NEAR_TIE):
                 adopt[int(t)] = gpu_idx[t]
     if adopt:
-        o = oracle.forward(inp, tokens=tokens, override_idx=adopt)
+        o = oracle.forward(inp, tokens=tokens, override_idx=adopt, act4=act4)
     o["n_flagged"], o["n_adopted"] = int(len(flagged)), len(adopt)
     return o
 

@@ -352,3 +352,52 @@ def test_block_is_the_layer_on_the_normalised_rows_plus_the_input():
     ref = np.array(brute.brute_layer(inner)["y"])
     assert np.abs(o["y_moe"] - ref).max() <= 1e-12 * np.abs(ref).max()
     assert np.array_equal(o["y"], oracle.bf16_to_f64(inp.x_bf16) + o["y_moe"])
+
+
+# --------------------------------------------------------------------------- activation-quantized variant
+def test_act4_quantizer_ocp_ties_saturation_and_exponent():
+    """OCP MX conversion to MXFP4: a block with amax 7 keeps exponent 0, so its values are the
+    E2M1 inputs: ties 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4 (even
+    codes), 7 saturates to 6.  A block with amax 0.3 takes exponent floor(log2 0.3) - 2 = -4:
+    0.3 / 2^-4 = 4.8 -> 4, i.e. 0.25.  An all-zero block stays zero."""
+    v = np.array([[0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 4.0, -0.25, -5.0, 0.0] + [0.0] * 20
+                  + [0.3, 0.03, -0.1] + [0.0] * 29 + [0.0] * 32])
+    q = oracle.mxfp4_quantize_rows(v)[0]
+    assert q[:12].tolist() == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, 4.0, 0.0, -4.0, 0.0]
+    # 0.03 / 2^-4 = 0.48 -> 0.5 (0.03125); -0.1 / 2^-4 = -1.6 -> -1.5 (-0.09375)
+    assert q[32:35].tolist() == [0.25, 0.03125, -0.09375]
+    assert np.all(q[64:] == 0.0)
+
+
+def test_act4_quantizer_is_idempotent_and_within_half_a_step():
+    """Quantizing twice changes nothing; every element is within half the local E2M1 step of
+    its input (times the block scale), or saturated at 6 times the scale."""
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((8, 256)) * np.exp(rng.uniform(-8, 8, (8, 1)))
+    q = oracle.mxfp4_quantize_rows(v)
+    assert np.array_equal(oracle.mxfp4_quantize_rows(q), q)
+    b = v.reshape(8, -1, 32)
+    E = np.floor(np.log2(np.abs(b).max(-1, keepdims=True))) - 2
+    r = np.abs(b) / 2.0 ** E
+    half_step = np.where(r < 2, 0.25, np.where(r < 4, 0.5, 1.0))
+    err = np.abs(b - q.reshape(b.shape)) / 2.0 ** E
+    assert np.all((err <= half_step + 1e-12) | ((r > 6) & (np.abs(q.reshape(b.shape)) == 6 * 2.0 ** E)))
+
+
+@pytest.mark.parametrize("case", [
+    dict(cfg=0),
+    dict(cfg=dict(T=5, D=64, E=1, k=1, I=64, seed=25)),              # one expert
+    dict(cfg=dict(T=6, D=64, E=3, k=3, I=64, seed=26)),              # k = E
+    dict(cfg=dict(T=1, D=96, E=8, k=4, I=64, seed=27)),              # single token
+])
+def test_act4_oracle_equals_dense_brute_force(case):
+    """The activation-quantized layer against the pure-Python dense evaluation with its own
+    element-by-element MXFP4 quantizer."""
+    inp = synth.make_inputs(case["cfg"])
+    o = oracle.forward(inp, act4=True)
+    b = brute.brute_layer(inp, act4=True)
+    assert o["idx"].tolist() == b["idx"]
+    yb = np.array(b["y"])
+    assert np.abs(o["y"] - yb).max() <= 1e-12 * np.abs(yb).max()
+    # and it is not the W4A16 layer
+    assert not np.allclose(o["y"], oracle.forward(inp)["y"], rtol=1e-3, atol=0)
