@@ -184,14 +184,30 @@ __device__ __forceinline__ Fp4Block quant_fp4x32(const float (&v)[32]) {
   int E = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 2;
   E = E < -127 ? -127 : (E > 127 ? 127 : E);
   r.scale = (uint32_t)(E + 127);
-  const float inv = ldexpf(1.0f, -E);
   uint32_t w[4];
+  if (E > -126) {
+    // the packed conversion divides by the scale and rounds exactly as above (checked against
+    // e2m1_code over ties, saturation and signs at scales 2^-20 .. 2^10); two values per call
+    const float sc = ldexpf(1.0f, E);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t x = 0;
+    for (int d = 0; d < 4; ++d) {
+      uint32_t x = 0;
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 0], v[8 * d + 1], sc, 0);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 2], v[8 * d + 3], sc, 1);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 4], v[8 * d + 5], sc, 2);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 6], v[8 * d + 7], sc, 3);
+      w[d] = x;
+    }
+  } else {
+    // scales below the fp32 normal range: element by element
+    const float inv = ldexpf(1.0f, -E);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x |= e2m1_code(v[8 * d + j], inv) << (4 * j);
-    w[d] = x;
+    for (int d = 0; d < 4; ++d) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x |= e2m1_code(v[8 * d + j], inv) << (4 * j);
+      w[d] = x;
+    }
   }
   r.codes = make_uint4(w[0], w[1], w[2], w[3]);
   return r;
