@@ -165,3 +165,50 @@ def test_prepack_layout(D_, I_):
     co, so = M.moe_mxfp4_prepack(d, M.MOE_STAGE_DOWN, inp.dn_codes, inp.dn_scales)
     rc, rs = prepack_reference(inp.dn_codes, inp.dn_scales, D_, I_, I_, False)
     assert np.array_equal(co, rc) and np.array_equal(so, rs)
+
+
+def test_block_and_act4_entry_points_reject_bad_arguments(L):
+    """The pre-norm block and the MXFP4-activation entry points validate before any launch."""
+    d = ctypes.byref(D)
+    A = 1 << 20                                   # fake, aligned, never dereferenced
+    w = M.moe_weights(A, A, A, A)
+    # RMSNorm: eps must be positive and finite; pointers 16-byte aligned; T = 0 is a no-op
+    assert L.moe_rmsnorm(d, 4, A, A, 0.0, A, None) == M.MOE_EINVAL
+    assert L.moe_rmsnorm(d, 4, A, A, -1e-5, A, None) == M.MOE_EINVAL
+    assert L.moe_rmsnorm(d, 4, A, A, float("nan"), A, None) == M.MOE_EINVAL
+    assert L.moe_rmsnorm(d, 4, A, A + 4, 1e-5, A, None) == M.MOE_EINVAL            # misaligned gamma
+    assert L.moe_rmsnorm(d, 4, None, A, 1e-5, A, None) == M.MOE_EINVAL
+    assert L.moe_rmsnorm(d, 0, A, A, 1e-5, A, None) == M.MOE_OK
+    # combine with residual
+    assert L.moe_combine_residual(d, 4, A, A, None, A, M.MOE_FP32, None) == M.MOE_EINVAL
+    assert L.moe_combine_residual(d, 4, A, A, A + 8, A, M.MOE_FP32, None) == M.MOE_EINVAL
+    assert L.moe_combine_residual(d, 4, A, A, A, A, 9, None) == M.MOE_EINVAL
+    assert L.moe_combine_residual(d, 0, A, A, A, A, M.MOE_BF16, None) == M.MOE_OK
+    # block forward: its workspace is the normalised rows (256-byte rounded) + moe_forward's
+    for T in (1, 4, 32, 4096):
+        assert L.moe_block_workspace_bytes(d, T) == -(-T * 2880 * 2 // 256) * 256 + L.moe_workspace_bytes(d, T)
+    need = L.moe_block_workspace_bytes(d, 4)
+    assert L.moe_block_forward(d, 4, A, A, 1e-5, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need - 1,
+                               None) == M.MOE_EWORKSPACE
+    assert L.moe_block_forward(d, 4, A, None, 1e-5, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need,
+                               None) == M.MOE_EINVAL
+    assert L.moe_block_forward(d, 4, A, A, 0.0, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need,
+                               None) == M.MOE_EINVAL
+    assert L.moe_block_forward(d, 0, A, A, 1e-5, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need,
+                               None) == M.MOE_OK
+    # MXFP4 activations: 48 bytes per row and 64-wide k-tile
+    assert L.moe_act4_pack_bytes(2880, 7) == 7 * 45 * 48
+    assert L.moe_act4_pack_bytes(96, 7) == 0
+    assert L.moe_pack_act4(96, 4, A, A, None) == M.MOE_EUNSUPPORTED
+    assert L.moe_pack_act4(64, 4, A, A + 8, None) == M.MOE_EINVAL
+    assert L.moe_pack_act4(64, 0, A, A, None) == M.MOE_OK
+    assert L.moe_expert_gemm_mxfp4_act4(d, 4, 7, A, A, A, A, A, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4_act4(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4_act4(d, 0, M.MOE_STAGE_GATE_UP, A, A, A, A, None, A, None) == M.MOE_OK
+    # the act4 workspace holds smaller packed rows than the default one
+    for T in (4, 32, 4096):
+        assert 0 < L.moe_workspace_bytes_act4(d, T) < L.moe_workspace_bytes(d, T)
+    need4 = L.moe_workspace_bytes_act4(d, 4)
+    assert L.moe_forward_act4(d, 4, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need4 - 1,
+                              None) == M.MOE_EWORKSPACE
+    assert L.moe_forward_act4(d, 0, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need4, None) == M.MOE_OK
