@@ -61,6 +61,7 @@ def workload_name(cfg: dict) -> str:
 
 GEMM_SRC = os.path.join(ROOT, "mxfp4_expert_layer_moe_amd", "csrc", "gemm.hip")
 GU_KERNEL_PREFIX = "void moe::expert_gemm_kernel<0,"
+GU_KERNEL_BF16_SUFFIX = ", 0>(moe::GemmArgs)"     # last template argument: bf16 (split FP6) activations
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -106,7 +107,7 @@ def traffic_report(args):
     for key, d, counter in (("fetch", args.traffic_report[0], "FETCH_SIZE"),
                             ("write", args.traffic_report[1], "WRITE_SIZE")):
         per = _per_dispatch(_counter_rows(d), counter)
-        gu = [v for n, v in per.values() if n.startswith(GU_KERNEL_PREFIX)]
+        gu = [v for n, v in per.values() if n.startswith(GU_KERNEL_PREFIX) and n.endswith(GU_KERNEL_BF16_SUFFIX)]
         cp = [v for n, v in per.values() if n.startswith(COPY_KERNEL)][-3:]
         if not gu or len(cp) < 3:
             raise SystemExit(f"{d}: {len(gu)} gate/up dispatches, {len(cp)} calibration copies")
