@@ -112,10 +112,10 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
     ssbase[nb] = q * g.KG * 256;
   }
   auto load_b = [&](const int nb, const int kt) {
-    return __builtin_amdgcn_raw_buffer_load_b128(rsB, voffB, sbase[nb] + kt * 1024, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(rsB, voffB, sbase[nb] + kt * 1024, kLoadStream);
   };
   auto load_s = [&](const int nb, const int grp) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsS, voffS, ssbase[nb] + grp * 256, 0);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsS, voffS, ssbase[nb] + grp * 256, kLoadStream);
   };
 
   // weight ring: slot j holds k-tile kt with kt % P == j; scale slot s holds group (kt / 4) with (kt/4) % (P/4) == s
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
 #define MOE_DECODE_DOWN_NB 1
 #endif
 #ifndef MOE_DECODE_DOWN_P
-#define MOE_DECODE_DOWN_P 16
+#define MOE_DECODE_DOWN_P 8
 #endif
 #ifndef MOE_DECODE_GU_P
 #define MOE_DECODE_GU_P 8
