@@ -26,19 +26,23 @@ def row_bytes(K: int) -> int:
     return K // 64 * 112
 
 
-def decode(buf, K: int, rows: int):
-    """buf: uint8 array (at least rows*row_bytes(K)) -> (hi, lo) float64 [rows][K]."""
+def decode(buf, K: int, rows: int, chunk: int = 2048):
+    """buf: uint8 array (at least rows*row_bytes(K)) -> (hi, lo) float64 [rows][K].
+    Rows are decoded `chunk` at a time so the bit-level temporaries stay small."""
     kt = K // 64
-    a = np.asarray(buf, dtype=np.uint8)[: rows * row_bytes(K)].reshape(rows, kt, 112)
-    out = []
-    for term in range(2):
-        codes = a[:, :, term * 48:(term + 1) * 48].reshape(rows, kt, 2, 24)
-        bits = np.unpackbits(codes, axis=3, bitorder="little").reshape(rows, kt, 2, 32, 6)
-        c = (bits * (1 << np.arange(6))).sum(axis=4)
-        sbyte = a[:, :, 96 + 2 * term:98 + 2 * term].astype(np.int64)          # [rows][kt][2]
-        val = _E2M3[c] * np.ldexp(1.0, sbyte - 127)[..., None]
-        out.append(val.reshape(rows, K))
-    return out[0], out[1]
+    a = np.asarray(buf, dtype=np.uint8).reshape(-1)[: rows * row_bytes(K)].reshape(rows, kt, 112)
+    hi, lo = np.empty((rows, K)), np.empty((rows, K))
+    weights = (1 << np.arange(6)).astype(np.uint8)
+    for r0 in range(0, rows, chunk):
+        sub = a[r0:r0 + chunk]
+        n = sub.shape[0]
+        for term, dst in ((0, hi), (1, lo)):
+            codes = sub[:, :, term * 48:(term + 1) * 48].reshape(n, kt, 2, 24)
+            bits = np.unpackbits(codes, axis=3, bitorder="little").reshape(n, kt, 2, 32, 6)
+            c = (bits * weights).sum(axis=4, dtype=np.int64)
+            sbyte = sub[:, :, 96 + 2 * term:98 + 2 * term].astype(np.int64)    # [n][kt][2]
+            dst[r0:r0 + n] = (_E2M3[c] * np.ldexp(1.0, sbyte - 127)[..., None]).reshape(n, K)
+    return hi, lo
 
 
 def decode_sum(buf, K: int, rows: int) -> np.ndarray:

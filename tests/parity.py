@@ -106,7 +106,9 @@ def compare(inp, g: dict, o: dict, check_h: bool = True) -> dict:
     rms_y = float(np.sqrt(np.mean(o["y"] ** 2)))
     stats["rms_y"] = rms_y
     if check_h and pos:
-        hs = actpack.decode_sum(g["h_packed"], I, T * k)[pos]
+        rb = actpack.row_bytes(I)
+        hrows = np.asarray(g["h_packed"]).reshape(-1)[: T * k * rb].reshape(T * k, rb)[pos]
+        hs = actpack.decode_sum(hrows, I, len(pos))
         ho = np.array([o["h"][p] for p in pos])
         dh = np.abs(hs - ho).max() / max(np.abs(ho).max(), 1e-30)
         stats["h_max_err_rel_max"] = float(dh)

@@ -71,6 +71,18 @@ SMALL = {
     "multi_tile_multi_group": dict(cfg=dict(T=200, D=256, E=8, k=2, I=512, seed=46)),
     "k_tail_groups": dict(cfg=dict(T=70, D=320, E=4, k=2, I=448, seed=47)),
     "skew_small": dict(cfg=dict(T=300, D=128, E=32, k=4, I=128, seed=48), bias="zipf"),
+    # size thresholds of the path, each met exactly and passed by one:
+    # 8-row tiles up to 8 assignments per expert (here 64 = 8 x 8), 128-row tiles past it
+    "decode_tiles_at_limit": dict(cfg=dict(T=32, D=64, E=8, k=2, I=64, seed=53)),
+    "prefill_tiles_past_limit": dict(cfg=dict(T=33, D=64, E=8, k=2, I=64, seed=54)),
+    # grouping in one 256-thread workgroup up to 256 assignments, one 1024-thread workgroup up
+    # to 1024, three kernels past that
+    "grouping_256_threads_at_limit": dict(cfg=dict(T=64, D=64, E=16, k=4, I=64, seed=58)),
+    "grouping_1024_threads_past_256": dict(cfg=dict(T=65, D=64, E=16, k=4, I=64, seed=59)),
+    "grouping_one_workgroup_at_limit": dict(cfg=dict(T=256, D=64, E=16, k=4, I=64, seed=55)),
+    "grouping_three_kernels_past_limit": dict(cfg=dict(T=257, D=64, E=16, k=4, I=64, seed=56)),
+    # the one-workgroup selection takes at most 32 tokens and 32 experts
+    "experts_33_general_selection": dict(cfg=dict(T=32, D=64, E=33, k=4, I=64, seed=57)),
 }
 
 
@@ -154,6 +166,17 @@ def test_full_size_workload(cfg):
     n = FULL[cfg]["tokens"]
     tokens = None if n is None else np.sort(np.random.default_rng(100 + cfg).choice(inp.T, n, replace=False))
     _full_check(f"config{cfg}", inp, tokens)
+
+
+def test_large_batch_full_shape():
+    """32768 tokens at the 20b shape (131072 assignments, four times the largest benchmark
+    workload's): routing, grouping and the tile table bit-exact for every token, the expert
+    outputs on 32 sampled tokens."""
+    t0 = time.time()
+    inp = synth.make_inputs(dict(T=32768, D=2880, E=32, k=4, I=2880, seed=71))
+    print(f"[parity] large batch generated in {time.time() - t0:.1f}s", flush=True)
+    tokens = np.sort(np.random.default_rng(171).choice(inp.T, 32, replace=False))
+    _full_check("large_batch_T32768", inp, tokens)
 
 
 def test_clamp_stress_prefill_shape():
