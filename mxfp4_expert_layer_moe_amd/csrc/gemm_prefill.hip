@@ -31,6 +31,8 @@
 //    chunks and issues one FP4 x FP4 instruction per weight tile in the plain
 //    operand layout (lanes 0-31 block 0, lanes 32-63 block 1, weights as
 //    loaded); its gate/up epilogue quantizes h to MXFP4.
+#include <type_traits>
+
 #include "mfma_ops.h"
 
 namespace moe {
@@ -116,6 +118,12 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   const int e = __builtin_amdgcn_readfirstlane(hdr.x);
   const int p0 = __builtin_amdgcn_readfirstlane(hdr.y);
   const int nrows = __builtin_amdgcn_readfirstlane(hdr.z);
+
+  // The rest of the kernel exists in four copies, one per number NRB of 32-row blocks that hold
+  // rows of the tile: a partial tile's empty row blocks get neither operand reads nor matrix
+  // instructions.  Every other step is the same in all copies.
+  auto body = [&](auto nrb_c) __attribute__((always_inline)) {
+  constexpr int NRB = decltype(nrb_c)::value;
 
   // down: each row's gate weight, loaded now and waited for only in the epilogue
   float wrow = 0.0f;
@@ -244,9 +252,13 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     uint32_t sqn[kPWaveTiles][2];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      const AOps cur = nxt;
-      nxt = rb < 3 ? read_ops(kt, rb + 1) : read_ops(min(kt + 1, KT - 1), 0);
-      if constexpr (F4) {
+      AOps cur;
+      if (rb < NRB) {                                     // resolved at compile time
+        cur = nxt;
+        nxt = rb + 1 < NRB ? read_ops(kt, rb + 1) : read_ops(min(kt + 1, KT - 1), 0);
+      }
+      if (rb >= NRB) {
+      } else if constexpr (F4) {
         const v8i a = __builtin_shufflevector(cur.q, cur.q, 0, 1, 2, 3, 12, 13, 14, 15);
 #pragma unroll
         for (int cb = 0; cb < kPWaveTiles; ++cb)
@@ -379,6 +391,12 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
       __builtin_amdgcn_wave_barrier();
     }
   }
+  };
+  const int live_blocks = (nrows + 31) >> 5;             // 1..4, uniform
+  if (live_blocks >= 4) body(std::integral_constant<int, 4>{});
+  else if (live_blocks == 3) body(std::integral_constant<int, 3>{});
+  else if (live_blocks == 2) body(std::integral_constant<int, 2>{});
+  else body(std::integral_constant<int, 1>{});
 }
 
 #ifndef MOE_PREFILL_NA
