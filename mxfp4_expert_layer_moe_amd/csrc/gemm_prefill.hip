@@ -143,14 +143,18 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     // rows past the tile repeat its last row
     aoff[i] = (uint32_t)srow[min(row, nrows - 1)] * g.arb + (uint32_t)(q - row * (CH / 16)) * 16u;
   }
+  // piece sets i whose pieces all lie past the occupied row blocks are neither loaded nor staged
+  constexpr int kLivePieces = NRB * 32 * (CH / 16);
   auto load_a = [&](const int kt, v4i (&buf)[NPC]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NPC; ++i) buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, aoff[i], kt * CH, 0);
+    for (int i = 0; i < NPC; ++i)
+      if (256 * i < kLivePieces) buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, aoff[i], kt * CH, 0);
   };
   auto store_a = [&](const int s, const v4i (&buf)[NPC]) __attribute__((always_inline)) {
     uint8_t* dst = sA + s * kPSlotBytes + tid * 16;
 #pragma unroll
-    for (int i = 0; i < NPC; ++i) *reinterpret_cast<v4i*>(dst + i * 4096) = buf[i];
+    for (int i = 0; i < NPC; ++i)
+      if (256 * i < kLivePieces) *reinterpret_cast<v4i*>(dst + i * 4096) = buf[i];
   };
 
   // ---- weights: this wavefront's four 32-column tiles of expert e -----------------------------
