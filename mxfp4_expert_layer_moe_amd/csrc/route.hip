@@ -93,10 +93,15 @@ constexpr int kLogitBatch = 4;                 // k-steps whose loads are issued
 static bool route_small(int T, int E) { return T <= 32 && E <= 32; }
 constexpr int kSmallKW = 16;
 
+// Larger batches: route_logits_wide_kernel, one workgroup per (64-token block, 32-expert tile)
+// and K slice.
+constexpr int kWideWaves = 8;                  // 2 token tiles x 4 k-step lanes
+constexpr int kWideTokens = 64;
+
 static int route_kw(int T, int E) {
   if (route_small(T, E)) return kSmallKW;
-  const int tiles = ((T + kRouteTokens - 1) / kRouteTokens) * ((E + 31) / 32);
-  return tiles <= 64 ? 4 : (tiles <= 256 ? 2 : 1);
+  const int blocks = ((T + kWideTokens - 1) / kWideTokens) * ((E + 31) / 32);
+  return blocks <= 128 ? 4 : (blocks <= 256 ? 2 : 1);     // about two workgroups per compute unit
 }
 
 struct RouteWs {
@@ -185,6 +190,28 @@ __device__ __forceinline__ void logit_steps(int T, int D, int E, const uint16_t*
   }
 }
 
+// Exact split of n fp32 router weights into three bf16 terms by truncation (hi + mid + lo == w),
+// as in logit_steps, packed two per dword in element order.
+template <int N>
+__device__ __forceinline__ void split_terms(const float (&wv)[N], uint32_t (&hu)[N / 2], uint32_t (&mu)[N / 2],
+                                            uint32_t (&lu)[N / 2]) {
+#pragma unroll
+  for (int i = 0; i < N; i += 2) {
+    uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t h = trunc_bf16_bits(wv[i + j]);
+      const float r1 = wv[i + j] - __uint_as_float(h);        // exact
+      const uint32_t m = trunc_bf16_bits(r1);
+      const float r2 = r1 - __uint_as_float(m);               // exact, <= 8 significant bits
+      hb[j] = h >> 16; mb[j] = m >> 16; lb[j] = __float_as_uint(r2) >> 16;
+    }
+    hu[i / 2] = hb[0] | (hb[1] << 16);
+    mu[i / 2] = mb[0] | (mb[1] << 16);
+    lu[i / 2] = lb[0] | (lb[1] << 16);
+  }
+}
+
 // Fixed-order sum of the 16 wavefronts' partial tiles: slot s = p_s + p_(s+8) is left in
 // red[s] (the caller adds slots 0..7 in order); the squared-norm partials go to rsq.
 __device__ __forceinline__ void reduce_partials(const double (&accd)[16], float sq, float xs,
@@ -256,6 +283,129 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, i
     for (int w = 0; w < kLogitWaves; ++w) v += rsq[w][which][r];
     if (which == 0 && nt == 0 && tt * kRouteTokens + r < T) xsq[(size_t)kw * T + tt * kRouteTokens + r] = v;
     if (which == 1 && tt == 0) wsq[(size_t)kw * epad + nt * 32 + r] = v;
+  }
+}
+
+// Router logits for larger batches.  A workgroup of 8 wavefronts takes 64 tokens (two 32-token
+// tiles) x one 32-expert tile x a contiguous slice of K (KW slices).  K goes in rounds of 64:
+// every thread loads one float4 of the round's 32 x 64 router chunk, splits it into the three
+// bf16 terms and stores them in an LDS ring of two rounds, so each router weight is split once
+// per 64 tokens and read from LDS by both token tiles; wavefront (tile q, lane group j) takes
+// k-step j of every round for tile q.  The arithmetic per k-step is that of logit_steps: three
+// bf16 MFMAs from zero, their fp32 result added into float64.  The four k-step lanes' partial
+// tiles are summed in LDS in a fixed order.  Loads run two rounds ahead.
+constexpr int kWideRowBytes = 128 + 16;        // one expert row of a round in bf16, padded
+constexpr int kWidePlane = 32 * kWideRowBytes; // one term of a round
+constexpr int kWideBuf = 3 * kWidePlane;
+
+__global__ __launch_bounds__(kWideWaves * 64) void route_logits_wide_kernel(
+    int T, int D, int E, int KW, const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    double* __restrict__ logit, float* __restrict__ xsq, float* __restrict__ wsq, int logit_wgs,
+    uint8_t* __restrict__ xpack, int af) {
+  constexpr int kRedBytes = 4 * 2 * 32 * 33 * 8;                 // [k-step lane][tile][token][expert]
+  static_assert(2 * kWideBuf <= kRedBytes, "the ring fits the reduction area");
+  __shared__ __align__(16) uint8_t smem[kRedBytes];
+  __shared__ float rsx[4][2][32];                               // partial ||x_t||^2
+  if ((int)blockIdx.x >= logit_wgs) {                           // activation split, one block per lane
+    const long long blk = (long long)(blockIdx.x - logit_wgs) * (kWideWaves * 64) + threadIdx.x;
+    pack_block_lane(x, D, (long long)T * (D / kBlock), blk, xpack, af);
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int tq = wave & 1, kq = wave >> 1;
+  const int nte = (E + 31) / 32;
+  const int kw = blockIdx.x % KW;
+  const int nt = (blockIdx.x / KW) % nte;
+  const int tb = blockIdx.x / (KW * nte);
+  const int epad = nte * 32;
+  const int row = lane & 31, half = lane >> 5;
+  const int tok = tb * kWideTokens + tq * 32 + row;
+  const int rounds = D / 64;
+  const int r0 = rounds * kw / KW, r1 = rounds * (kw + 1) / KW;
+  // this thread's float4 of every router chunk, and its x row (clamped; masked at the end)
+  const int wrow = tid >> 4, wc4 = tid & 15;
+  const bool wlive = nt * 32 + wrow < E;
+  const float* wsrc = wr + (size_t)min(nt * 32 + wrow, E - 1) * D + 4 * wc4;
+  const uint16_t* xa = x + (size_t)min(tok, T - 1) * D + 16 * kq + 8 * half;
+  auto load_w = [&](const int r) {
+    return wlive && r < r1 ? *reinterpret_cast<const float4*>(wsrc + 64 * r) : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto load_x = [&](const int r) {
+    return r < r1 ? *reinterpret_cast<const uint4*>(xa + 64 * r) : make_uint4(0, 0, 0, 0);
+  };
+  float4 wq[2] = {load_w(r0), load_w(r0 + 1)};
+  uint4 xq[2] = {load_x(r0), load_x(r0 + 1)};
+  double accd[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) accd[i] = 0.0;
+  float xs = 0.0f, sq = 0.0f;
+  auto round = [&](const int r, const int slot) __attribute__((always_inline)) {
+    uint8_t* buf = smem + slot * kWideBuf;
+    {
+      const float wv[4] = {wq[slot].x, wq[slot].y, wq[slot].z, wq[slot].w};
+      uint32_t hu[2], mu[2], lu[2];
+      split_terms<4>(wv, hu, mu, lu);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sq += wv[i] * wv[i];
+      uint8_t* dst = buf + wrow * kWideRowBytes + wc4 * 8;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(hu[0], hu[1]);
+      *reinterpret_cast<uint2*>(dst + kWidePlane) = make_uint2(mu[0], mu[1]);
+      *reinterpret_cast<uint2*>(dst + 2 * kWidePlane) = make_uint2(lu[0], lu[1]);
+    }
+    const uint4 xu = xq[slot];
+    wq[slot] = load_w(r + 2);
+    xq[slot] = load_x(r + 2);
+    __syncthreads();                                            // the round's terms are in LDS
+    const uint8_t* bb = buf + row * kWideRowBytes + 32 * kq + 16 * half;
+    const uint4 hb = *reinterpret_cast<const uint4*>(bb);
+    const uint4 mb = *reinterpret_cast<const uint4*>(bb + kWidePlane);
+    const uint4 lb = *reinterpret_cast<const uint4*>(bb + 2 * kWidePlane);
+    const uint32_t uw[4] = {xu.x, xu.y, xu.z, xu.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(uw[i] << 16), hi = __uint_as_float(uw[i] & 0xFFFF0000u);
+      xs += lo * lo + hi * hi;
+    }
+    const v8bf a = __builtin_bit_cast(v8bf, xu);
+    v16f t = {};
+    t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, lb), t, 0, 0, 0);
+    t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, mb), t, 0, 0, 0);
+    t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, hb), t, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accd[i] += (double)t[i];
+  };
+  // The ring slot of round r is (r - r0) & 1: a slot is rewritten two rounds after its reads, and
+  // every wavefront has passed the barrier of the round in between.
+  int r = r0;
+  for (; r + 1 < r1; r += 2) {
+    round(r, 0);
+    round(r + 1, 1);
+  }
+  if (r < r1) round(r, 0);
+  __syncthreads();                                              // the ring is free
+  double (*red)[2][32][33] = reinterpret_cast<double (*)[2][32][33]>(smem);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) red[kq][tq][8 * (i >> 2) + 4 * half + (i & 3)][row] = accd[i];
+  xs += __shfl_xor(xs, 32);
+  if (half == 0) rsx[kq][tq][row] = xs;
+  // the router rows' squared norms over this K slice: 16 threads per row, summed in a fixed order
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) sq += __shfl_xor(sq, d);
+  if (tb == 0 && wc4 == 0) wsq[(size_t)kw * epad + nt * 32 + wrow] = sq;
+  __syncthreads();
+  for (int j = tid; j < 2 * 32 * 32; j += kWideWaves * 64) {
+    const int q = j >> 10, m = (j >> 5) & 31, c = j & 31;
+    const double v = ((red[0][q][m][c] + red[1][q][m][c]) + red[2][q][m][c]) + red[3][q][m][c];
+    const int tj = tb * kWideTokens + q * 32 + m;
+    if (tj < T) logit[((size_t)kw * T + tj) * epad + nt * 32 + c] = v;
+  }
+  if (nt == 0 && tid < 64) {
+    const int q = tid >> 5, m = tid & 31;
+    const float v = ((rsx[0][q][m] + rsx[1][q][m]) + rsx[2][q][m]) + rsx[3][q][m];
+    const int tj = tb * kWideTokens + q * 32 + m;
+    if (tj < T) xsq[(size_t)kw * T + tj] = v;
   }
 }
 
@@ -628,11 +778,19 @@ static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const fl
   *logit = reinterpret_cast<double*>(base + L.logit);
   *xsq = reinterpret_cast<float*>(base + L.xsq);
   *wsq = reinterpret_cast<float*>(base + L.wsq);
-  const int logit_wgs = ((T + kRouteTokens - 1) / kRouteTokens) * ((E + 31) / 32) * *KW;
   const long long pack_blocks = xpack ? (long long)T * (D / kBlock) : 0;
-  const long long pack_wgs = (pack_blocks + kLogitWaves * 64 - 1) / (kLogitWaves * 64);
-  route_logits_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kLogitWaves * 64), 0, s>>>(
-      T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
+  const int nte = (E + 31) / 32;
+  if (route_small(T, E)) {
+    const int logit_wgs = ((T + kRouteTokens - 1) / kRouteTokens) * nte * *KW;
+    const long long pack_wgs = (pack_blocks + kLogitWaves * 64 - 1) / (kLogitWaves * 64);
+    route_logits_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kLogitWaves * 64), 0, s>>>(
+        T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
+  } else {
+    const int logit_wgs = ((T + kWideTokens - 1) / kWideTokens) * nte * *KW;
+    const long long pack_wgs = (pack_blocks + kWideWaves * 64 - 1) / (kWideWaves * 64);
+    route_logits_wide_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kWideWaves * 64), 0, s>>>(
+        T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
+  }
   return hipGetLastError();
 }
 
