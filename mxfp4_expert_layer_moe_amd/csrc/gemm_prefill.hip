@@ -119,9 +119,9 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   const int p0 = __builtin_amdgcn_readfirstlane(hdr.y);
   const int nrows = __builtin_amdgcn_readfirstlane(hdr.z);
 
-  // The rest of the kernel exists in four copies, one per number NRB of 32-row blocks that hold
-  // rows of the tile: a partial tile's empty row blocks get neither operand reads nor matrix
-  // instructions.  Every other step is the same in all copies.
+  // With K known at compile time the rest of the kernel exists in four copies, one per number NRB
+  // of 32-row blocks that hold rows of the tile: a partial tile's empty row blocks get neither
+  // operand reads, staging nor matrix instructions.  Every other step is the same in all copies.
   auto body = [&](auto nrb_c) __attribute__((always_inline)) {
   constexpr int NRB = decltype(nrb_c)::value;
 
@@ -396,7 +396,8 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     }
   }
   };
-  const int live_blocks = (nrows + 31) >> 5;             // 1..4, uniform
+  // (the generic-K kernel keeps one copy: its k-loop is not unrolled and it serves odd shapes only)
+  const int live_blocks = KTC > 0 ? (nrows + 31) >> 5 : 4;   // 1..4, uniform
   if (live_blocks >= 4) body(std::integral_constant<int, 4>{});
   else if (live_blocks == 3) body(std::integral_constant<int, 3>{});
   else if (live_blocks == 2) body(std::integral_constant<int, 2>{});
