@@ -71,6 +71,9 @@ SMALL = {
     "multi_tile_multi_group": dict(cfg=dict(T=200, D=256, E=8, k=2, I=512, seed=46)),
     "k_tail_groups": dict(cfg=dict(T=70, D=320, E=4, k=2, I=448, seed=47)),
     "skew_small": dict(cfg=dict(T=300, D=128, E=32, k=4, I=128, seed=48), bias="zipf"),
+    # degenerate routing: a single expert (every gate 1), and top-1 of 8
+    "one_expert": dict(cfg=dict(T=5, D=64, E=1, k=1, I=64, seed=60)),
+    "top1_of_8": dict(cfg=dict(T=40, D=64, E=8, k=1, I=64, seed=61)),
     # size thresholds of the path, each met exactly and passed by one:
     # 8-row tiles up to 8 assignments per expert (here 64 = 8 x 8), 128-row tiles past it
     "decode_tiles_at_limit": dict(cfg=dict(T=32, D=64, E=8, k=2, I=64, seed=53)),
