@@ -6,6 +6,7 @@ output within 2e-2 x RMS(y); the bf16 output equal to RNE(fp32 output).
 Small cases compare every token; the full-size workloads compare routing for
 all tokens and the expert outputs on a seeded sample of tokens.
 """
+import dataclasses
 import json
 import os
 import sys
@@ -14,6 +15,7 @@ import time
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from tests import parity
 
@@ -169,6 +171,20 @@ def test_full_size_workload(cfg):
     n = FULL[cfg]["tokens"]
     tokens = None if n is None else np.sort(np.random.default_rng(100 + cfg).choice(inp.T, n, replace=False))
     _full_check(f"config{cfg}", inp, tokens)
+
+
+@pytest.mark.parametrize("T", [24, 300])           # one-workgroup selection / 16-token workgroups
+def test_duplicate_router_rows_force_exact_rescoring(T):
+    """Experts 2j and 2j+1 get the same router row and bias, so their logits tie exactly; with an
+    odd k the k-th and (k+1)-th places are always such a pair, so every token is flagged and
+    re-scored in float64, and the tie must go to the lower expert id, as in the oracle."""
+    inp = synth.make_inputs(dict(T=T, D=128, E=16, k=3, I=128, seed=62))
+    wr, br = inp.w_router.copy(), inp.b_router.copy()
+    wr[1::2], br[1::2] = wr[0::2], br[0::2]
+    inp = dataclasses.replace(inp, w_router=wr, b_router=br)
+    o = oracle.forward(inp)
+    assert o["flagged"].all()                           # every token goes through the re-scoring
+    _full_check(f"duplicate_router_rows_T{T}", inp)
 
 
 def test_large_batch_full_shape():
