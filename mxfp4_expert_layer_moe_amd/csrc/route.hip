@@ -6,26 +6,24 @@
 // Experts": the router picks several experts and weights them, e.g.
 // A = 0.7 NN2 + 0.3 NN4; gpt-oss keeps 4 of 32 / 128).
 //
-// Two kernels:
-//  route_logits: KW workgroups of 16 wavefronts per (32-token tile, 32-expert
-//     tile) split the K loop (KW > 1 only for small batches, so that a decode
-//     step still spreads over many compute units); each wavefront issues the
-//     loads of four k-steps before their matrix instructions.  Logits run on
-//     the bf16 matrix cores:
-//     x is bf16 and the fp32 router weight is split exactly into three bf16
-//     terms (truncation: hi + mid + lo == w), so every product is exact.  Each
-//     16-wide k-step's three MFMAs start from zero and their small fp32 result
-//     is added into a float64 accumulator, so the only fp32 roundings are those
-//     of 16-term partial sums.  The 16 K-partials of a workgroup are summed in
-//     LDS in a fixed order and its float64 tile is written to the workspace,
-//     with the squared norms of the x rows and w rows.
-//  route_select_small (batches of at most 32 tokens and 32 experts, i.e.
-//     decode): one workgroup sums the partial tiles into an LDS logit table,
-//     then selects with one lane per token (the token's 32 scores sit in its
-//     registers), the same rules and arithmetic as below, and for the layer
-//     forward groups the assignments by expert in the same workgroup.  The
-//     logit kernel splits K sixteen ways at these sizes, so its work spreads
-//     over sixteen compute units.
+// Kernels:
+//  route_logits (at most 32 tokens and 32 experts, i.e. decode): 16 workgroups of 16 wavefronts
+//     split the K loop of the (32-token, 32-expert) tile sixteen ways, so a decode step spreads
+//     over sixteen compute units; each wavefront issues the loads of four k-steps before their
+//     matrix instructions.  Logits run on the bf16 matrix cores: x is bf16 and the fp32 router
+//     weight is split exactly into three bf16 terms (truncation: hi + mid + lo == w), so every
+//     product is exact.  Each 16-wide k-step's three MFMAs start from zero and their small fp32
+//     result is added into a float64 accumulator, so the only fp32 roundings are those of
+//     16-term partial sums.  The 16 K-partials of a workgroup are summed in LDS in a fixed
+//     order and its float64 tile is written to the workspace, with the squared norms of the x
+//     rows and w rows.
+//  route_logits_wide (larger batches): the same arithmetic per k-step, one workgroup of 8
+//     wavefronts per (64-token block, 32-expert tile, K slice); the router chunk of each 64-wide
+//     round is split once into an LDS ring shared by both 32-token tiles.
+//  route_select_small (with route_logits): one workgroup, one thread per (token, expert) pair;
+//     sums the partial tiles into an LDS logit table, ranks each pair among its token's scores,
+//     applies the same rules and arithmetic as route_select, and for the layer forward groups
+//     the assignments by expert in the same workgroup.
 //  route_select: one wavefront per token.  Sums the KW partial tiles in a
 //     fixed order (deterministic), adds the bias, takes the top-k by
 //     wave-wide arg-max (larger logit first, lower id on ties).  If any other
