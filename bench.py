@@ -34,7 +34,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps before each timed region (default: about 0.2 s of steps for the "
+                        "workload, so the GPU clock has settled: 2000 decode steps, 300 prefill steps)")
     p.add_argument("--config", type=int, default=1, help="workload index (1 = gpt-oss-20b decode)")
     p.add_argument("--layers", type=int, default=None, help="distinct weight copies to rotate over")
     p.add_argument("--kernel-steps", type=int, default=None, help="launches of the dominant kernel to time")
@@ -196,6 +198,10 @@ def main():
     M.lib()
     cfg = synth.CONFIGS[args.config]
     decode = args.config == 1
+    if args.warmup is None:
+        # short warmups time the GPU partly before its clock has ramped up: measured 4-5% slower
+        # prefill steps after 5 warmup steps than after 300
+        args.warmup = 2000 if decode else (20 if args.config == 0 else 300)
     L = args.layers or (24 if decode else 2)
     t0 = time.time()
     inp = synth.make_inputs(args.config)
