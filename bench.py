@@ -61,7 +61,16 @@ def workload_name(cfg: dict) -> str:
             f"{cfg['E']} experts, top-{cfg['k']}, MXFP4 experts, bf16 activations")
 
 
-GEMM_SRC = os.path.join(ROOT, "mxfp4_expert_layer_moe_amd", "csrc", "gemm.hip")
+# the decode GEMM kernel and the headers whose device code it compiles
+GEMM_SRCS = [os.path.join(ROOT, "mxfp4_expert_layer_moe_amd", "csrc", f)
+             for f in ("gemm.hip", "mfma_ops.h", "moe_internal.h")]
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 GU_KERNEL_PREFIX = "void moe::expert_gemm_kernel<0,"
 GU_KERNEL_BF16_SUFFIX = ", 0>(moe::GemmArgs)"     # last template argument: bf16 (split FP6) activations
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -103,7 +112,7 @@ def traffic_report(args):
         raise SystemExit("--traffic-report needs the --copy-mib the runs used")
     rec = {"workload": workload_name(cfg),
            "kernel": "expert_gemm_kernel<0> (gate/up + SwiGLU)",
-           "kernel_source_sha256_16": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16],
+           "kernel_source_sha256_16": gemm_source_hash(),
            "command": args.command}
     total = 0.0
     for key, d, counter in (("fetch", args.traffic_report[0], "FETCH_SIZE"),
@@ -147,14 +156,13 @@ def stats_report(args):
     print("\n".join(lines))
 
 
-def traffic_for(kernel_src: str, workload: str):
+def traffic_for(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if rec.get("kernel_source_sha256_16") != h or rec.get("workload") != workload:
+    if rec.get("kernel_source_sha256_16") != gemm_source_hash() or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -281,7 +289,6 @@ def main():
     gu_alg_bytes = gu_weight_bytes + T * D * 2 + T * k * I * 2            # weights + x in + h out (bf16)
     gu_flops = 2.0 * T * k * D * 2 * I
     workload = workload_name(cfg)
-    src = GEMM_SRC
     if decode or gu_alg_bytes / HBM_PEAK_GBS > gu_flops / FP4_PEAK_TFLOPS / 1e3:
         achieved = gu_alg_bytes / (k_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -290,7 +297,7 @@ def main():
         achieved = gu_flops / (k_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP4_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / FP4_PEAK_TFLOPS, 4))
-    roof["traffic"] = traffic_for(src, workload)
+    roof["traffic"] = traffic_for(workload)
     roof["kernel"] = "expert_gemm_kernel<0> (gate/up + SwiGLU)"
     roof["kernel_ms"] = round(k_ms, 5)
     roof["alg_bytes_per_launch"] = int(gu_alg_bytes)
