@@ -438,12 +438,6 @@ hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, flo
   g.scales_per_expert = w_scales_per_expert(N, K);
   const long long items = tile_slots((long long)T * k, E) * g.ngroups;
   const dim3 grid((unsigned)((items + 7) / 8 * 8));
-#ifdef MOE_PREFILL_GENERIC_ONLY
-  g.KT = g.KT + 0 * 45;
-  if (stage == 0) expert_gemm_prefill_kernel<0, 0, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
-  else expert_gemm_prefill_kernel<1, 0, kPNA, kPP><<<grid, dim3(256), 0, s>>>(g);
-  return hipGetLastError();
-#endif
   if (af == kActFp4) {
     if (stage == 0) {
       if (g.KT == 45) expert_gemm_prefill_kernel<0, 45, kPNA, kPP, kActFp4><<<grid, dim3(256), 0, s>>>(g);
