@@ -212,3 +212,22 @@ def test_block_and_act4_entry_points_reject_bad_arguments(L):
     assert L.moe_forward_act4(d, 4, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need4 - 1,
                               None) == M.MOE_EWORKSPACE
     assert L.moe_forward_act4(d, 0, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need4, None) == M.MOE_OK
+
+
+def test_largest_batch_is_accepted_and_one_more_token_is_not(L):
+    """The packed activation rows are addressed with 32-bit buffer offsets: T*k*(packed row
+    bytes) must stay below 2^32.  At the 20b shape (5040 packed bytes per 2880-wide row, top-4)
+    that is T = 213044; the entry points accept it and reject T + 1 before any launch."""
+    d = M.moe_dims(d_model=2880, d_ff=2880, n_experts=32, top_k=4, swiglu_limit=7.0)
+    assert L.moe_act_pack_bytes(2880, 1) == 5040
+    T = ((1 << 32) - 1) // (4 * 5040)
+    assert T == 213044
+    assert L.moe_workspace_bytes(ctypes.byref(d), T) > 0
+    assert L.moe_workspace_bytes(ctypes.byref(d), T + 1) == 0
+    A = 1 << 20                                              # fake, aligned, never dereferenced
+    w = M.moe_weights(A, A, A, A)
+    dp = ctypes.byref(d)
+    assert L.moe_route(dp, T + 1, A, A, A, A, A, None, A, 1 << 40, None) == M.MOE_EUNSUPPORTED
+    assert L.moe_forward(dp, T + 1, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, 1 << 40, None) == M.MOE_EUNSUPPORTED
+    # with T itself the arguments pass and only the (too small) workspace is refused
+    assert L.moe_forward(dp, T, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, 256, None) == M.MOE_EWORKSPACE

@@ -198,6 +198,24 @@ def test_large_batch_full_shape():
     _full_check("large_batch_T32768", inp, tokens)
 
 
+def test_maximum_batch_full_shape():
+    """The largest batch the C ABI accepts at the 20b shape: T*k*(packed row bytes) < 2^32, the
+    reach of the GEMMs' 32-bit buffer offsets, so the packed h buffer ends 256 bytes short of
+    4 GiB.  Routing, grouping and the tile table are checked for every token (852176 assignments),
+    the outputs on 16 sampled tokens."""
+    from mxfp4_expert_layer_moe_amd import moe_dims, moe_workspace_bytes, moe_act_pack_bytes
+    D, k = 2880, 4
+    T = ((1 << 32) - 1) // (k * moe_act_pack_bytes(D, 1))
+    assert T == 213044 and moe_act_pack_bytes(D, T * k) == 4294967040
+    dims = moe_dims(d_model=D, d_ff=D, n_experts=32, top_k=k, swiglu_limit=7.0)
+    assert moe_workspace_bytes(dims, T) > 0 and moe_workspace_bytes(dims, T + 1) == 0
+    t0 = time.time()
+    inp = synth.make_inputs(dict(T=T, D=D, E=32, k=k, I=D, seed=72))
+    print(f"[parity] maximum batch generated in {time.time() - t0:.1f}s", flush=True)
+    tokens = np.sort(np.random.default_rng(172).choice(inp.T, 16, replace=False))
+    _full_check("maximum_batch_T213044", inp, tokens)
+
+
 def test_clamp_stress_prefill_shape():
     inp = synth.make_inputs(dict(T=512, D=2880, E=32, k=4, I=2880, seed=70), x_scale=8.0)
     tokens = np.arange(0, 512, 16)
