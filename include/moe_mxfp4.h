@@ -120,9 +120,9 @@ size_t moe_prepacked_scales_bytes(const moe_dims* dims, moe_stage stage);
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t T);
 
 /*
- * Router, top-k and softmax gating ("Mixture of Experts" section of the
- * ewbang.com walk-through: the router scores experts, keeps several and weights
- * them; gpt-oss keeps 4).
+ * Router, top-k and softmax gating ("gpt-oss architecture walk-through",
+ * section "Mixture of Experts": the router scores experts, keeps several and
+ * weights them; gpt-oss keeps 4).
  *   x_bf16    [T][d_model] bf16, row-major, 16-byte aligned
  *   w_router  [n_experts][d_model] fp32, 16-byte aligned;  b_router [n_experts] fp32
  *   topk_idx  out [T][top_k] int32: selected expert ids, ascending per token

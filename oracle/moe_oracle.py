@@ -19,7 +19,7 @@ pages describe the layer:
      "Swish/SwiGLU", Fig. 6-7], width 2880 [model card config table], clamp
      limit swiglu_limit = 7 [model card raw config];
   5. expert weights in MXFP4: 4-bit values, one 8-bit scale per 32 values,
-     4.25 bits per parameter [ewbang.com walk-through, "Quantization"];
+     4.25 bits per parameter [gpt-oss architecture walk-through, "Quantization"];
      element and scale formats E2M1 / E8M0 per the OCP Microscaling v1.0
      specification;
   6. combine: the weighted sum of the selected experts' outputs.
