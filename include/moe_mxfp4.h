@@ -150,7 +150,7 @@ moe_status moe_route(const moe_dims* dims, int32_t T, const void* x_bf16, const 
  *   perm      out [T*top_k]: assignment id at each grouped position
  *   inv       out [T*top_k]: inv[perm[p]] = p
  *   tiles     out, moe_tile_table_bytes(dims, T) bytes, 16-byte aligned: the
- *             row-tile table: 8-row tiles when T*top_k <= 8*n_experts (48
+ *             row-tile table: 8-row tiles when T*top_k <= 6*n_experts (48
  *             int32 per slot), else 128-row tiles (132 int32 per slot).  A
  *             slot holds expert or -1, first grouped position, row count,
  *             number of tiles in use, then the assignment id of each row.

@@ -30,10 +30,10 @@ def run_gpu(layer, stream=None) -> dict:
 
 def check_tiles(tiles: np.ndarray, offsets: np.ndarray, perm: np.ndarray, n: int, E: int):
     """The row-tile table (include/moe_mxfp4.h): every expert's grouped rows cut into tiles of
-    8 rows (n <= 8E, 48 ints per slot) or 128 rows (132 ints per slot), in expert order; each slot
+    8 rows (n <= 6E, 48 ints per slot) or 128 rows (132 ints per slot), in expert order; each slot
     holds {expert, first position, rows, tiles in use} and the assignment id of every row; then
     empty slots (expert -1)."""
-    bm = 8 if n <= 8 * E else 128
+    bm = 8 if n <= 6 * E else 128
     ints = max(48, 4 + bm)
     slots = -(-n // bm) + min(E, n)
     t = tiles[: slots * ints].reshape(slots, ints)

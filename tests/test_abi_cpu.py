@@ -94,14 +94,16 @@ def test_bad_arguments_rejected_before_launch(L):
     assert L.moe_permute(d, 4, A, A, A, A, A, None, None) == M.MOE_EINVAL             # no tile table
     assert L.moe_permute(d, 4, A, A, A, A, A, A + 4, None) == M.MOE_EINVAL            # misaligned tiles
     assert L.moe_permute(d, 0, A, A, A, A, A, A, None) == M.MOE_OK
-    # tile table: 8-row tiles (48-int slots) at decode sizes, 128-row tiles (132-int slots) beyond
-    # 8 rows per expert on average
+    # tile table: 8-row tiles (48-int slots) up to 6 assignments per expert on average, 128-row
+    # tiles (132-int slots) beyond
     # followed by the grouping's scratch: [G][E] counts (G = ceil(n / 1024)) and E + 1 tile starts,
     # the whole rounded up to 16 bytes
     def table(n, E, bm, ints):
         words = (-(-n // bm) + min(E, n)) * ints + (-(-n // 1024)) * E + E + 1
         return -(-words // 4) * 16
     assert L.moe_tile_table_bytes(d, 32) == table(128, 32, 8, 48)
+    assert L.moe_tile_table_bytes(d, 48) == table(192, 32, 8, 48)         # 6 per expert: 8-row tiles
+    assert L.moe_tile_table_bytes(d, 49) == table(196, 32, 128, 132)      # past it: 128-row tiles
     assert L.moe_tile_table_bytes(d, 4096) == table(16384, 32, 128, 132)
     assert L.moe_tile_table_bytes(d, 4097) == table(16388, 32, 128, 132)
     assert L.moe_pack_act(96, 4, A, A, None) == M.MOE_EUNSUPPORTED

@@ -77,9 +77,9 @@ SMALL = {
     "one_expert": dict(cfg=dict(T=5, D=64, E=1, k=1, I=64, seed=60)),
     "top1_of_8": dict(cfg=dict(T=40, D=64, E=8, k=1, I=64, seed=61)),
     # size thresholds of the path, each met exactly and passed by one:
-    # 8-row tiles up to 8 assignments per expert (here 64 = 8 x 8), 128-row tiles past it
-    "decode_tiles_at_limit": dict(cfg=dict(T=32, D=64, E=8, k=2, I=64, seed=53)),
-    "prefill_tiles_past_limit": dict(cfg=dict(T=33, D=64, E=8, k=2, I=64, seed=54)),
+    # 8-row tiles up to 6 assignments per expert (here 48 = 6 x 8), 128-row tiles past it
+    "decode_tiles_at_limit": dict(cfg=dict(T=24, D=64, E=8, k=2, I=64, seed=53)),
+    "prefill_tiles_past_limit": dict(cfg=dict(T=25, D=64, E=8, k=2, I=64, seed=54)),
     # grouping in one 256-thread workgroup up to 256 assignments, one 1024-thread workgroup up
     # to 1024, three kernels past that
     "grouping_256_threads_at_limit": dict(cfg=dict(T=64, D=64, E=16, k=4, I=64, seed=58)),
