@@ -176,12 +176,15 @@ def cpu_baseline(inp, n_tokens):
     except Exception:
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     tokens = np.arange(min(n_tokens, inp.T))
-    t0 = time.perf_counter()
-    oracle.forward(inp, tokens=tokens)
+    # whole passes over the sample until about 10 s of CPU work (at most 4 passes)
+    passes, t0 = 0, time.perf_counter()
+    while passes < 4 and (passes == 0 or time.perf_counter() - t0 < 10.0):
+        oracle.forward(inp, tokens=tokens)
+        passes += 1
     dt = time.perf_counter() - t0
-    return dict(value=round(len(tokens) / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
+    return dict(value=round(passes * len(tokens) / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"float64 oracle, whole layer (routing of all {inp.T} tokens, experts and combine for "
-                       f"{len(tokens)} tokens), {dt:.1f} s")
+                       f"{len(tokens)} tokens), {passes} pass(es) in {dt:.1f} s")
 
 
 def main():
