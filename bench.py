@@ -194,8 +194,8 @@ def main():
     if args.stats_report:
         return stats_report(args)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
-                          "(the multi-GPU sharding is described in the design notes, not built)"}))
+        print(json.dumps({"error": "the MoE layer here runs on one GPU only: --gpus must be 1 "
+                          "(expert-parallel sharding over several GPUs is designed, not implemented)"}))
         sys.exit(2)
     import numpy as np
     import torch
