@@ -110,10 +110,12 @@ moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const u
   if (launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, tiles, wts->gu_codes, wts->gu_scales, nullptr, hpack,
                   stream, af))
     return MOE_EHIP;
+  // the down projection writes each row at its assignment index t*k + j, so the combine reads a
+  // token's rows directly (same values and sums as the step-by-step entry points)
   if (launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, tiles, wts->dn_codes, wts->dn_scales, w, yperm, stream,
-                  af))
+                  af, 1))
     return MOE_EHIP;
-  if (launch_combine(T, D, k, yperm, inv, residual, y, y_dtype == MOE_BF16, stream)) return MOE_EHIP;
+  if (launch_combine(T, D, k, yperm, nullptr, residual, y, y_dtype == MOE_BF16, stream)) return MOE_EHIP;
   return MOE_OK;
 }
 

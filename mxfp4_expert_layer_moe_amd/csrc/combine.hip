@@ -7,12 +7,16 @@
 // and sums them in fp32 in slot order (ascending expert id): no atomics, the
 // same bits on every run.  HBM-bound: reads k rows, writes one.  A thread owns 8
 // columns of a token and issues the index and row loads of 4 slots at a time, so
-// a token's gather costs two memory round trips per 4 slots.
+// a token's gather costs two memory round trips per 4 slots.  When the down
+// projection wrote the rows in assignment order (row t*k + j, the whole-layer
+// path), the rows are read directly: one round trip.
 //
 // With a residual (the MoE half of a pre-norm transformer block, y = x + MoE(xn):
 // the block's input and output are both [N x D], "gpt-oss architecture
 // walk-through", section "Transformer Blocks"), the bf16 residual row is added
 // to the slot-order sum with one more fp32 addition.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -20,7 +24,7 @@ namespace moe {
 constexpr int kCombineCols = 8;        // columns per thread: one 16-byte fp16 load per row
 constexpr int kCombineBatch = 4;       // slots whose index and row loads are issued together
 
-template <bool BF16_OUT, bool RESIDUAL>
+template <bool BF16_OUT, bool RESIDUAL, bool DIRECT>
 __global__ __launch_bounds__(256) void combine_kernel(int T, int D, int k, const _Float16* __restrict__ y_perm,
                                                       const int32_t* __restrict__ inv,
                                                       const uint16_t* __restrict__ residual, void* __restrict__ y) {
@@ -36,7 +40,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int D, int k, const
   for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
     int p[kCombineBatch];
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) p[u] = j0 + u < k ? inv[(size_t)t * k + j0 + u] : 0;
+    for (int u = 0; u < kCombineBatch; ++u)
+      p[u] = j0 + u >= k ? 0 : DIRECT ? t * k + j0 + u : inv[(size_t)t * k + j0 + u];
     h8 v[kCombineBatch];
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u)
@@ -75,13 +80,18 @@ hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int
   const long long n = (long long)T * (D / kCombineCols);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
-  if (residual) {
-    if (y_bf16) combine_kernel<true, true><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, residual, y);
-    else combine_kernel<false, true><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, residual, y);
-  } else {
-    if (y_bf16) combine_kernel<true, false><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, nullptr, y);
-    else combine_kernel<false, false><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, nullptr, y);
-  }
+  auto go = [&](auto direct) {
+    constexpr bool DIRECT = decltype(direct)::value;
+    if (residual) {
+      if (y_bf16) combine_kernel<true, true, DIRECT><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, residual, y);
+      else combine_kernel<false, true, DIRECT><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, residual, y);
+    } else {
+      if (y_bf16) combine_kernel<true, false, DIRECT><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, nullptr, y);
+      else combine_kernel<false, false, DIRECT><<<grid, block, 0, s>>>(T, D, k, y_perm, inv, nullptr, y);
+    }
+  };
+  if (inv) go(std::false_type{});
+  else go(std::true_type{});
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ namespace moe {
 
 struct GemmArgs {
   int T, k, E, K, KT, KG, units, out_K;
+  int out_assign;                                       // down: rows to their assignment index
   float limit;
   const uint8_t* a_packed;
   const int32_t* tiles;
@@ -90,7 +91,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   if (tid < nrows) srow[tid] = STAGE == 0 ? tile[4 + tid] / g.k : p0 + tid;
   // down: each row's gate weight topk_w[perm[p]], fetched now so it is there for the epilogue
   float wl = 0.0f;
-  if (STAGE == 1 && valid) wl = g.topk_w[tile[4 + i]];
+  int al = 0;
+  if (STAGE == 1 && valid) {
+    al = tile[4 + i];
+    wl = g.topk_w[al];
+  }
 
   // K chunk staged at once: everything if it fits, else a multiple of the prefetch depth
   int KC = KTC > 0 ? KTC : g.KT;
@@ -299,9 +304,10 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
       if (8 * (r >> 2) >= nrows) break;
       const int m = 8 * (r >> 2) + 4 * half + (r & 3);
       const float wm = __shfl(wl, m);
+      const int orow = g.out_assign ? __shfl(al, m) : p0 + m;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        if (m < nrows) out[(size_t)(p0 + m) * D + (size_t)(NB * u + nb) * kNTile + (lane & 31)] = (_Float16)(acc[nb][r] * wm);
+        if (m < nrows) out[(size_t)orow * D + (size_t)(NB * u + nb) * kNTile + (lane & 31)] = (_Float16)(acc[nb][r] * wm);
     }
   }
 }
@@ -321,10 +327,11 @@ constexpr int kDownP = MOE_DECODE_DOWN_P;     // and k-tiles in flight
 
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
-                       void* out, hipStream_t s, int af) {
+                       void* out, hipStream_t s, int af, int out_assign) {
   if (T == 0) return hipSuccess;
   GemmArgs g;
   g.T = T; g.k = k; g.E = E; g.limit = limit;
+  g.out_assign = stage == 1 && out_assign;
   g.a_packed = a_packed; g.tiles = tiles; g.codes = codes; g.scales = scales;
   g.topk_w = topk_w; g.out = out;
   const int N = stage == 0 ? 2 * I : D;
@@ -338,7 +345,8 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   const long long n_assign = (long long)T * k;
   // batches with many rows per expert (128-row tiles) go to the prefill kernel
   if (tile_rows(n_assign, E) != 8)
-    return launch_gemm_prefill(stage, T, D, I, E, k, limit, a_packed, tiles, codes, scales, topk_w, out, s, af);
+    return launch_gemm_prefill(stage, T, D, I, E, k, limit, a_packed, tiles, codes, scales, topk_w, out, s, af,
+                               out_assign);
   // decode-sized batches (8-row tiles whose activations fit LDS whole)
   const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));
   // the model's K = 2880 (45 k-tiles): fully unrolled k-loop

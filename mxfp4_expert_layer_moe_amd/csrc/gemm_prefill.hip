@@ -39,6 +39,7 @@ namespace moe {
 
 struct PrefillArgs {
   int k, KT, KG, nt, ngroups, out_K;
+  int out_assign;                                        // down: rows to their assignment index
   float limit;
   const uint8_t* a_packed;
   uint32_t a_bytes, arb;
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   __shared__ __attribute__((aligned(16))) uint8_t sA[kPSlots * kPSlotBytes];
   __shared__ int srow[kPrefillRows];
   __shared__ float sgate[kPrefillRows];
+  __shared__ int sdst[kPrefillRows];                     // down: output row of each tile row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -365,7 +367,10 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     }
   } else {
     // ---- down: scale row p by its gate weight, fp16, transpose through LDS, 16-byte row stores --
-    if (tid < kPrefillRows) sgate[tid] = wrow;
+    if (tid < kPrefillRows) {
+      sgate[tid] = wrow;
+      sdst[tid] = g.out_assign ? a_id : p0 + tid;
+    }
     __syncthreads();
     const int D = g.out_K;
     uint8_t* out = reinterpret_cast<uint8_t*>(g.out);
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
         const uint4 v = *reinterpret_cast<const uint4*>(ep + row * kPOutStride + c8);
         const int m = rb * 32 + row;
         if (m < nrows && c0 + c8 < D)
-          *reinterpret_cast<uint4*>(out + ((size_t)(p0 + m) * D + c0 + c8) * 2) = v;
+          *reinterpret_cast<uint4*>(out + ((size_t)sdst[m] * D + c0 + c8) * 2) = v;
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -415,8 +420,10 @@ constexpr int kPP = MOE_PREFILL_P;
 
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
-                               const uint8_t* scales, const float* topk_w, void* out, hipStream_t s, int af) {
+                               const uint8_t* scales, const float* topk_w, void* out, hipStream_t s, int af,
+                               int out_assign) {
   PrefillArgs g;
+  g.out_assign = stage == 1 && out_assign;
   const int K = stage == 0 ? D : I;
   const int N = stage == 0 ? 2 * I : D;
   g.k = k;
