@@ -228,7 +228,10 @@ moe_status moe_rmsnorm(const moe_dims* dims, int32_t T, const void* x_bf16, cons
 
 /*
  * The whole layer: route -> permute -> pack x -> gate/up + SwiGLU -> down ->
- * combine, enqueued on `stream` with no host synchronisation.
+ * combine, enqueued on `stream` with no host synchronisation.  y has the same
+ * bits as the step-by-step entry points above give on the same inputs.  (Inside
+ * the workspace the down stage writes each row at its assignment t*top_k + j
+ * rather than at its permuted position, so the combine needs no inverse lookup.)
  *   ws / ws_bytes: device scratch of at least moe_workspace_bytes(dims, T)
  *   bytes, 256-byte aligned; its contents are undefined after the call.
  */
