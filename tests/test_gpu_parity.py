@@ -87,6 +87,8 @@ SMALL = {
     "grouping_one_workgroup_at_limit": dict(cfg=dict(T=256, D=64, E=16, k=4, I=64, seed=55)),
     "grouping_three_kernels_past_limit": dict(cfg=dict(T=257, D=64, E=16, k=4, I=64, seed=56)),
     # the one-workgroup selection takes at most 32 tokens and 32 experts
+    "selection_one_workgroup_at_limit": dict(cfg=dict(T=32, D=64, E=32, k=4, I=64, seed=62)),
+    "tokens_33_general_selection": dict(cfg=dict(T=33, D=64, E=32, k=4, I=64, seed=63)),
     "experts_33_general_selection": dict(cfg=dict(T=32, D=64, E=33, k=4, I=64, seed=57)),
 }
 
