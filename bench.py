@@ -100,23 +100,23 @@ def _per_dispatch(rows, counter: str):
     return dict(sorted(out.items()))
 
 
-def traffic_report(args):
+def traffic_record(fetch_dir: str, write_dir: str, copy_mib: int, config: int, command: str = "") -> dict:
     """Gate/up kernel HBM bytes per launch, each counter scaled by what it reads for a plain copy.
 
-    FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  The last three copyBuffer dispatches
-    of each run are the --copy-mib calibration copies (read and write copy_mib MiB each).
+    FETCH_SIZE and WRITE_SIZE are in KiB per dispatch (summed over the rows rocprofv3 writes for
+    one dispatch).  The last three copyBuffer dispatches of each run are the --copy-mib
+    calibration copies (read and write copy_mib MiB each).
     """
-    cfg = dict(__import__("synth").CONFIGS[args.config])
-    known = args.copy_mib * 2 ** 20
+    cfg = dict(__import__("synth").CONFIGS[config])
+    known = copy_mib * 2 ** 20
     if known <= 0:
         raise SystemExit("--traffic-report needs the --copy-mib the runs used")
     rec = {"workload": workload_name(cfg),
            "kernel": "expert_gemm_kernel<0> (gate/up + SwiGLU)",
            "kernel_source_sha256_16": gemm_source_hash(),
-           "command": args.command}
+           "command": command}
     total = 0.0
-    for key, d, counter in (("fetch", args.traffic_report[0], "FETCH_SIZE"),
-                            ("write", args.traffic_report[1], "WRITE_SIZE")):
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         per = _per_dispatch(_counter_rows(d), counter)
         gu = [v for n, v in per.values() if n.startswith(GU_KERNEL_PREFIX) and n.endswith(GU_KERNEL_BF16_SUFFIX)]
         cp = [v for n, v in per.values() if n.startswith(COPY_KERNEL)][-3:]
@@ -132,6 +132,12 @@ def traffic_report(args):
         total += kib * 1024.0 * factor
     rec["copy_bytes_each_way"] = known
     rec["hbm_bytes_per_launch"] = int(total)
+    return rec
+
+
+def traffic_report(args):
+    """Write the traffic record of two counter runs to profiles/gate_up_gemm_traffic.json."""
+    rec = traffic_record(args.traffic_report[0], args.traffic_report[1], args.copy_mib, args.config, args.command)
     path = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
