@@ -50,6 +50,8 @@ def parse():
                         "(FETCH_SIZE, WRITE_SIZE) of this script with --copy-mib, then exit")
     p.add_argument("--stats-report", nargs=2, metavar=("STATS_CSV", "OUT_TXT"),
                    help="summarise a rocprofv3 --stats kernel table as text, then exit")
+    p.add_argument("--pmc-report", nargs=2, metavar=("PMC_DIR", "OUT_TXT"),
+                   help="summarise a rocprofv3 --pmc --kernel-trace run (per-kernel counters, clock, MFMA rate)")
     p.add_argument("--command", default="", help="the command that made the profile (for the reports)")
     p.add_argument("--no-block", action="store_true", help="skip the timing of the pre-norm block forward")
     p.add_argument("--no-act4", action="store_true", help="skip the timing of the MXFP4-activation variant")
@@ -162,6 +164,64 @@ def stats_report(args):
     print("\n".join(lines))
 
 
+def pmc_summary(d: str) -> list:
+    """Per kernel of a rocprofv3 --pmc --kernel-trace run: dispatches, mean duration, the mean of
+    each counter per dispatch, and two derived figures when their counters are there:
+    SQ_INSTS_VALU_MFMA_MOPS_F6F4 x 512 / duration (FP4/FP6 matrix FLOP/s executed, the counter
+    being in units of 512 operations: 256 per 32x32x64 instruction) and
+    SQ_VALU_MFMA_BUSY_CYCLES / 1024 (matrix-pipe busy cycles per SIMD: the counter sums all
+    256 compute units x 4 SIMDs)."""
+    import csv
+    import glob
+    rows = _counter_rows(d)
+    traces = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    dur = {}
+    for f in traces:
+        for r in csv.DictReader(open(f)):
+            dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    per = {}                                   # kernel -> dispatch -> counter -> summed value
+    for r in rows:
+        k = per.setdefault(r["Kernel_Name"], {}).setdefault(int(r["Dispatch_Id"]), {})
+        k[r["Counter_Name"]] = k.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = []
+    for name, ds in per.items():
+        counters = sorted({c for v in ds.values() for c in v})
+        mean = {c: sum(v.get(c, 0.0) for v in ds.values()) / len(ds) for c in counters}
+        secs = [dur[i] for i in ds if i in dur]
+        rec = dict(kernel=name, dispatches=len(ds), counters=mean)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            rec["mfma_busy_cycles_per_simd"] = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024
+        if secs:
+            t = sum(secs) / len(secs)
+            rec["mean_us"] = t * 1e6
+            if "SQ_INSTS_VALU_MFMA_MOPS_F6F4" in mean:
+                rec["mfma_f6f4_TFLOP_per_s"] = mean["SQ_INSTS_VALU_MFMA_MOPS_F6F4"] * 512 / t * 1e-12
+        out.append(rec)
+    return sorted(out, key=lambda r: -r.get("mean_us", 0.0))
+
+
+def pmc_report(args):
+    recs = pmc_summary(args.pmc_report[0])
+    lines = ["# rocprofv3 --pmc counter summary (mean per dispatch)",
+             f"# command: {args.command}" if args.command else "# command: (not given)"]
+    for r in recs:
+        if not any(k in r["kernel"] for k in ("expert_gemm", "route", "combine", "permute", "rmsnorm", "pack")):
+            continue
+        head = f"{r['kernel']}  dispatches={r['dispatches']}"
+        if "mean_us" in r:
+            head += f"  mean={r['mean_us']:.2f} us"
+        if r.get("mfma_f6f4_TFLOP_per_s"):
+            head += f"  F6F4 MFMA executed={r['mfma_f6f4_TFLOP_per_s']:.1f} TFLOP/s"
+        if r.get("mfma_busy_cycles_per_simd"):
+            head += f"  MFMA busy={r['mfma_busy_cycles_per_simd']:.4g} cycles/SIMD"
+        lines.append(head)
+        for c, v in r["counters"].items():
+            lines.append(f"    {c:<36} {v:.6g}")
+    with open(args.pmc_report[1], "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_for(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
@@ -199,6 +259,8 @@ def main():
         return traffic_report(args)
     if args.stats_report:
         return stats_report(args)
+    if args.pmc_report:
+        return pmc_report(args)
     if args.gpus != 1:
         print(json.dumps({"error": "the MoE layer here runs on one GPU only: --gpus must be 1 "
                           "(expert-parallel sharding over several GPUs is designed, not implemented)"}))

@@ -72,3 +72,30 @@ def test_traffic_is_reported_only_for_the_source_it_was_measured_on(monkeypatch)
     assert bench.traffic_for(rec["workload"] + " (other)") is None
     monkeypatch.setattr(bench, "gemm_source_hash", lambda: "0" * 16)
     assert bench.traffic_for(rec["workload"]) is None
+
+
+def test_pmc_summary_means_per_dispatch_and_derives_the_matrix_rate(tmp_path):
+    d = tmp_path / "p"
+    os.makedirs(d)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        # two dispatches of one kernel; dispatch 1's MOPS split over two rows
+        for i, mops, busy in ((1, 1000.0, 2048.0), (2, 3000.0, 4096.0)):
+            w.writerow(dict(Dispatch_Id=i, Kernel_Name=GU_BF16, Counter_Name="SQ_INSTS_VALU_MFMA_MOPS_F6F4",
+                            Counter_Value=mops / 2))
+            w.writerow(dict(Dispatch_Id=i, Kernel_Name=GU_BF16, Counter_Name="SQ_INSTS_VALU_MFMA_MOPS_F6F4",
+                            Counter_Value=mops / 2))
+            w.writerow(dict(Dispatch_Id=i, Kernel_Name=GU_BF16, Counter_Name="SQ_VALU_MFMA_BUSY_CYCLES",
+                            Counter_Value=busy))
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerow(dict(Dispatch_Id=1, Kernel_Name=GU_BF16, Start_Timestamp=0, End_Timestamp=1000))
+        w.writerow(dict(Dispatch_Id=2, Kernel_Name=GU_BF16, Start_Timestamp=5000, End_Timestamp=8000))
+    (r,) = bench.pmc_summary(str(d))
+    assert r["dispatches"] == 2
+    assert r["counters"]["SQ_INSTS_VALU_MFMA_MOPS_F6F4"] == 2000.0
+    assert abs(r["mean_us"] - 2.0) < 1e-9                                  # (1 + 3) us / 2
+    assert abs(r["mfma_f6f4_TFLOP_per_s"] - 2000.0 * 512 / 2e-6 * 1e-12) < 1e-9
+    assert r["mfma_busy_cycles_per_simd"] == 3072.0 / 1024
