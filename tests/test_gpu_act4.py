@@ -103,13 +103,18 @@ SMALL = {
     "single_token": dict(cfg=dict(T=1, D=128, E=8, k=4, I=128, seed=40)),
     "multi_tile": dict(cfg=dict(T=200, D=256, E=8, k=2, I=512, seed=46)),
     "k_tail_groups": dict(cfg=dict(T=70, D=320, E=4, k=2, I=448, seed=47)),
+    # 8-row tiles up to 6 assignments per expert (48 = 6 x 8), 128-row tiles past it
+    "decode_tiles_at_limit": dict(cfg=dict(T=24, D=64, E=8, k=2, I=64, seed=53)),
+    "prefill_tiles_past_limit": dict(cfg=dict(T=25, D=64, E=8, k=2, I=64, seed=54)),
+    # pre-activations far past the clamp, and MXFP4 block scales well above 2^0
+    "large_activations_x8": dict(cfg=dict(T=24, D=128, E=8, k=2, I=128, seed=52), x_scale=8.0),
 }
 
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_act4_small_case_parity(name):
     c = SMALL[name]
-    _act4_check(name, synth.make_inputs(c["cfg"]))
+    _act4_check(name, synth.make_inputs(c["cfg"], x_scale=c.get("x_scale", 1.0)))
 
 
 @pytest.mark.parametrize("cfg,n_tokens", [(1, None), (2, 32), (3, 32)])
