@@ -116,6 +116,9 @@ def test_bad_arguments_rejected_before_launch(L):
     assert L.moe_expert_gemm_mxfp4(d, 0, M.MOE_STAGE_GATE_UP, A, A, A, A, None, A, None) == M.MOE_OK
     assert L.moe_combine(d, 4, A, A, A, 5, None) == M.MOE_EINVAL
     assert L.moe_combine(d, 4, A, A, A + 4, M.MOE_FP32, None) == M.MOE_EINVAL
+    # the inverse permutation is required: only the whole-layer path reads rows without it
+    assert L.moe_combine(d, 4, A, None, A, M.MOE_FP32, None) == M.MOE_EINVAL
+    assert L.moe_combine_residual(d, 4, A, None, A, A, M.MOE_FP32, None) == M.MOE_EINVAL
     w = M.moe_weights(A, A, A, A)
     need = L.moe_workspace_bytes(d, 4)
     assert L.moe_forward(d, 4, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, need - 1, None) == M.MOE_EWORKSPACE
