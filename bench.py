@@ -3,15 +3,30 @@
 
 One step = one pass of the whole layer (route, permute, activation split,
 gate/up GEMM + SwiGLU, down GEMM, combine) over one batch of synthetic tokens,
-through ``moe_forward``.  The default workload is the gpt-oss-20b MoE layer at
-decode: T=32 tokens, d_model = d_ff = 2880, 32 experts, top-4.  Steps rotate
-over L distinct device copies of the layer's weights (default 24, one decode
-step through every layer of the 20b model: 10.2 GB) so each step streams its
-weights from HBM rather than from the 256 MB last-level cache.
+through ``moe_forward``, inputs resident in HBM.
 
-Prints one JSON line.  ``value`` is tokens/s of the layer; ``roofline`` is the
-dominant kernel (the gate/up expert GEMM) launched back to back on its stream,
-between two HIP events; ``cpu_baseline`` is the float64 oracle on the host on a bounded sample.
+The headline is the largest workload: the gpt-oss-120b MoE layer with skewed
+routing, T=8192 tokens, d_model = d_ff = 2880, 128 experts, top-4 (a Zipf
+router bias: 10% of the experts take about half of the assignments, 4 take
+none).  The 20b decode (T=32), 20b prefill (T=4096) and 120b (T=4096)
+workloads are measured first, each as a sub-record of the same line with its
+own warm-up and step counts; the headline then runs exactly --warmup W untimed
+and --steps K timed steps.  Steps rotate over L device copies of the layer's
+weights (24 at decode, one decode step through every layer of the 20b model,
+10.2 GB; 2 otherwise) so weights stream from HBM, not the 256 MB last-level
+cache.
+
+Every record carries tokens/s, TFLOP/s and GB/s of the algorithmic work and the
+fractions R_HBM (of 8 TB/s), R_MXFP4 (of the 10.1 PFLOP/s dense FP4/FP6 matrix
+peak) and R_roof (the time the roofline allows over the measured time, with the
+matrix peak of the instruction mix the path issues: two FP6 x FP4 instructions
+per weight tile), each against the published peaks and against the peaks the
+probes of libmoe_peaks.so measure on the same GPU at the start of the run.
+
+Prints one JSON line.  ``roofline`` is the headline's dominant kernel (the
+gate/up expert GEMM) launched back to back on its stream between two HIP
+events; ``cpu_baseline`` is the float64 oracle on the host on a bounded sample
+of the headline workload, on all threads and on one.
 """
 from __future__ import annotations
 
@@ -26,18 +41,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix, published
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 / MXFP6 matrix, published
 EXPERT_BYTES_PER_PARAM = 17.0 / 32.0       # MXFP4: 4.25 bits
+HEADLINE = 4                   # the largest workload: gpt-oss-120b, skewed routing, T=8192
+SUB_RECORDS = (1, 2, 3)
+# instruction mix of each path: matrix instructions per 32x32x64 weight tile and their format pair
+MIX = {"default": dict(per_tile=2, fmt="fp6xfp4", what="two FP6 x FP4 instructions per weight tile "
+                                                       "(bf16 activations as hi + lo FP6 terms)"),
+       "act4": dict(per_tile=1, fmt="fp4xfp4", what="one FP4 x FP4 instruction per weight tile")}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps of the headline (default: 200 at decode sizes, 30 otherwise)")
     p.add_argument("--warmup", type=int, default=None,
-                   help="untimed steps before each timed region (default: about 0.2 s of steps for the "
-                        "workload, so the GPU clock has settled: 2000 decode steps, 300 prefill steps)")
-    p.add_argument("--config", type=int, default=1, help="workload index (1 = gpt-oss-20b decode)")
+                   help="untimed steps before the headline's timed region (default: about 0.2 s of steps "
+                        "for the workload, so the GPU clock has settled: 2000 decode steps, 300 prefill steps)")
+    p.add_argument("--config", type=int, default=HEADLINE, help="headline workload index (4 = gpt-oss-120b skewed)")
+    p.add_argument("--only", action="store_true", help="the headline workload only, no sub-records (profiling)")
+    p.add_argument("--no-peaks", action="store_true", help="skip the ceiling probes (fractions against spec only)")
     p.add_argument("--layers", type=int, default=None, help="distinct weight copies to rotate over")
     p.add_argument("--kernel-steps", type=int, default=None, help="launches of the dominant kernel to time")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -46,8 +70,8 @@ def parse():
                    help="after the measurements, run 3 plain device-to-device copies of this many MiB "
                         "(the calibration of the HBM byte counters)")
     p.add_argument("--traffic-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                   help="write the gate/up kernel's HBM traffic from two rocprofv3 --pmc runs "
-                        "(FETCH_SIZE, WRITE_SIZE) of this script with --copy-mib, then exit")
+                   help="write the --config workload's gate/up kernel HBM traffic from two rocprofv3 --pmc "
+                        "runs (FETCH_SIZE, WRITE_SIZE) of this script with --copy-mib, then exit")
     p.add_argument("--stats-report", nargs=2, metavar=("STATS_CSV", "OUT_TXT"),
                    help="summarise a rocprofv3 --stats kernel table as text, then exit")
     p.add_argument("--pmc-report", nargs=2, metavar=("PMC_DIR", "OUT_TXT"),
@@ -63,18 +87,35 @@ def workload_name(cfg: dict) -> str:
             f"{cfg['E']} experts, top-{cfg['k']}, MXFP4 experts, bf16 activations")
 
 
-# the decode GEMM kernel and the headers whose device code it compiles
-GEMM_SRCS = [os.path.join(ROOT, "mxfp4_expert_layer_moe_amd", "csrc", f)
-             for f in ("gemm.hip", "mfma_ops.h", "moe_internal.h")]
+# the gate/up GEMM kernels and the sources whose device code they compile: the small-batch kernel
+# (8-row tiles, decode) and the large-batch kernel (128-row tiles, prefill)
+CSRC = os.path.join(ROOT, "mxfp4_expert_layer_moe_amd", "csrc")
+GEMM_SRCS = {"decode": [os.path.join(CSRC, f) for f in ("gemm.hip", "mfma_ops.h", "moe_internal.h")],
+             "prefill": [os.path.join(CSRC, f) for f in ("gemm_prefill.hip", "mfma_ops.h", "moe_internal.h")]}
+GU_KERNEL = {"decode": ("void moe::expert_gemm_kernel<0,", ", 0>(moe::GemmArgs)"),
+             "prefill": ("void moe::expert_gemm_prefill_kernel<0,", ", 0>(moe::PrefillArgs)")}
+KERNEL_LABEL = {"decode": "expert_gemm_kernel<0> (gate/up + SwiGLU, 8-row tiles)",
+                "prefill": "expert_gemm_prefill_kernel<0> (gate/up + SwiGLU, 128-row tiles)"}
 
 
-def gemm_source_hash() -> str:
+def gemm_kind(cfg: dict) -> str:
+    """Which gate/up kernel the workload runs (the library's tile-height rule: 8-row tiles up to 6
+    assignments per expert on average)."""
+    return "decode" if cfg["T"] * cfg["k"] <= 6 * cfg["E"] else "prefill"
+
+
+def gemm_source_hash(kind: str = "decode") -> str:
     h = hashlib.sha256()
-    for f in GEMM_SRCS:
+    for f in GEMM_SRCS[kind]:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
-GU_KERNEL_PREFIX = "void moe::expert_gemm_kernel<0,"
-GU_KERNEL_BF16_SUFFIX = ", 0>(moe::GemmArgs)"     # last template argument: bf16 (split FP6) activations
+
+
+def traffic_path(cfg: dict) -> str:
+    slug = cfg["name"].replace(" ", "_")
+    return os.path.join(ROOT, "profiles", f"gate_up_gemm_traffic_{slug}_T{cfg['T']}.json")
+
+
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -110,17 +151,19 @@ def traffic_record(fetch_dir: str, write_dir: str, copy_mib: int, config: int, c
     calibration copies (read and write copy_mib MiB each).
     """
     cfg = dict(__import__("synth").CONFIGS[config])
+    kind = gemm_kind(cfg)
+    prefix, suffix = GU_KERNEL[kind]
     known = copy_mib * 2 ** 20
     if known <= 0:
         raise SystemExit("--traffic-report needs the --copy-mib the runs used")
     rec = {"workload": workload_name(cfg),
-           "kernel": "expert_gemm_kernel<0> (gate/up + SwiGLU)",
-           "kernel_source_sha256_16": gemm_source_hash(),
+           "kernel": KERNEL_LABEL[kind],
+           "kernel_source_sha256_16": gemm_source_hash(kind),
            "command": command}
     total = 0.0
     for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         per = _per_dispatch(_counter_rows(d), counter)
-        gu = [v for n, v in per.values() if n.startswith(GU_KERNEL_PREFIX) and n.endswith(GU_KERNEL_BF16_SUFFIX)]
+        gu = [v for n, v in per.values() if n.startswith(prefix) and n.endswith(suffix)]
         cp = [v for n, v in per.values() if n.startswith(COPY_KERNEL)][-3:]
         if not gu or len(cp) < 3:
             raise SystemExit(f"{d}: {len(gu)} gate/up dispatches, {len(cp)} calibration copies")
@@ -138,9 +181,9 @@ def traffic_record(fetch_dir: str, write_dir: str, copy_mib: int, config: int, c
 
 
 def traffic_report(args):
-    """Write the traffic record of two counter runs to profiles/gate_up_gemm_traffic.json."""
+    """Write the traffic record of two counter runs to profiles/gate_up_gemm_traffic_<workload>.json."""
     rec = traffic_record(args.traffic_report[0], args.traffic_report[1], args.copy_mib, args.config, args.command)
-    path = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
+    path = traffic_path(__import__("synth").CONFIGS[args.config])
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -222,35 +265,185 @@ def pmc_report(args):
     print("\n".join(lines))
 
 
-def traffic_for(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
+def traffic_for(cfg: dict):
+    """HBM bytes per launch of the workload's gate/up kernel from committed rocprofv3 counter runs,
+    if they were taken on this kernel source."""
+    path = traffic_path(cfg)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256_16") != gemm_source_hash() or rec.get("workload") != workload:
+    if rec.get("kernel_source_sha256_16") != gemm_source_hash(gemm_kind(cfg)) or \
+            rec.get("workload") != workload_name(cfg):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, n_tokens):
+    """The float64 oracle on the host on a bounded sample of the workload: routing of every token,
+    experts and combine for the first n_tokens tokens.  Timed on all the threads numpy's BLAS uses
+    and again on one."""
     import numpy as np
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:
+    except Exception:                           # pragma: no cover - threadpoolctl is installed
+        threadpool_limits = None
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     tokens = np.arange(min(n_tokens, inp.T))
-    # whole passes over the sample until about 10 s of CPU work (at most 4 passes)
-    passes, t0 = 0, time.perf_counter()
-    while passes < 4 and (passes == 0 or time.perf_counter() - t0 < 10.0):
+
+    def timed():
+        t0 = time.perf_counter()
         oracle.forward(inp, tokens=tokens)
-        passes += 1
-    dt = time.perf_counter() - t0
-    return dict(value=round(passes * len(tokens) / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"float64 oracle, whole layer (routing of all {inp.T} tokens, experts and combine for "
-                       f"{len(tokens)} tokens), {passes} pass(es) in {dt:.1f} s")
+        return time.perf_counter() - t0
+    dt = timed()
+    rec = dict(value=round(len(tokens) / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
+               sample=f"float64 oracle on the headline workload: routing of all {inp.T} tokens, experts and "
+                      f"combine for {len(tokens)} tokens, one pass in {dt:.1f} s on {cores} threads",
+               nproc=os.cpu_count(), cpu_model=cpu_model())
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1 = timed()
+        rec["value_1_thread"] = round(len(tokens) / d1, 3)
+        rec["seconds_1_thread"] = round(d1, 1)
+    return rec
+
+
+def fractions(flops: float, nbytes: float, secs: float, peaks: dict | None, mix: str) -> dict:
+    """R_HBM, R_MXFP4 and R_roof of work (flops, bytes) done in secs, against the published peaks and
+    the measured ones.  R_roof = max(bytes / BW, flops / P_mix) / secs, where P_mix is the matrix rate
+    of the path's format pair divided by its instructions per weight tile."""
+    m = MIX[mix]
+    out = {"instruction_mix": m["what"]}
+    sides = [("spec", HBM_PEAK_GBS, FP4_PEAK_TFLOPS, FP4_PEAK_TFLOPS)]
+    if peaks:
+        sides.append(("measured", peaks["stream_read_nt_GB_per_s"], peaks["mfma_fp4xfp4_TFLOP_per_s"],
+                      peaks[f"mfma_{m['fmt']}_TFLOP_per_s"]))
+    for side, bw, p4, pfmt in sides:
+        bw_b, p4_f, pmix_f = bw * 1e9, p4 * 1e12, pfmt * 1e12 / m["per_tile"]
+        t_roof = max(nbytes / bw_b, flops / pmix_f)
+        out[side] = dict(R_HBM=round(nbytes / secs / bw_b, 4), R_MXFP4=round(flops / secs / p4_f, 4),
+                         R_roof=round(t_roof / secs, 4),
+                         roof_bound="hbm" if nbytes / bw_b >= flops / pmix_f else "mfma",
+                         peaks=dict(hbm_GB_per_s=bw, mxfp4_TFLOP_per_s=p4,
+                                    instruction_mix_TFLOP_per_s=round(pfmt / m["per_tile"], 1)))
+    return out
+
+
+def _time_steps(fn, copies, warmup: int, steps: int) -> float:
+    """ms per call of fn(weights) over `steps` calls after `warmup` untimed ones, HIP events on the
+    current stream (the calls run back to back on it), weight copies rotated."""
+    import torch
+    stream = torch.cuda.current_stream()
+    L = len(copies)
+    for s in range(warmup):
+        fn(copies[s % L])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for s in range(steps):
+        fn(copies[s % L])
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def default_counts(ci: int):
+    """(warm-up, timed steps) of a workload: about 0.2 s of warm-up so the clock has settled."""
+    decode = synth_configs()[ci]["T"] <= 64
+    return (2000, 200) if decode else ((20, 20) if ci == 0 else (300, 30))
+
+
+def synth_configs():
+    import synth
+    return synth.CONFIGS
+
+
+class Workload:
+    """A workload's inputs on the device, its weight copies and its algorithmic work."""
+
+    def __init__(self, ci: int, layers: int | None):
+        import synth
+        from mxfp4_expert_layer_moe_amd.device import DeviceLayer
+        self.ci = ci
+        self.cfg = dict(synth.CONFIGS[ci])
+        t0 = time.time()
+        self.inp = synth.make_inputs(ci)
+        self.layer = DeviceLayer(self.inp)
+        self.L = layers or (24 if self.cfg["T"] <= 64 else 2)
+        self.copies = [self.layer.weights] + [self.layer.weights.clone() for _ in range(self.L - 1)]
+        print(f"[bench] workload {ci} ({self.cfg['name']}, T={self.cfg['T']}) ready in {time.time() - t0:.1f}s",
+              file=sys.stderr, flush=True)
+
+    def measure(self, warmup: int, steps: int, peaks: dict | None, block: bool = True, act4: bool = True,
+                kernel_steps: int | None = None) -> dict:
+        import torch
+        inp, layer, copies = self.inp, self.layer, self.copies
+        T, D, E, k, I = inp.T, inp.D, inp.E, inp.k, inp.I
+        t0 = time.perf_counter()
+        ms = _time_steps(lambda w: layer.forward(weights=w), copies, warmup, steps)
+        wall = time.perf_counter() - t0
+        layer.route(logits=False)
+        layer.permute()
+        layer.pack_x()
+        torch.cuda.synchronize()
+        touched = int((layer.counts.cpu().numpy() > 0).sum())
+        flops = T * k * (2 * D * 2 * I + 2 * I * D) + 2 * T * D * E
+        nbytes = touched * 3 * D * I * EXPERT_BYTES_PER_PARAM + T * D * 2 * 2 + E * D * 4
+        secs = ms * 1e-3
+        rec = {"workload": workload_name(self.cfg), "tokens_per_step": T, "experts_touched": touched,
+               "weight_copies_rotated": self.L, "warmup": warmup, "steps": steps,
+               "ms_per_step": round(ms, 5), "tokens_per_s": round(T / secs, 1),
+               "TFLOP_per_s": round(flops / secs / 1e12, 2), "GB_per_s": round(nbytes / secs / 1e9, 1),
+               "alg_flops": int(flops), "alg_bytes": int(nbytes), "wall_s_timed": round(wall, 3),
+               "fractions": fractions(flops, nbytes, secs, peaks, "default")}
+        # the dominant kernel alone: the gate/up expert GEMM, launched back to back
+        kind = gemm_kind(self.cfg)
+        k_ms = _time_steps(lambda w: layer.gate_up(weights=w), copies, warmup, kernel_steps or steps)
+        gu_bytes = touched * 2 * I * D * EXPERT_BYTES_PER_PARAM + T * D * 2 + T * k * I * 2
+        gu_flops = 2.0 * T * k * D * 2 * I
+        ks = k_ms * 1e-3
+        fr = fractions(gu_flops, gu_bytes, ks, peaks, "default")
+        bound = fr["spec"]["roof_bound"]
+        if bound == "hbm":
+            achieved = gu_bytes / ks / 1e9
+            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4))
+        else:
+            achieved = gu_flops / ks / 1e12
+            roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP4_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / FP4_PEAK_TFLOPS, 4))
+        roof["traffic"] = traffic_for(self.cfg)
+        roof.update(kernel=KERNEL_LABEL[kind], kernel_ms=round(k_ms, 5), alg_bytes_per_launch=int(gu_bytes),
+                    alg_flops_per_launch=int(gu_flops), fractions=fr)
+        rec["gate_up_kernel"] = roof
+        if block:
+            b_ms = _time_steps(lambda w: layer.block_forward(weights=w), copies, warmup, steps)
+            rec["block"] = {"what": "RMSNorm -> MoE layer -> residual add (moe_block_forward)",
+                            "ms_per_step": round(b_ms, 5), "tokens_per_s": round(T / (b_ms * 1e-3), 1),
+                            "extra_ms_over_layer": round(b_ms - ms, 5)}
+        if act4:
+            a_ms = _time_steps(lambda w: layer.forward_act4(weights=w), copies, warmup, steps)
+            rec["act4"] = {"what": "MXFP4 activations into the expert GEMMs (moe_forward_act4; a lower-precision "
+                                   "contract)", "ms_per_step": round(a_ms, 5),
+                           "tokens_per_s": round(T / (a_ms * 1e-3), 1),
+                           "fractions": fractions(flops, nbytes, a_ms * 1e-3, peaks, "act4")}
+        return rec
+
+    def free(self):
+        import torch
+        self.layer = self.copies = None
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -265,144 +458,65 @@ def main():
         print(json.dumps({"error": "the MoE layer here runs on one GPU only: --gpus must be 1 "
                           "(expert-parallel sharding over several GPUs is designed, not implemented)"}))
         sys.exit(2)
-    import numpy as np
     import torch
-    import synth
     import mxfp4_expert_layer_moe_amd as M
-    from mxfp4_expert_layer_moe_amd.device import DeviceLayer
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     M.lib()
-    cfg = synth.CONFIGS[args.config]
-    decode = args.config == 1
-    if args.warmup is None:
-        # short warmups time the GPU partly before its clock has ramped up: measured 4-5% slower
-        # prefill steps after 5 warmup steps than after 300
-        args.warmup = 2000 if decode else (20 if args.config == 0 else 300)
-    L = args.layers or (24 if decode else 2)
-    t0 = time.time()
-    inp = synth.make_inputs(args.config)
-    print(f"[bench] inputs for config {args.config} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    layer = DeviceLayer(inp)
-    copies = [layer.weights] + [layer.weights.clone() for _ in range(L - 1)]
+    head_ci = args.config
+    dw, ds = default_counts(head_ci)
+    warmup = dw if args.warmup is None else args.warmup
+    steps = ds if args.steps is None else args.steps
+    subs = [] if args.only else [c for c in SUB_RECORDS if c != head_ci]
+    # every workload is on the device before any timing, so the GPU does not idle between them
+    work = {ci: Workload(ci, args.layers if ci == head_ci else None) for ci in subs + [head_ci]}
+    peaks = None
+    if not args.no_peaks:
+        from mxfp4_expert_layer_moe_amd import peaks as P
+        peaks = P.measure_all()
+        print(f"[bench] measured ceilings {json.dumps(peaks)}", file=sys.stderr, flush=True)
+    records = {}
+    for ci in subs:
+        sw, ss = default_counts(ci)
+        records[ci] = work[ci].measure(sw, ss, peaks, block=not args.no_block, act4=not args.no_act4)
+        print(f"[bench] workload {ci}: {records[ci]['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+    # ---- the headline: exactly `warmup` untimed and `steps` timed whole-layer steps -------------
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    T, D, E, k, I = inp.T, inp.D, inp.E, inp.k, inp.I
-
-    # ---- headline: K whole-layer steps ---------------------------------------
-    for s in range(args.warmup):
-        layer.forward(weights=copies[s % L])
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for s in range(args.steps):
-        layer.forward(weights=copies[s % L])
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
-
-    # ---- the pre-norm block around the layer, y = x + MoE(RMSNorm(x)), same steps -----
-    block = None
-    if not args.no_block:
-        for s in range(args.warmup):
-            layer.block_forward(weights=copies[s % L])
-        torch.cuda.synchronize()
-        eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        eb0.record(stream)
-        for s in range(args.steps):
-            layer.block_forward(weights=copies[s % L])
-        eb1.record(stream)
-        torch.cuda.synchronize()
-        b_ms = eb0.elapsed_time(eb1) / args.steps
-        block = {"what": "RMSNorm -> MoE layer -> residual add (moe_block_forward)",
-                 "ms_per_step": round(b_ms, 5), "tokens_per_s": round(T / (b_ms * 1e-3), 1),
-                 "extra_ms_over_layer": round(b_ms - ms_step, 5)}
-
-    # ---- the activation-quantized variant (MXFP4 activations), same steps ---------
-    act4 = None
-    if not args.no_act4:
-        for s in range(args.warmup):
-            layer.forward_act4(weights=copies[s % L])
-        torch.cuda.synchronize()
-        e40, e41 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e40.record(stream)
-        for s in range(args.steps):
-            layer.forward_act4(weights=copies[s % L])
-        e41.record(stream)
-        torch.cuda.synchronize()
-        a_ms = e40.elapsed_time(e41) / args.steps
-        act4 = {"what": "MXFP4 activations into the expert GEMMs (moe_forward_act4; a lower-precision contract)",
-                "ms_per_step": round(a_ms, 5), "tokens_per_s": round(T / (a_ms * 1e-3), 1)}
-
-    # ---- dominant kernel alone: gate/up expert GEMM, per-launch HIP events -----
-    layer.route(logits=False)
-    layer.permute()
-    layer.pack_x()
-    torch.cuda.synchronize()
-    counts = layer.counts.cpu().numpy()
-    touched = int((counts > 0).sum())
-    nk = args.kernel_steps or args.steps
-    for s in range(args.warmup):
-        layer.gate_up(weights=copies[s % L])
-    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ka.record(stream)                        # the launches run back to back on this stream
-    for s in range(nk):
-        layer.gate_up(weights=copies[s % L])
-    kb.record(stream)
-    torch.cuda.synchronize()
-    k_ms = ka.elapsed_time(kb) / nk
-    gu_weight_bytes = touched * 2 * I * D * EXPERT_BYTES_PER_PARAM
-    gu_alg_bytes = gu_weight_bytes + T * D * 2 + T * k * I * 2            # weights + x in + h out (bf16)
-    gu_flops = 2.0 * T * k * D * 2 * I
-    workload = workload_name(cfg)
-    if decode or gu_alg_bytes / HBM_PEAK_GBS > gu_flops / FP4_PEAK_TFLOPS / 1e3:
-        achieved = gu_alg_bytes / (k_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4))
-    else:
-        achieved = gu_flops / (k_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP4_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / FP4_PEAK_TFLOPS, 4))
-    roof["traffic"] = traffic_for(workload)
-    roof["kernel"] = "expert_gemm_kernel<0> (gate/up + SwiGLU)"
-    roof["kernel_ms"] = round(k_ms, 5)
-    roof["alg_bytes_per_launch"] = int(gu_alg_bytes)
-
-    # whole-layer algorithmic bytes / flops (touched experts' weights, x and y in bf16, router weights)
-    layer_bytes = touched * 3 * D * I * EXPERT_BYTES_PER_PARAM + T * D * 2 * 2 + E * D * 4
-    layer_flops = T * k * (2 * D * 2 * I + 2 * I * D) + 2 * T * D * E
-
+    head = work[head_ci].measure(warmup, steps, peaks, block=not args.no_block, act4=not args.no_act4,
+                                 kernel_steps=args.kernel_steps)
+    cfg = work[head_ci].cfg
+    roof = head.pop("gate_up_kernel")
     out = {
         "metric": "MoE-layer tokens/s (whole layer, one MI355X)",
-        "value": round(T / (ms_step * 1e-3), 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4(e2m1,e8m0) x bf16 -> fp32",
+        "dtype": "mxfp4 weights (e2m1, e8m0 per 32) x activations as hi+lo mxfp6 terms (e2m3, e8m0 per 32) "
+                 "-> fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": workload, "tokens_per_step": T, "weight_copies_rotated": L,
-                   "experts_touched": touched},
-        "layer": {"alg_bytes": int(layer_bytes), "GB_per_s": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
-                  "hbm_frac": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                  "TFLOP_per_s": round(layer_flops / (ms_step * 1e-3) / 1e12, 2),
-                  "wall_s_timed": round(wall, 3)},
+        "config": {"workload": head["workload"], "tokens_per_step": cfg["T"],
+                   "weight_copies_rotated": head["weight_copies_rotated"],
+                   "experts_touched": head["experts_touched"]},
+        "layer": {k: head[k] for k in ("alg_flops", "alg_bytes", "TFLOP_per_s", "GB_per_s", "wall_s_timed",
+                                        "fractions")},
         "roofline": roof,
         "cpu_baseline": None,
+        "peaks_measured": peaks,
+        "workloads": {synth_configs()[ci]["name"]: rec for ci, rec in records.items()},
     }
-    if block is not None:
-        out["block"] = block
-    if act4 is not None:
-        out["act4"] = act4
+    for key in ("block", "act4"):
+        if key in head:
+            out[key] = head[key]
+    for w in work.values():
+        w.free()
     if args.copy_mib > 0:                     # counter calibration: plain copies of known size, untimed
         n = args.copy_mib * 2 ** 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -414,7 +528,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens or (T if decode else 8))
+        out["cpu_baseline"] = cpu_baseline(work[head_ci].inp, args.cpu_tokens or (cfg["T"] if cfg["T"] <= 64 else 8))
     print(json.dumps(out), flush=True)
 
 

@@ -34,6 +34,19 @@
  *    grouped by expert (ascending) and, within an expert, by token.
  *  - Calls that share no buffers may run concurrently on different streams.
  *
+ * The step-by-step boundary (what differs from a plain bf16 interface)
+ * --------------------------------------------------------------------
+ *  - moe_permute also writes a row-tile table (expert, first grouped row, row
+ *    count and the assignment id of every row of each tile); the expert GEMMs
+ *    start from that table, not from perm and offsets.
+ *  - The expert GEMMs take their activations already packed ("split MX6",
+ *    below), not as bf16 rows: moe_pack_act packs x, and the gate/up stage
+ *    writes h in the same packed format, which the down stage reads.  A packed
+ *    row decodes to within 2^-8 of its 32-value block maximum of the bf16 row
+ *    (hi + lo; the bf16 h the layer defines is rounded before it is packed).
+ *  - The down stage writes y_perm in fp16, each row already multiplied by its
+ *    gate; moe_combine sums a token's rows.
+ *
  * Activation pack format ("split MX6")
  * ------------------------------------
  * The expert GEMMs consume activations that are already split into two MX
@@ -109,14 +122,19 @@ typedef struct {
 /* Human-readable name of a status code (static string). */
 const char* moe_status_str(moe_status s);
 
-/* Bytes of `rows` packed activation rows of length K (0 if K % 64 != 0). */
+/* Bytes of `rows` packed activation rows of length K (0 if K % 64 != 0): the split-MX6
+ * encoding above of the bf16 activations that enter the expert projections. */
 size_t moe_act_pack_bytes(int32_t K, int32_t rows);
 
-/* Bytes of the prepacked codes / scales of all experts for one stage. */
+/* Bytes of the prepacked codes / scales of all experts for one stage: 4 bits per weight plus
+ * one scale byte per 32 weights, 4.25 bits per parameter ("gpt-oss architecture
+ * walk-through", section "Quantization"); the scales are padded to whole groups of 4 k-tiles. */
 size_t moe_prepacked_codes_bytes(const moe_dims* dims, moe_stage stage);
 size_t moe_prepacked_scales_bytes(const moe_dims* dims, moe_stage stage);
 
-/* Workspace bytes moe_forward needs for T tokens (0 on invalid dims). */
+/* Workspace bytes moe_forward needs for T tokens (0 on invalid dims or an unsupported T): the
+ * scratch of the whole layer defined at the top of this file (routing results, the grouping,
+ * packed x and h, y_perm, the router's float64 partials), 256-byte aligned regions. */
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t T);
 
 /*
@@ -144,8 +162,16 @@ moe_status moe_route(const moe_dims* dims, int32_t T, const void* x_bf16, const 
 
 /*
  * Group the T*top_k assignments by expert (deterministic, no atomics on order)
- * and cut every expert's rows into row tiles for the expert GEMMs.
- *   topk_idx  [T][top_k] int32, every entry in [0, n_experts)
+ * and cut every expert's rows into row tiles for the expert GEMMs.  Only the
+ * selected experts run for a token, so each expert's feed-forward block works
+ * on the rows routed to it ("From GPT-2 to gpt-oss", section 4 "Mixture of
+ * Experts": the MoE module is sparse, not every expert is active for a token;
+ * "gpt-oss architecture walk-through", section "Mixture of Experts").
+ *   topk_idx  [T][top_k] int32, every entry in [0, n_experts) (precondition; an
+ *             entry outside it is a caller error: that assignment gets no row,
+ *             it is left out of counts, perm and the tiles, its inv entry is -1,
+ *             offsets[n_experts] counts only the valid ones, and perm past
+ *             offsets[n_experts] is left unwritten)
  *   counts    out [n_experts]; offsets out [n_experts + 1] (exclusive prefix sum)
  *   perm      out [T*top_k]: assignment id at each grouped position
  *   inv       out [T*top_k]: inv[perm[p]] = p
@@ -160,7 +186,10 @@ moe_status moe_permute(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
                        int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t stream);
 
 /*
- * Split bf16 rows into the packed hi/lo MX6 activation format above.
+ * Split bf16 rows into the packed hi/lo MX6 activation format above (the
+ * activations entering an expert's projections are the bf16 rows of the layer;
+ * the scaled matrix instruction that reads the MXFP4 weights, "gpt-oss
+ * architecture walk-through", section "Quantization", takes no bf16 operand).
  *   a_bf16   [rows][K] bf16 row-major, 16-byte aligned;  K % 64 == 0
  *   a_packed out, moe_act_pack_bytes(K, rows) bytes, 16-byte aligned
  */
@@ -168,6 +197,13 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
 
 /*
  * Grouped expert GEMM on MXFP4 weights with the CDNA4 scaled FP4 matrix cores.
+ * Each expert is a SwiGLU feed-forward block ("From GPT-2 to gpt-oss", section 3
+ * "Swish/SwiGLU", Figures 6-7: gate and up projections, silu(gate) * up, down
+ * projection), its pre-activations clamped at swiglu_limit (7 in the "GPT-OSS
+ * 20B" model card's raw config), its weights MXFP4 ("gpt-oss architecture
+ * walk-through", section "Quantization").  This call takes the packed
+ * activations and the row-tile table (see "The step-by-step boundary" above),
+ * not bf16 rows with perm and offsets.
  *  MOE_STAGE_GATE_UP:
  *    a_packed  packed x, T rows of d_model (moe_pack_act output); the row of
  *              grouped position p is token perm[p] / top_k
@@ -191,7 +227,10 @@ moe_status moe_expert_gemm_mxfp4(const moe_dims* dims, int32_t T, moe_stage stag
 
 /*
  * Weighted combine: y[t] = sum over the token's slots j (ascending expert id)
- * of y_perm[inv[t*top_k + j]], summed in fp32.
+ * of y_perm[inv[t*top_k + j]], summed in fp32: the gate-weighted sum of the
+ * selected experts' outputs ("gpt-oss architecture walk-through", section
+ * "Mixture of Experts": A = 0.7 x network 2 + 0.3 x network 4).  A slot whose
+ * inv entry is negative (an invalid expert id given to moe_permute) adds nothing.
  *   y_perm [T*top_k][d_model] fp16 (gate already applied);  inv from moe_permute
  *   y      out [T][d_model], fp32 (MOE_FP32) or bf16 round-to-nearest-even (MOE_BF16)
  */
@@ -228,7 +267,12 @@ moe_status moe_rmsnorm(const moe_dims* dims, int32_t T, const void* x_bf16, cons
 
 /*
  * The whole layer: route -> permute -> pack x -> gate/up + SwiGLU -> down ->
- * combine, enqueued on `stream` with no host synchronisation.  y has the same
+ * combine, enqueued on `stream` with no host synchronisation.  This is the MoE
+ * layer of a gpt-oss transformer block ("gpt-oss architecture walk-through",
+ * sections "Transformer Blocks" and "Mixture of Experts": a router and several
+ * expert networks replace the block's feed-forward network; [N x 2880] in and
+ * out; the top 4 experts of 32 (20b) or 128 (120b) are active per token), with
+ * the SwiGLU experts and MXFP4 weights of moe_expert_gemm_mxfp4.  y has the same
  * bits as the step-by-step entry points above give on the same inputs.  (Inside
  * the workspace the down stage writes each row at its assignment t*top_k + j
  * rather than at its permuted position, so the combine needs no inverse lookup.)
@@ -281,7 +325,10 @@ moe_status moe_block_forward(const moe_dims* dims, int32_t T, const void* x_bf16
 
 /*
  * Quantize fp32 rows [rows][K] (host memory, K % 32 == 0) to canonical MXFP4
- * with the OCP Microscaling v1.0 rule: scale exponent floor(log2(amax)) - 2,
+ * (the MoE weights are quantized to 4-bit floats after training, one 8-bit
+ * scale per 32 values: "gpt-oss architecture walk-through", section
+ * "Quantization"; "From GPT-2 to gpt-oss", section "MXFP4") with the OCP
+ * Microscaling v1.0 rule: scale exponent floor(log2(amax)) - 2,
  * elements rounded to nearest even on the E2M1 grid, saturating at +-6; an
  * all-zero block gets scale byte 0.  codes [rows][K/2], scales [rows][K/32].
  */
@@ -289,7 +336,8 @@ moe_status moe_mxfp4_quantize(const float* w, int64_t rows, int32_t K, uint8_t* 
 
 /*
  * Reorder canonical MXFP4 bytes of all n_experts experts (host memory) into
- * the device tile layout.  stage GATE_UP: N = 2*d_ff rows of K = d_model;
+ * the device tile layout (the same 4.25-bit-per-parameter MXFP4 values of
+ * "gpt-oss architecture walk-through", section "Quantization", only moved).  stage GATE_UP: N = 2*d_ff rows of K = d_model;
  * stage DOWN: N = d_model rows of K = d_ff.
  */
 moe_status moe_mxfp4_prepack(const moe_dims* dims, moe_stage stage, const uint8_t* codes,

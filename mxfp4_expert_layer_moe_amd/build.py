@@ -1,4 +1,5 @@
-"""Build libmoe_mxfp4.so (gfx950 only) in-tree with hipcc.
+"""Build libmoe_mxfp4.so (the layer) and libmoe_peaks.so (the ceiling probes), gfx950 only,
+in-tree with hipcc.
 
     python -m mxfp4_expert_layer_moe_amd.build        # or build() from Python
 """
@@ -13,6 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe_mxfp4.so")
+PEAKS_LIB = os.path.join(LIBDIR, "libmoe_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["api.cpp", "route.hip", "permute.hip", "pack.hip", "gemm.hip", "gemm_prefill.hip", "combine.hip",
@@ -35,11 +38,11 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library; returns its path."""
+    """Compile every source for gfx950 and link both shared libraries; returns the layer's path."""
     os.makedirs(LIBDIR, exist_ok=True)
     cc = hipcc()
     objs, procs = [], []
-    for src in SOURCES:
+    for src in SOURCES + PEAKS_SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(LIBDIR, os.path.splitext(src)[0] + ".o")
         cmd = [cc, *HIPFLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", path, "-o", obj]
@@ -58,12 +61,14 @@ def build(verbose: bool = False) -> str:
             print(msgs)
     if failed:
         raise RuntimeError(f"hipcc failed on {failed}")
-    tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    n = len(SOURCES)
+    for lib, lib_objs in ((LIB, objs[:n]), (PEAKS_LIB, objs[n:])):
+        tmp = lib + ".tmp"
+        cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *lib_objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -45,10 +45,10 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int D, int k, const
     h8 v[kCombineBatch];
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u)
-      if (j0 + u < k) v[u] = *reinterpret_cast<const h8*>(y_perm + (size_t)p[u] * D + c);
+      if (j0 + u < k && p[u] >= 0) v[u] = *reinterpret_cast<const h8*>(y_perm + (size_t)p[u] * D + c);
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u)                 // slot order
-      if (j0 + u < k) {
+    for (int u = 0; u < kCombineBatch; ++u)                 // slot order; a slot with inv = -1 has no row
+      if (j0 + u < k && p[u] >= 0) {
 #pragma unroll
         for (int i = 0; i < kCombineCols; ++i) acc[i] += (float)v[u][i];
       }

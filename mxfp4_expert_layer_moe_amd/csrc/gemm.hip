@@ -237,11 +237,13 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
             acc[nb] = mma_sel(j & 3, al[cur], bv, acc[nb], sl[cur], sbq[j >> 2][nb]);
           }
         }
-        const int kn = min(kt + P, kend - 1);
+        // the refill runs past the staged chunk into the next one (chunks start at multiples of
+        // P, so slot j of the next chunk is k-tile kt + P); only the end of K clamps it
+        const int kn = min(kt + P, g.KT - 1);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) bq[j][nb] = load_b(nb, kn);
         if ((j & 3) == 3) {
-          const int grp = min((kt + P - 3) / 4, (kend - 1) / 4);
+          const int grp = min((kt + P - 3) / 4, (g.KT - 1) / 4);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) sbq[j >> 2][nb] = load_s(nb, grp);
         }
@@ -312,18 +314,9 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   }
 }
 
-#ifndef MOE_DECODE_DOWN_NB
-#define MOE_DECODE_DOWN_NB 1
-#endif
-#ifndef MOE_DECODE_DOWN_P
-#define MOE_DECODE_DOWN_P 8
-#endif
-#ifndef MOE_DECODE_GU_P
-#define MOE_DECODE_GU_P 8
-#endif
-constexpr int kGateUpP = MOE_DECODE_GU_P;     // gate/up weight k-tiles in flight per wavefront
-constexpr int kDownNB = MOE_DECODE_DOWN_NB;   // down-projection weight tiles per wavefront
-constexpr int kDownP = MOE_DECODE_DOWN_P;     // and k-tiles in flight
+constexpr int kGateUpP = 8;     // gate/up weight k-tiles in flight per wavefront
+constexpr int kDownNB = 1;      // down-projection weight tiles per wavefront
+constexpr int kDownP = 8;       // and k-tiles in flight
 
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,

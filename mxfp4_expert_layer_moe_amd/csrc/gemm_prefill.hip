@@ -409,14 +409,8 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   else body(std::integral_constant<int, 1>{});
 }
 
-#ifndef MOE_PREFILL_NA
-#define MOE_PREFILL_NA 2
-#endif
-#ifndef MOE_PREFILL_P
-#define MOE_PREFILL_P 4
-#endif
-constexpr int kPNA = MOE_PREFILL_NA;
-constexpr int kPP = MOE_PREFILL_P;
+constexpr int kPNA = 2;         // activation k-tiles in flight in registers
+constexpr int kPP = 4;          // weight k-tiles in flight per wavefront
 
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,

@@ -24,6 +24,8 @@
 //      (a ballot match inside a wavefront, per-wavefront counts across them).
 // The per-workgroup counts and the expert tile starts live in the scratch tail
 // of the tile buffer.
+// An expert id outside [0, E) (a caller error) gets no row: it is left out of
+// counts, perm and the tiles, and its inv entry is -1, which the combine skips.
 #include "permute_body.h"
 
 namespace moe {
@@ -156,7 +158,10 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(int n, int E
   __syncthreads();
   if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
   __syncthreads();
-  if (!valid) return;
+  if (!valid) {
+    if (a < n) inv[a] = -1;                             // an id outside [0, E): no row
+    return;
+  }
   int pos = offsets[e] + base[(size_t)blockIdx.x * E + e] + rank;
   for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
   perm[pos] = (int32_t)a;

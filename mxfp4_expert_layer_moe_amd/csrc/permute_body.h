@@ -121,6 +121,7 @@ __device__ inline void permute_group(int n, int E, int bm, int slots,
       __syncthreads();
       if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
       __syncthreads();
+      if (!valid && a < n) inv[a] = -1;                  // an id outside [0, E): no row
       if (valid) {
         int pos = base[e] + rank;
         for (int w = 0; w < wave; ++w) pos += wcnt[w][e];

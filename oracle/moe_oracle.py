@@ -166,11 +166,14 @@ def swiglu(g: np.ndarray, u: np.ndarray, limit: float) -> np.ndarray:
     return silu(g) * u
 
 
-def expert_ffn(xr: np.ndarray, gu_codes, gu_scales, dn_codes, dn_scales, limit: float, act4: bool = False):
+def expert_ffn(xr: np.ndarray, gu_codes, gu_scales, dn_codes, dn_scales, limit: float, act4: bool = False,
+               preact: bool = False):
     """One expert on rows xr [M][D]: returns (h [M][I] bf16-rounded f64, z [M][D] f64).
 
     act4: the activation-quantized variant; the rows entering each projection (x, then h) are
-    quantized to MXFP4 first (mxfp4_quantize_rows), and the returned h is that quantized h."""
+    quantized to MXFP4 first (mxfp4_quantize_rows), and the returned h is that quantized h.
+    preact: also return the gate and up pre-activations g, u [M][I] (before the clamp), as
+    (h, z, g, u); the arithmetic is the same either way."""
     w_gu = mxfp4_decode(gu_codes, gu_scales)        # [2I][D]
     I = w_gu.shape[0] // 2
     xa = mxfp4_quantize_rows(xr) if act4 else xr
@@ -182,7 +185,7 @@ def expert_ffn(xr: np.ndarray, gu_codes, gu_scales, dn_codes, dn_scales, limit: 
         h = mxfp4_quantize_rows(h)
     w_dn = mxfp4_decode(dn_codes, dn_scales)        # [D][I]
     z = h @ w_dn.T
-    return h, z
+    return (h, z, g, u) if preact else (h, z)
 
 
 def mxfp4_quantize_rows(v: np.ndarray) -> np.ndarray:
@@ -220,7 +223,8 @@ def combine(w: np.ndarray, z_perm: np.ndarray, inv: np.ndarray, tokens: np.ndarr
     return y
 
 
-def forward(inp, tokens=None, override_idx: dict | None = None, act4: bool = False) -> dict:
+def forward(inp, tokens=None, override_idx: dict | None = None, act4: bool = False,
+            preact: bool = False) -> dict:
     """Evaluate the layer.
 
     inp: object with T, D, E, k, I, swiglu_limit, x_bf16, w_router, b_router,
@@ -232,6 +236,8 @@ def forward(inp, tokens=None, override_idx: dict | None = None, act4: bool = Fal
     for those tokens (used for near-tie tokens only).
     act4: the activation-quantized variant (MXFP4 activations into both expert
     projections; routing on the unquantized x).
+    preact: also keep each evaluated position's gate and up pre-activations
+    (before the clamp) in g and u, by position p.
 
     Returns a dict with logits, idx, flagged, gap, w, counts, offsets, perm,
     inv, tokens, and for the evaluated tokens: h (by position p), z (by
@@ -250,24 +256,31 @@ def forward(inp, tokens=None, override_idx: dict | None = None, act4: bool = Fal
 
     want = np.zeros(T, dtype=bool)
     want[tokens] = True
-    h_all, z_all = {}, {}
+    h_all, z_all, g_all, u_all = {}, {}, {}, {}
     for e in range(E):
         seg = np.arange(offsets[e], offsets[e + 1])
         seg = seg[want[perm[seg] // k]]
         if seg.size == 0:
             continue
         rows = x[perm[seg] // k]
-        h, z = expert_ffn(rows, inp.gu_codes[e], inp.gu_scales[e], inp.dn_codes[e],
-                          inp.dn_scales[e], inp.swiglu_limit, act4=act4)
+        res = expert_ffn(rows, inp.gu_codes[e], inp.gu_scales[e], inp.dn_codes[e],
+                         inp.dn_scales[e], inp.swiglu_limit, act4=act4, preact=preact)
+        h, z = res[0], res[1]
         for i, p in enumerate(seg):
             h_all[int(p)] = h[i]
             z_all[int(p)] = z[i]
+            if preact:
+                g_all[int(p)] = res[2][i]
+                u_all[int(p)] = res[3][i]
     z_perm = np.zeros((T * k, inp.D), dtype=np.float64)
     for p, zz in z_all.items():
         z_perm[p] = zz
     y = combine(w, z_perm, inv, tokens, k)
-    return dict(logits=logits, idx=idx, flagged=flagged, gap=gap, w=w, counts=counts,
-                offsets=offsets, perm=perm, inv=inv, tokens=tokens, h=h_all, z=z_all, y=y)
+    out = dict(logits=logits, idx=idx, flagged=flagged, gap=gap, w=w, counts=counts,
+               offsets=offsets, perm=perm, inv=inv, tokens=tokens, h=h_all, z=z_all, y=y)
+    if preact:
+        out["g"], out["u"] = g_all, u_all
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -50,6 +50,55 @@ def decode_sum(buf, K: int, rows: int) -> np.ndarray:
     return hi + lo
 
 
+# ---- host encoder of the same format (CPU tests of the parity machinery) --------------------
+# Written from the format description: per 32-value block, the shared exponent floor(log2 amax) - 2
+# as an E8M0 byte clamped to [1, 253] (127 for an all-zero block); each value divided by the scale
+# and rounded to the nearest E2M3 magnitude, ties to the even code, saturating at 7.5.  lo is the
+# same encoding of what hi leaves over.
+_E2M3_POS = _E2M3[:32]                     # codes 0..31: the non-negative magnitudes, ascending
+
+
+def _scale_byte(amax: np.ndarray) -> np.ndarray:
+    ex = np.frexp(np.where(amax > 0, amax, 1.0))[1] - 1 - 2       # floor(log2 amax) - 2
+    return np.where(amax > 0, np.clip(ex + 127, 1, 253), 127).astype(np.int64)
+
+
+def _e2m3_codes(q: np.ndarray) -> np.ndarray:
+    """Nearest E2M3 code of each value (ties to the even code, magnitudes past 7.5 to 7.5)."""
+    m = np.minimum(np.abs(q), 7.5)
+    d = np.abs(m[..., None] - _E2M3_POS)
+    best = d.min(axis=-1, keepdims=True)
+    even = np.arange(32) % 2 == 0
+    tie_even = (d == best) & even
+    code = np.where(tie_even.any(axis=-1), np.argmax(tie_even, axis=-1), np.argmax(d == best, axis=-1))
+    return code | np.where(q < 0, 32, 0)
+
+
+def _split_block_terms(v: np.ndarray):
+    """v [..., 32] -> (codes hi, codes lo, scale byte hi, scale byte lo)."""
+    sh = _scale_byte(np.abs(v).max(-1))
+    ch = _e2m3_codes(v / np.ldexp(1.0, sh - 127)[..., None])
+    hi = _E2M3[ch] * np.ldexp(1.0, sh - 127)[..., None]
+    r = v - hi
+    sl = _scale_byte(np.abs(r).max(-1))
+    cl = _e2m3_codes(r / np.ldexp(1.0, sl - 127)[..., None])
+    return ch, cl, sh, sl
+
+
+def encode(v: np.ndarray) -> np.ndarray:
+    """Rows [R][K] of bf16 values (float64) -> packed bytes uint8 [R][row_bytes(K)]."""
+    R, K = v.shape
+    kt = K // 64
+    ch, cl, sh, sl = _split_block_terms(np.asarray(v, np.float64).reshape(R, kt, 2, 32))
+    out = np.zeros((R, kt, 112), np.uint8)
+    for term, c in ((0, ch), (1, cl)):
+        bits = ((c[..., None] >> np.arange(6)) & 1).astype(np.uint8).reshape(R, kt, 2, 192)
+        out[:, :, term * 48:(term + 1) * 48] = np.packbits(bits, axis=-1, bitorder="little").reshape(R, kt, 48)
+    out[:, :, 96:98] = sh
+    out[:, :, 98:100] = sl
+    return out.reshape(R, kt * 112)
+
+
 # ---- MXFP4 activation rows (the activation-quantized entry points) -------------------------
 # Per row, K/64 chunks of 48 bytes: [0,16) E2M1 codes of block 2kt (element i in nibble i, low
 # nibble first), [16,32) codes of block 2kt+1, [32],[33] their E8M0 scale bytes.

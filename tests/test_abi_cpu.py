@@ -22,8 +22,8 @@ def L():
     return M.lib()
 
 
-def header_functions():
-    src = open(os.path.join(ROOT, "include", "moe_mxfp4.h")).read()
+def header_functions(header="moe_mxfp4.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
@@ -34,6 +34,22 @@ def test_library_exports_every_header_symbol(L):
     assert sorted(M.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_probe_library_exports_every_header_symbol():
+    from mxfp4_expert_layer_moe_amd import peaks
+    P = peaks.lib()
+    names = header_functions("moe_peaks.h")
+    assert sorted(peaks.EXPORTS) == names
+    for n in names:
+        assert hasattr(P, n), n
+    # the work each probe reports, and argument checks before any launch
+    assert P.moe_peak_mfma_flops(peaks.FP6_FP4, 10, 3) == 10 * 4 * 3 * 4 * 2 * 32 * 32 * 64
+    assert P.moe_peak_mfma_flops(peaks.BF16, 10, 3) == 10 * 4 * 3 * 4 * 2 * 32 * 32 * 16
+    assert P.moe_peak_mfma(peaks.FP6_FP4, 0, 1, 16, None) == 1
+    assert P.moe_peak_mfma(9, 1, 1, 16, None) == 1
+    assert P.moe_peak_stream_read(16, 24, 1, 1, 16, None) == 1           # not a multiple of 16 bytes
+    assert P.moe_peak_stream_read(None, 32, 1, 1, 16, None) == 1
 
 
 def test_status_strings(L):

@@ -15,6 +15,8 @@ import bench  # noqa: E402
 GU_BF16 = "void moe::expert_gemm_kernel<0, 8, 8, 45, 1, 1, 2, 0>(moe::GemmArgs)"
 GU_ACT4 = "void moe::expert_gemm_kernel<0, 8, 8, 45, 1, 1, 2, 1>(moe::GemmArgs)"
 DOWN = "void moe::expert_gemm_kernel<1, 8, 8, 45, 2, 1, 1, 0>(moe::GemmArgs)"
+PF_BF16 = "void moe::expert_gemm_prefill_kernel<0, 45, 2, 4, 0>(moe::PrefillArgs)"
+PF_ACT4 = "void moe::expert_gemm_prefill_kernel<0, 45, 2, 4, 1>(moe::PrefillArgs)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -54,8 +56,48 @@ def test_traffic_record_scales_each_counter_by_the_copy_calibration(tmp_path):
     assert rec["fetch_bytes_per_launch"] == 2000 * 1024 * 2          # mean of 1000 and 3000 KiB, x 2
     assert rec["write_bytes_per_launch"] == 20 * 1024
     assert rec["hbm_bytes_per_launch"] == 2000 * 1024 * 2 + 20 * 1024
-    assert rec["kernel_source_sha256_16"] == bench.gemm_source_hash()
+    assert rec["kernel_source_sha256_16"] == bench.gemm_source_hash("decode")
     assert rec["workload"] == bench.workload_name(__import__("synth").CONFIGS[1])
+    assert rec["kernel"].startswith("expert_gemm_kernel<0>")
+
+
+def test_traffic_record_of_a_prefill_workload_counts_the_large_batch_kernel(tmp_path):
+    mib = 16
+    kib = mib * 1024
+    _write_counters(tmp_path / "f", "FETCH_SIZE",
+                    [(1, GU_BF16, 9e9), (2, PF_BF16, 500.0), (3, PF_ACT4, 7e9), (4, PF_BF16, 1500.0),
+                     (6, COPY, kib / 2), (7, COPY, kib / 2), (8, COPY, kib / 2)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE",
+                    [(2, PF_BF16, 10.0), (4, PF_BF16, 30.0), (6, COPY, kib), (7, COPY, kib), (8, COPY, kib)])
+    rec = bench.traffic_record(str(tmp_path / "f"), str(tmp_path / "w"), mib, 4, "cmd")
+    assert rec["fetch_gate_up_dispatches"] == 2
+    assert rec["fetch_bytes_per_launch"] == 1000 * 1024 * 2
+    assert rec["kernel_source_sha256_16"] == bench.gemm_source_hash("prefill")
+    assert rec["kernel"].startswith("expert_gemm_prefill_kernel<0>")
+
+
+def test_fractions_against_spec_and_measured_peaks():
+    peaks = {"stream_read_nt_GB_per_s": 6000.0, "mfma_fp4xfp4_TFLOP_per_s": 7000.0,
+             "mfma_fp6xfp4_TFLOP_per_s": 8000.0}
+    # 1 TFLOP and 1 GB in 1 ms: 1 PF/s and 1 TB/s
+    f = bench.fractions(1e12, 1e9, 1e-3, peaks, "default")
+    assert f["spec"]["R_HBM"] == round(1000 / 8000, 4)
+    assert f["spec"]["R_MXFP4"] == round(1000 / 10100, 4)
+    # the default path issues two FP6 x FP4 instructions per tile: half the format's rate
+    assert f["spec"]["R_roof"] == round(max(1e9 / 8e12, 1e12 / 5.05e15) / 1e-3, 4)
+    assert f["spec"]["roof_bound"] == "mfma"
+    assert f["measured"]["R_HBM"] == round(1000 / 6000, 4)
+    assert f["measured"]["R_roof"] == round(max(1e9 / 6e12, 1e12 / 4e15) / 1e-3, 4)
+    g = bench.fractions(1e12, 1e9, 1e-3, None, "act4")
+    assert "measured" not in g and g["spec"]["R_roof"] == round(max(1e9 / 8e12, 1e12 / 10.1e15) / 1e-3, 4)
+
+
+def test_the_headline_is_the_largest_workload():
+    import synth
+    sizes = {c: synth.CONFIGS[c]["T"] * synth.CONFIGS[c]["E"] for c in synth.CONFIGS}
+    assert bench.HEADLINE == max(sizes, key=sizes.get)
+    assert set(bench.SUB_RECORDS) | {bench.HEADLINE} == set(synth.CONFIGS) - {0}
+    assert bench.gemm_kind(synth.CONFIGS[1]) == "decode" and bench.gemm_kind(synth.CONFIGS[4]) == "prefill"
 
 
 def test_traffic_record_needs_three_calibration_copies(tmp_path):
@@ -65,13 +107,19 @@ def test_traffic_record_needs_three_calibration_copies(tmp_path):
         bench.traffic_record(str(tmp_path / "f"), str(tmp_path / "w"), 16, 1)
 
 
-def test_traffic_is_reported_only_for_the_source_it_was_measured_on(monkeypatch):
-    rec = json.load(open(os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")))
-    monkeypatch.setattr(bench, "gemm_source_hash", lambda: rec["kernel_source_sha256_16"])
-    assert bench.traffic_for(rec["workload"]) == rec["hbm_bytes_per_launch"]
-    assert bench.traffic_for(rec["workload"] + " (other)") is None
-    monkeypatch.setattr(bench, "gemm_source_hash", lambda: "0" * 16)
-    assert bench.traffic_for(rec["workload"]) is None
+def test_traffic_is_reported_only_for_the_source_it_was_measured_on(monkeypatch, tmp_path):
+    import synth
+    cfg = dict(synth.CONFIGS[4])
+    rec = {"workload": bench.workload_name(cfg), "kernel_source_sha256_16": "ab" * 8,
+           "hbm_bytes_per_launch": 12345}
+    path = tmp_path / "t.json"
+    path.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "traffic_path", lambda c: str(path))
+    monkeypatch.setattr(bench, "gemm_source_hash", lambda kind="decode": "ab" * 8)
+    assert bench.traffic_for(cfg) == 12345
+    assert bench.traffic_for(dict(cfg, T=4096)) is None                  # another workload
+    monkeypatch.setattr(bench, "gemm_source_hash", lambda kind="decode": "0" * 16)
+    assert bench.traffic_for(cfg) is None
 
 
 def test_pmc_summary_means_per_dispatch_and_derives_the_matrix_rate(tmp_path):

@@ -117,7 +117,8 @@ def test_act4_small_case_parity(name):
     _act4_check(name, synth.make_inputs(c["cfg"], x_scale=c.get("x_scale", 1.0)))
 
 
-@pytest.mark.parametrize("cfg,n_tokens", [(1, None), (2, 32), (3, 32)])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,n_tokens", [(1, None), (2, 32), (3, 32), (4, 512)])
 def test_act4_full_size_workload(cfg, n_tokens):
     inp = synth.make_inputs(cfg)
     tokens = None if n_tokens is None else np.sort(np.random.default_rng(300 + cfg).choice(inp.T, n_tokens,

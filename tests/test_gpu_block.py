@@ -92,11 +92,11 @@ def _block_check(name, inp, tokens=None):
     torch.cuda.synchronize()
     assert np.array_equal(b32.cpu().numpy(), y32)
     assert np.array_equal(b16, y16)
-    # and against the oracle's block output on the evaluated tokens
-    ob = oracle.block_forward(inp, tokens=o["tokens"], override_idx=None if not o["n_adopted"] else
-                              {int(t): g["idx"][t] for t in np.nonzero(o["flagged"])[0]})
-    dy = np.abs(y32[ob["tokens"]].astype(np.float64) - ob["y"]).max()
-    rms_moe = float(np.sqrt(np.mean(ob["y_moe"] ** 2)))
+    # and against the oracle's block output on the evaluated tokens: oracle.block_forward is the
+    # input row plus the layer on the normalised rows, which o already holds (same adoption)
+    ob_y = x32[o["tokens"]].astype(np.float64) + o["y"]
+    dy = np.abs(y32[o["tokens"]].astype(np.float64) - ob_y).max()
+    rms_moe = float(np.sqrt(np.mean(o["y"] ** 2)))
     stats["block_y_max_err_over_rms_moe"] = float(dy / rms_moe)
     assert dy <= parity.TOL_Y * rms_moe
     stats["seconds"] = round(time.time() - t0, 1)
@@ -118,7 +118,8 @@ def test_block_small_case_parity(name):
     _block_check(name, synth.make_inputs(c["cfg"], x_scale=c.get("x_scale", 1.0)))
 
 
-@pytest.mark.parametrize("cfg,n_tokens", [(1, None), (2, 32)])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,n_tokens", [(1, None), (2, 32), (3, 512), (4, 512)])
 def test_block_full_size_workload(cfg, n_tokens):
     inp = synth.make_inputs(cfg)
     tokens = None if n_tokens is None else np.sort(np.random.default_rng(200 + cfg).choice(inp.T, n_tokens,

@@ -220,7 +220,7 @@ def test_sparse_oracle_equals_dense_brute_force(case):
     yb = np.array(b["y"])
     scale = np.abs(yb).max()
     assert np.abs(o["y"] - yb).max() <= 1e-12 * scale
-    if case.get("x_scale") == 8.0:
+    if case.get("x_scale", 1.0) > 1.0:
         x = oracle.bf16_to_f64(inp.x_bf16)
         g = x @ oracle.mxfp4_decode(inp.gu_codes[0], inp.gu_scales[0]).T
         assert (np.abs(g) > 7).mean() > 0.2           # the clamp really binds
