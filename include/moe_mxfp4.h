@@ -284,6 +284,30 @@ moe_status moe_forward(const moe_dims* dims, int32_t T, const void* x_bf16, cons
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_forward for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  The same kernels and
+ * the same result bits as moe_forward, with no workspace argument: the scratch
+ * is a file-scope device array of MOE_FORWARD_NOALLOC_MAX_WORKSPACE bytes that
+ * each GPU holds from the library's load until the process ends (its device
+ * address is looked up once per device, on the first call made with that
+ * device current).  The call allocates and frees nothing, and calls no
+ * allocating library routine.
+ *  - Limit: T with moe_workspace_bytes(dims, T) > MOE_FORWARD_NOALLOC_MAX_WORKSPACE
+ *    returns MOE_EWORKSPACE before anything is launched (at d_model = d_ff = 2880
+ *    and top_k = 4: T up to 339 with 32 experts, 318 with 128; decode batches).
+ *  - Every call on one GPU uses that GPU's one array: calls that overlap on one
+ *    GPU (other streams, other threads) race and must be serialised by the
+ *    caller.  Nothing in the array needs to start at zero; it keeps the last
+ *    call's contents.
+ *  - `stream` must belong to the current device (else MOE_EINVAL); other
+ *    arguments and errors as moe_forward.
+ */
+#define MOE_FORWARD_NOALLOC_MAX_WORKSPACE ((size_t)16 << 20)
+moe_status moe_forward_noalloc(const moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                               const float* b_router, const moe_weights* weights, void* y, moe_dtype y_dtype,
+                               hipStream_t stream);
+
+/*
  * The activation-quantized variant (W4A4): the expert GEMMs take their
  * activations as MXFP4 (format above) and run one FP4 x FP4 scaled matrix
  * instruction per weight tile, the full MXFP4 rate of the matrix cores (the

@@ -26,7 +26,8 @@ EXPORTS = ("moe_status_str", "moe_act_pack_bytes", "moe_prepacked_codes_bytes", 
            "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine", "moe_forward", "moe_mxfp4_quantize",
            "moe_mxfp4_prepack", "moe_combine_residual", "moe_rmsnorm", "moe_block_workspace_bytes",
            "moe_block_forward", "moe_act4_pack_bytes", "moe_pack_act4", "moe_expert_gemm_mxfp4_act4",
-           "moe_workspace_bytes_act4", "moe_forward_act4")
+           "moe_workspace_bytes_act4", "moe_forward_act4", "moe_forward_noalloc")
+MOE_FORWARD_NOALLOC_MAX_WORKSPACE = 16 << 20
 
 
 class MoeError(RuntimeError):
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_gemm_mxfp4_act4.argtypes = [dp, i32, ctypes.c_int, vp, i32p, vp, vp, f32p, vp, vp]
         L.moe_forward_act4.argtypes = [dp, i32, vp, f32p, f32p, ctypes.POINTER(moe_weights), vp, ctypes.c_int, vp,
                                        sz, vp]
+        L.moe_forward_noalloc.argtypes = [dp, i32, vp, f32p, f32p, ctypes.POINTER(moe_weights), vp, ctypes.c_int, vp]
         L.moe_rmsnorm.argtypes = [dp, i32, vp, f32p, ctypes.c_float, vp, vp]
         L.moe_block_forward.argtypes = [dp, i32, vp, f32p, ctypes.c_float, f32p, f32p, ctypes.POINTER(moe_weights),
                                         vp, ctypes.c_int, vp, sz, vp]
@@ -89,7 +91,7 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_route", "moe_permute", "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine",
                      "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_prepack", "moe_combine_residual",
                      "moe_rmsnorm", "moe_block_forward", "moe_pack_act4", "moe_expert_gemm_mxfp4_act4",
-                     "moe_forward_act4"):
+                     "moe_forward_act4", "moe_forward_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -180,6 +182,11 @@ def moe_forward(d, T, x, w_router, b_router, weights: moe_weights, y, y_dtype, w
         ws_bytes = ws.numel() * ws.element_size()
     _check(lib().moe_forward(ctypes.byref(d), T, _p(x), _p(w_router), _p(b_router), ctypes.byref(weights), _p(y),
                              y_dtype, _p(ws), ws_bytes, _s(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(d, T, x, w_router, b_router, weights: moe_weights, y, y_dtype, stream=None):
+    _check(lib().moe_forward_noalloc(ctypes.byref(d), T, _p(x), _p(w_router), _p(b_router), ctypes.byref(weights),
+                                     _p(y), y_dtype, _s(stream)), "moe_forward_noalloc")
 
 
 def moe_combine_residual(d, T, y_perm, inv, residual, y, y_dtype, stream=None):

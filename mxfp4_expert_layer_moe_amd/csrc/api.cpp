@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe_mxfp4.h"
 #include "moe_internal.h"
 
@@ -66,19 +68,28 @@ WsLayout ws_layout(const moe_dims* d, int32_t T, int af = kActSplit6) {
   return L;
 }
 
-moe_status check_forward(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
-                         const float* b_router, const moe_weights* wts, const void* y, moe_dtype y_dtype,
-                         const void* ws) {
+// the whole-layer arguments other than the workspace
+moe_status check_layer_args(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                            const float* b_router, const moe_weights* wts, const void* y, moe_dtype y_dtype) {
   moe_status st = check_dims(d);
   if (st != MOE_OK) return st;
   if ((st = check_T(d, T)) != MOE_OK) return st;
   if (y_dtype != MOE_BF16 && y_dtype != MOE_FP32) return MOE_EINVAL;
-  if (!x_bf16 || !w_router || !b_router || !wts || !y || !ws) return MOE_EINVAL;
+  if (!x_bf16 || !w_router || !b_router || !wts || !y) return MOE_EINVAL;
   if (!wts->gu_codes || !wts->gu_scales || !wts->dn_codes || !wts->dn_scales) return MOE_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(b_router, 4) || !aligned(y, 16) ||
-      !aligned(ws, kAlignWs) || !aligned(wts->gu_codes, 16) || !aligned(wts->dn_codes, 16) ||
-      !aligned(wts->gu_scales, 4) || !aligned(wts->dn_scales, 4))
+      !aligned(wts->gu_codes, 16) || !aligned(wts->dn_codes, 16) || !aligned(wts->gu_scales, 4) ||
+      !aligned(wts->dn_scales, 4))
     return MOE_EINVAL;
+  return MOE_OK;
+}
+
+moe_status check_forward(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                         const float* b_router, const moe_weights* wts, const void* y, moe_dtype y_dtype,
+                         const void* ws) {
+  const moe_status st = check_layer_args(d, T, x_bf16, w_router, b_router, wts, y, y_dtype);
+  if (st != MOE_OK) return st;
+  if (!ws || !aligned(ws, kAlignWs)) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -119,6 +130,42 @@ moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const u
   return MOE_OK;
 }
 
+}  // namespace
+
+// ---- the whole layer with no allocation ------------------------------------------------------
+// For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
+// that forbid it): moe_forward's scratch lives in this file-scope device array instead of a
+// workspace argument.  Each GPU holds its own copy, at its own address, until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, looked up once per device with
+// that device current, and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+static_assert(kNoAllocScratchBytes % 256 == 0, "scratch regions are 256-byte aligned");
+static_assert(kNoAllocScratchBytes == MOE_FORWARD_NOALLOC_MAX_WORKSPACE, "the header states the limit");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+uint8_t* scratch_ptr[kMaxDevices];
+
+// The device address of the current device's scratch array (looked up on the first call per device).
+moe_status scratch_of_current_device(hipStream_t stream, uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  if (stream) {                          // the stream must run on the current device
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_EHIP;
+    if (sdev != dev) return MOE_EINVAL;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    scratch_ptr[dev] = (uint8_t*)p;
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -294,6 +341,20 @@ moe_status moe_forward(const moe_dims* d, int32_t T, const void* x_bf16, const f
   if (T == 0) return MOE_OK;
   return forward_impl(d, T, (const uint16_t*)x_bf16, nullptr, w_router, b_router, wts, y, y_dtype,
                       (uint8_t*)ws, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                               const float* b_router, const moe_weights* wts, void* y, moe_dtype y_dtype,
+                               hipStream_t stream) {
+  // the checks of moe_forward, with the scratch array standing in for the workspace; all before
+  // any HIP call
+  moe_status st = check_layer_args(d, T, x_bf16, w_router, b_router, wts, y, y_dtype);
+  if (st != MOE_OK) return st;
+  if (ws_layout(d, T).total > kNoAllocScratchBytes) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  uint8_t* base = nullptr;
+  if ((st = scratch_of_current_device(stream, &base)) != MOE_OK) return st;
+  return forward_impl(d, T, (const uint16_t*)x_bf16, nullptr, w_router, b_router, wts, y, y_dtype, base, stream);
 }
 
 size_t moe_workspace_bytes_act4(const moe_dims* d, int32_t T) {

@@ -17,6 +17,8 @@ constexpr int kKTile = 64;          // K per scaled MFMA 32x32x64
 constexpr int kMTile = 32;          // rows per MFMA tile
 constexpr int kNTile = 32;          // output columns per MFMA tile
 constexpr int kMaxExperts = 256;
+// scratch of the entry point that allocates nothing (moe_forward_noalloc), per GPU
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 
 // ---------------------------------------------------------------------------
 // Packed activation rows ("split MX6"): hi and lo FP6 E2M3 terms per 32-block.
@@ -150,6 +152,7 @@ hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, flo
 // inv null: the rows are in assignment order (row t*k + j), as the down stage writes with out_assign
 hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, const uint16_t* residual,
                           void* y, int y_bf16, hipStream_t s);
+
 hipError_t launch_rmsnorm(int T, int D, const uint16_t* x, const float* gamma, float eps, uint16_t* xn,
                           hipStream_t s);
 

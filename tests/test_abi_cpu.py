@@ -252,3 +252,20 @@ def test_largest_batch_is_accepted_and_one_more_token_is_not(L):
     assert L.moe_forward(dp, T + 1, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, 1 << 40, None) == M.MOE_EUNSUPPORTED
     # with T itself the arguments pass and only the (too small) workspace is refused
     assert L.moe_forward(dp, T, A, A, A, ctypes.byref(w), A, M.MOE_FP32, A, 256, None) == M.MOE_EWORKSPACE
+
+
+def test_noalloc_forward_rejects_before_any_device_call(L):
+    """moe_forward_noalloc checks its arguments and its scratch limit on the host first: a batch
+    whose workspace passes the 16 MiB array is refused with MOE_EWORKSPACE, bad arguments with
+    MOE_EINVAL, and T = 0 returns MOE_OK, all without a device (none in this process)."""
+    d = M.dims(2880, 2880, 32, 4)
+    assert M.MOE_FORWARD_NOALLOC_MAX_WORKSPACE == 16 << 20
+    big = 340                                   # the first T past the limit at this shape
+    assert M.moe_workspace_bytes(d, big) > M.MOE_FORWARD_NOALLOC_MAX_WORKSPACE >= M.moe_workspace_bytes(d, big - 1)
+    w = M.moe_weights(256, 256, 256, 256)
+    args = lambda T, y=256: (ctypes.byref(d), T, 256, 256, 256, ctypes.byref(w), y, M.MOE_FP32, None)
+    assert L.moe_forward_noalloc(*args(big)) == M.MOE_EWORKSPACE
+    assert L.moe_forward_noalloc(*args(8, y=None)) == M.MOE_EINVAL
+    assert L.moe_forward_noalloc(*args(8, y=258)) == M.MOE_EINVAL            # misaligned output
+    assert L.moe_forward_noalloc(*args(-1)) == M.MOE_EINVAL
+    assert L.moe_forward_noalloc(*args(0)) == M.MOE_OK
