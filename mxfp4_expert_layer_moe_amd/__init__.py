@@ -97,6 +97,18 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+def _dense_decode(T: int, E: int, k: int, D: int) -> bool:
+    """Whether moe_forward takes the dense decode path (the library's rule, for tests and reports):
+    at most 32 tokens and 32 experts, at most 6 assignments per expert, d_model up to 2880, and an
+    expert left untouched with probability (1 - k/E)^T <= 0.15."""
+    if T < 1 or T > 32 or E > 32 or T * k > 6 * E or D // 64 > 45:
+        return False
+    untouched = 1.0
+    for _ in range(T):
+        untouched *= 1.0 - k / E
+    return untouched <= 0.15
+
+
 def _p(t):
     """Device/host pointer of a tensor, ndarray, int or None."""
     if t is None:

@@ -18,7 +18,7 @@ PEAKS_LIB = os.path.join(LIBDIR, "libmoe_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "pack.hip", "gemm.hip", "gemm_prefill.hip", "combine.hip",
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "pack.hip", "gemm.hip", "gemm_prefill.hip", "gemm_dense.hip", "combine.hip",
            "norm.hip"]
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled: plain fp32 VALU only

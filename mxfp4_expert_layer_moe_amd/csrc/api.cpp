@@ -61,7 +61,10 @@ WsLayout ws_layout(const moe_dims* d, int32_t T, int af = kActSplit6) {
   L.inv = take(n * 4);
   L.tiles = take(tile_table_bytes(d, T));
   L.xpack = take((size_t)T * act_row_bytes_af(af, d->d_model));
-  L.hpack = take(n * act_row_bytes_af(af, d->d_ff));
+  // the dense decode path writes h for every (expert, token) pair
+  const size_t hrows = af == kActSplit6 && dense_decode(T, d->n_experts, d->top_k, d->d_model)
+                           ? (n > (size_t)T * d->n_experts ? n : (size_t)T * d->n_experts) : n;
+  L.hpack = take(hrows * act_row_bytes_af(af, d->d_ff));
   L.yperm = take(n * (size_t)d->d_model * 2);
   L.route = take(route_workspace_bytes(T, d->d_model, d->n_experts));
   L.total = o;
@@ -115,6 +118,21 @@ moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const u
   uint8_t* hpack = base + L.hpack;
   _Float16* yperm = (_Float16*)(base + L.yperm);
   const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
+  if (af == kActSplit6 && dense_decode(T, E, k, D)) {
+    // routing off the weight stream: logits, then the dense gate/up with the selection beside it,
+    // then the down projection of each expert's selected tokens (rows at t*k + j)
+    DenseSelection sel = {x, w_router, b_router, nullptr, nullptr, nullptr, idx, w, counts, offsets, perm, inv, tiles};
+    if (launch_route_partials(T, D, E, x, w_router, base + L.route, xpack, stream, &sel)) return MOE_EHIP;
+    if (launch_gemm_dense_gate_up(T, D, I, E, k, d->swiglu_limit, xpack, wts->gu_codes, wts->gu_scales, hpack, &sel,
+                                  stream))
+      return MOE_EHIP;
+    // the routed down projection, reading packed h row e*T + t for each tile row
+    if (launch_gemm(1, T, D, I, E, k, d->swiglu_limit, hpack, tiles, wts->dn_codes, wts->dn_scales, w, yperm, stream,
+                    kActSplit6, /*out_assign=*/1, /*dense_rows=*/1))
+      return MOE_EHIP;
+    if (launch_combine(T, D, k, yperm, nullptr, residual, y, y_dtype == MOE_BF16, stream)) return MOE_EHIP;
+    return MOE_OK;
+  }
   if (launch_route_front(T, D, E, k, x, w_router, b_router, idx, w, base + L.route, xpack, counts, offsets, perm,
                          inv, tiles, stream, af))
     return MOE_EHIP;

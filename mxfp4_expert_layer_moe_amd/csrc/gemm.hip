@@ -32,6 +32,7 @@ namespace moe {
 struct GemmArgs {
   int T, k, E, K, KT, KG, units, out_K;
   int out_assign;                                       // down: rows to their assignment index
+  int dense_rows;                                       // down: packed h row e*T + t (dense decode path)
   float limit;
   const uint8_t* a_packed;
   const int32_t* tiles;
@@ -88,7 +89,10 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
   const int i = lane & 31;
   const int half = lane >> 5;
   const bool valid = i < nrows;
-  if (tid < nrows) srow[tid] = STAGE == 0 ? tile[4 + tid] / g.k : p0 + tid;
+  // activation row of each tile row: gate/up the token's x row; down the grouped row of h, or on the
+  // dense decode path (whose gate/up wrote h for every expert and token) row e*T + t
+  if (tid < nrows)
+    srow[tid] = STAGE == 0 ? tile[4 + tid] / g.k : (g.dense_rows ? e * g.T + tile[4 + tid] / g.k : p0 + tid);
   // down: each row's gate weight topk_w[perm[p]], fetched now so it is there for the epilogue
   float wl = 0.0f;
   int al = 0;
@@ -320,11 +324,12 @@ constexpr int kDownP = 8;       // and k-tiles in flight
 
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
-                       void* out, hipStream_t s, int af, int out_assign) {
+                       void* out, hipStream_t s, int af, int out_assign, int dense_rows) {
   if (T == 0) return hipSuccess;
   GemmArgs g;
   g.T = T; g.k = k; g.E = E; g.limit = limit;
   g.out_assign = stage == 1 && out_assign;
+  g.dense_rows = stage == 1 && dense_rows;
   g.a_packed = a_packed; g.tiles = tiles; g.codes = codes; g.scales = scales;
   g.topk_w = topk_w; g.out = out;
   const int N = stage == 0 ? 2 * I : D;
@@ -337,9 +342,11 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   g.scales_per_expert = w_scales_per_expert(N, g.K);
   const long long n_assign = (long long)T * k;
   // batches with many rows per expert (128-row tiles) go to the prefill kernel
-  if (tile_rows(n_assign, E) != 8)
+  if (tile_rows(n_assign, E) != 8) {
+    if (g.dense_rows) return hipErrorInvalidValue;     // the dense decode path uses 8-row tiles only
     return launch_gemm_prefill(stage, T, D, I, E, k, limit, a_packed, tiles, codes, scales, topk_w, out, s, af,
                                out_assign);
+  }
   // decode-sized batches (8-row tiles whose activations fit LDS whole)
   const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));
   // the model's K = 2880 (45 k-tiles): fully unrolled k-loop

@@ -141,10 +141,12 @@ hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* coun
                           int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s);
 hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipStream_t s, int af = kActSplit6);
 // out_assign (down stage only): row p of the output goes to the row of its assignment perm[p]
-// = t*k + j instead of row p, so the combine reads a token's rows without the inverse permutation
+// = t*k + j instead of row p, so the combine reads a token's rows without the inverse permutation.
+// dense_rows (down stage only, 8-row tiles): the activation of tile row p is packed h row e*T + t
+// (the dense decode path's gate/up output) instead of row p.
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
-                       void* out, hipStream_t s, int af = kActSplit6, int out_assign = 0);
+                       void* out, hipStream_t s, int af = kActSplit6, int out_assign = 0, int dense_rows = 0);
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
                                const uint8_t* scales, const float* topk_w, void* out, hipStream_t s,
@@ -153,6 +155,46 @@ hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, flo
 hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, const uint16_t* residual,
                           void* y, int y_bf16, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// The dense decode path of the whole-layer entry points (gemm_dense.hip): at most 32 tokens and
+// 32 experts, d_model up to 2880, and so many assignments that an expert goes untouched with
+// probability (1 - k/E)^T <= 0.15.  The gate/up projection then runs over every (expert, token) pair with the
+// selection and grouping in the same launch; the down projection is the routed one.
+// ---------------------------------------------------------------------------
+constexpr int kDenseMaxKT = 45;              // the dense gate/up stages all of K in LDS: up to 2880
+__host__ inline bool dense_decode(int T, int E, int k, int D) {
+  if (T < 1 || T > 32 || E > 32 || (long long)T * k > (long long)kSmallTileLimit * E) return false;
+  if (D / kKTile > kDenseMaxKT) return false;
+  double untouched = 1.0;
+  for (int t = 0; t < T; ++t) untouched *= 1.0 - (double)k / E;
+  return untouched <= 0.15;
+}
+// router partials of a forward pass (launch_route_partials), which the dense launch selects from,
+// and where the selection and the grouping go
+struct DenseSelection {
+  const uint16_t* x;
+  const float* wr;
+  const float* br;
+  const double* logit;
+  const float* xsq;
+  const float* wsq;
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  int32_t* tiles;
+};
+// The router logits of a forward pass as K-partials, with the activation split of x into xpack in
+// the same launch (no selection).  Fills sel's logit, xsq and wsq.
+hipError_t launch_route_partials(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
+                                 hipStream_t s, DenseSelection* sel);
+// the dense gate/up projection: packed x (T rows) -> packed h rows e*T + t for every expert e,
+// with the selection and the grouping of every token (sel) in the same launch
+hipError_t launch_gemm_dense_gate_up(int T, int D, int I, int E, int k, float limit, const uint8_t* xpack,
+                                     const uint8_t* codes, const uint8_t* scales, void* hpack,
+                                     const DenseSelection* sel, hipStream_t s);
 hipError_t launch_rmsnorm(int T, int D, const uint16_t* x, const float* gamma, float eps, uint16_t* xn,
                           hipStream_t s);
 

@@ -54,12 +54,22 @@ def _layer(inp):
 
 
 def _full_check(name, inp, tokens=None):
+    """Every intermediate of the step calls against the oracle, then moe_forward (the whole-layer
+    entry point: fused routing front end, the dense decode path where it applies, rows written at
+    their assignment index) equal to the step calls bit for bit."""
+    from mxfp4_expert_layer_moe_amd import _dense_decode
     print(f"[parity] start {name} T={inp.T} D={inp.D} E={inp.E} k={inp.k} I={inp.I}", flush=True)
     t0 = time.time()
     layer = _layer(inp)
     g = parity.run_gpu(layer)
     o = parity.oracle_with_adoption(inp, g["idx"], tokens=tokens)
     stats = parity.compare(inp, g, o)
+    y32 = layer.forward(bf16=False).clone()
+    y16 = layer.forward(bf16=True).clone()
+    torch.cuda.synchronize()
+    assert np.array_equal(y32.cpu().numpy(), g["y32"]), "moe_forward differs from the step calls"
+    assert np.array_equal(y16.view(torch.int16).cpu().numpy().view(np.uint16), g["y16"])
+    stats["forward_path"] = "dense" if _dense_decode(inp.T, inp.E, inp.k, inp.D) else "routed"
     stats["seconds"] = round(time.time() - t0, 1)
     _record(name, stats)
     return layer, g
@@ -94,6 +104,12 @@ SMALL = {
     "selection_one_workgroup_at_limit": dict(cfg=dict(T=32, D=64, E=32, k=4, I=64, seed=62)),
     "tokens_33_general_selection": dict(cfg=dict(T=33, D=64, E=32, k=4, I=64, seed=63)),
     "experts_33_general_selection": dict(cfg=dict(T=32, D=64, E=33, k=4, I=64, seed=57)),
+    # the dense decode path of moe_forward (every (expert, token) pair through gate/up, the selection
+    # beside it): used from (1 - k/E)^T <= 0.15; at 14 tokens of 32 experts it is not, at 15 it is
+    "dense_threshold_routed": dict(cfg=dict(T=14, D=128, E=32, k=4, I=128, seed=66)),
+    "dense_threshold_dense": dict(cfg=dict(T=15, D=128, E=32, k=4, I=128, seed=67)),
+    "dense_ragged_k_tail": dict(cfg=dict(T=29, D=320, E=20, k=3, I=192, seed=68)),
+    "dense_model_width_20_tokens": dict(cfg=dict(T=20, D=2880, E=32, k=4, I=2880, seed=69)),
     # full 8-row tiles whose activations do not fit LDS whole (K = 3072 and 4096): the small-batch
     # GEMMs stage K in chunks and their weight ring runs across the chunk boundaries
     "chunked_k_full_small_tiles": dict(cfg=dict(T=24, D=3072, E=8, k=2, I=4096, seed=64), bias="onehot3"),
@@ -172,12 +188,7 @@ def test_full_size_workload(cfg):
     t0 = time.time()
     inp = synth.make_inputs(cfg)
     print(f"[parity] config {cfg} generated in {time.time() - t0:.1f}s", flush=True)
-    layer, g = _full_check(f"config{cfg}", inp)
-    y32 = layer.forward(bf16=False).clone()
-    y16 = layer.forward(bf16=True).clone()
-    torch.cuda.synchronize()
-    assert np.array_equal(y32.cpu().numpy(), g["y32"]), "moe_forward differs from the step calls"
-    assert np.array_equal(y16.view(torch.int16).cpu().numpy().view(np.uint16), g["y16"])
+    _full_check(f"config{cfg}", inp)
 
 
 @pytest.mark.parametrize("T", [24, 300])           # one-workgroup selection / 16-token workgroups
