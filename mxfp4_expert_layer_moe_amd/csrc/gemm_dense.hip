@@ -19,10 +19,10 @@
 // path; the rows of unselected pairs are computed and never read.
 //
 // Layout: the (expert, output unit) pairs (a unit is a gate/up pair of 32-column weight tiles) are
-// dealt 16 to a workgroup of 16 wavefronts (four per SIMD), one pair per wavefront; the activation
-// rows are the same x for every expert.  At d_ff = 2880 (90 units) 32 experts give 180 workgroups,
-// which with the selection workgroup (dispatched first) are all resident at once, one per compute
-// unit (the staged rows take most of its LDS).  A workgroup stages the T token rows of all of K in
+// dealt 12 to a workgroup of 12 wavefronts (three per SIMD), one pair per wavefront; the activation
+// rows are the same x for every expert.  At d_ff = 2880 (90 units) 32 experts give 240 workgroups,
+// which with the selection workgroup (dispatched first, 768 threads in two passes of 24 tokens) are
+// all resident at once, one per compute unit (the staged rows take most of its LDS).  A workgroup stages the T token rows of all of K in
 // LDS once (the
 // packed rows' 112-byte chunks cut to their 104 used bytes: 32 x 45 x 104 = 146 KB at K = 2880; a
 // row stride of an odd number of 8-byte words puts 16 consecutive rows of one 8-byte read on
@@ -63,9 +63,9 @@ struct DenseArgs {
 };
 
 constexpr int kDenseTokens = 32;            // rows of the dense tile: every token of the batch
-constexpr int kDenseWaves = 16;             // wavefronts per workgroup (four per SIMD), one (expert, unit) each
+constexpr int kDenseWaves = 12;             // wavefronts per workgroup (three per SIMD), one (expert, unit) each
 constexpr int kDenseThreads = kDenseWaves * 64;
-static_assert(kDenseThreads == 1024, "the selection workgroup holds 32 tokens x 32 experts");
+
 constexpr int kDenseChunk = 104;            // staged bytes per row and k-tile (the used bytes, 8-aligned)
 constexpr int kDenseStageBytes = kDenseTokens * kDenseMaxKT * kDenseChunk;   // 149760
 
@@ -74,12 +74,12 @@ __global__ __launch_bounds__(kDenseThreads) void expert_gemm_dense_kernel(DenseA
   constexpr int NB = 2;                     // a SwiGLU pair of 32-column tiles per wavefront
   static_assert(P % 4 == 0, "prefetch depth covers whole scale groups");
   __shared__ __attribute__((aligned(16))) uint8_t sA[kDenseStageBytes];
-  static_assert(sizeof(SelectSmem<32>) <= kDenseStageBytes, "the selection borrows the staging buffer");
+  static_assert(sizeof(SelectSmem) <= kDenseStageBytes, "the selection borrows the staging buffer");
   if (blockIdx.x == 0) {
     // the selection and the grouping of all tokens, beside the dense gate/up projection
-    select_small<32>(*reinterpret_cast<SelectSmem<32>*>(sA), 0, g.T, g.D, g.E, g.k, g.x, g.wr, g.br, g.logit,
-                     g.xsq, g.wsq, g.sel_idx, g.sel_w, nullptr, g.bm, g.slots, g.counts, g.offsets, g.perm, g.inv,
-                     g.tiles);
+    select_small<kDenseThreads>(*reinterpret_cast<SelectSmem*>(sA), g.T, g.D, g.E, g.k, g.x, g.wr, g.br, g.logit,
+                                g.xsq, g.wsq, g.sel_idx, g.sel_w, nullptr, g.bm, g.slots, g.counts, g.offsets, g.perm,
+                                g.inv, g.tiles);
     return;
   }
   const int tid = threadIdx.x;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kDenseThreads) void expert_gemm_dense_kernel(DenseA
   }
 }
 
-constexpr int kDenseP = 4;        // weight k-tiles in flight per wavefront (16 wavefronts per compute unit)
+constexpr int kDenseP = 8;        // weight k-tiles in flight per wavefront
 
 hipError_t launch_gemm_dense_gate_up(int T, int D, int I, int E, int k, float limit, const uint8_t* xpack,
                                      const uint8_t* codes, const uint8_t* scales, void* hpack,
@@ -279,7 +279,7 @@ hipError_t launch_gemm_dense_gate_up(int T, int D, int I, int E, int k, float li
   g.bm = tile_rows(n, E);
   g.slots = (int)tile_slots(n, E);
   g.counts = sel->counts; g.offsets = sel->offsets; g.perm = sel->perm; g.inv = sel->inv; g.tiles = sel->tiles;
-  // workgroup 0: the selection; then the (expert, unit) pairs, 16 per workgroup
+  // workgroup 0: the selection; then the (expert, unit) pairs, 12 per workgroup
   const dim3 grid(1 + (E * g.units + kDenseWaves - 1) / kDenseWaves);
   if (g.KT == kDenseMaxKT) expert_gemm_dense_kernel<kDenseP, kDenseMaxKT><<<grid, dim3(kDenseThreads), 0, s>>>(g);
   else expert_gemm_dense_kernel<kDenseP, 0><<<grid, dim3(kDenseThreads), 0, s>>>(g);

@@ -556,9 +556,9 @@ __global__ __launch_bounds__(1024) void route_select_small_kernel(
     float* __restrict__ out_logits, int bm, int slots, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
     int32_t* __restrict__ tiles) {
-  __shared__ __align__(16) SelectSmem<32> smem;
-  select_small<32>(smem, 0, T, D, E, k, x, wr, br, logit, xsq, wsq, out_idx, out_w, out_logits, bm, slots, counts,
-                   offsets, perm, inv, tiles);
+  __shared__ __align__(16) SelectSmem smem;
+  select_small<1024>(smem, T, D, E, k, x, wr, br, logit, xsq, wsq, out_idx, out_w, out_logits, bm, slots, counts,
+                     offsets, perm, inv, tiles);
 }
 
 static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,

@@ -64,36 +64,39 @@ __device__ __forceinline__ int half_scan(int v) {
   return v;
 }
 
-// One thread per (token t, expert e) pair of NT consecutive tokens from token0: local token
-// tl = thread / 32, e = thread % 32, so a wavefront holds two tokens, one per half.  Partial tiles
-// -> scores in LDS; each pair's rank among its token's live experts (higher score first, lower id
-// first on equal scores) selects the top k; the same band test, exact re-scoring and gate
-// arithmetic as select_token.  With perm given it then groups the assignments by expert straight
-// from the per-token selection masks: the position of (t, e) in expert e's segment is the number
-// of earlier tokens that chose e.  Used by route_select_small_kernel and by the first workgroup of
-// the dense decode path's gate/up launch (gemm_dense.hip), both with NT = 32.
+// The selection of up to 32 tokens by one workgroup of THREADS threads, one thread per (token t,
+// expert e) pair: t = p * (THREADS / 32) + thread / 32 in pass p, e = thread % 32, so a wavefront
+// holds two tokens, one per half.  1024 threads take all 32 tokens in one pass, 768 in two.
+// Partial tiles -> scores in LDS; each pair's rank among its token's live experts (higher score
+// first, lower id first on equal scores) selects the top k; the same band test, exact re-scoring
+// and gate arithmetic as select_token.  With perm given it then groups the assignments by expert
+// straight from the per-token selection masks: the position of (t, e) in expert e's segment is the
+// number of earlier tokens that chose e.  Used by route_select_small_kernel (1024 threads) and by
+// the first workgroup of the dense decode path's gate/up launch (gemm_dense.hip, 768 threads); the
+// arithmetic of every pair is the same in both.
 // The selection's LDS, provided by the caller (the dense decode launch lends it its staging buffer).
-template <int NT>
 struct SelectSmem {
-  double lt[NT][34];          // [token][expert] scores (bias included); rows 16-byte aligned
-  double kth[NT], top[NT];    // k-th and largest selected score per token
-  float xn2[NT], wn2[32];
-  float ex_l[NT][33];         // gate numerators
-  uint32_t smask[NT];         // selected experts per token (bit e)
-  uint32_t fmask[NT];         // candidates of the flagged tokens (0: not flagged)
+  double lt[32][34];          // [token][expert] scores (bias included); rows 16-byte aligned
+  double kth[32], top[32];    // k-th and largest selected score per token
+  float xn2[32], wn2[32];
+  float ex_l[32][33];         // gate numerators
+  uint32_t smask[32];         // selected experts per token (bit e)
+  uint32_t fmask[32];         // candidates of the flagged tokens (0: not flagged)
 };
 
-template <int NT>
+template <int THREADS>
 __device__ __forceinline__ void select_small(
-    SelectSmem<NT>& S, int token0, int T, int D, int E, int k, const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    SelectSmem& S, int T, int D, int E, int k, const uint16_t* __restrict__ x, const float* __restrict__ wr,
     const float* __restrict__ br, const double* __restrict__ logit, const float* __restrict__ xsq,
     const float* __restrict__ wsq, int32_t* __restrict__ out_idx, float* __restrict__ out_w,
     float* __restrict__ out_logits, int bm, int slots, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
     int32_t* __restrict__ tiles) {
-  constexpr int kThreads = NT * 32;
-  constexpr int kWaves = kThreads / 64;
-  static_assert(NT == 32, "one workgroup of 32 tokens (the grouping reads every token's selection)");
+  constexpr int NT = 32;                      // tokens
+  constexpr int TPP = THREADS / 32;           // tokens per pass
+  constexpr int NP = (NT + TPP - 1) / TPP;    // passes
+  constexpr int kWaves = THREADS / 64;
+  static_assert(THREADS % 64 == 0 && THREADS >= 64, "whole wavefronts, the norms need 64 threads");
   auto& lt = S.lt;
   auto& xn2 = S.xn2;
   auto& wn2 = S.wn2;
@@ -104,154 +107,191 @@ __device__ __forceinline__ void select_small(
   auto& fmask = S.fmask;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int tl = tid >> 5, e = tid & 31;
-  const int t = token0 + tl;
+  const int e = tid & 31;
   const int hshift = lane & 32;               // this token's half of the wavefront ballots
-  const bool live = t < T && e < E;
-  {
-    // the kSmallKW partials in order, then the bias; every load is issued before the sums
-    if (live) {
-      double p[kSmallKW];
+  int tk[NP];
+  bool live[NP];
 #pragma unroll
-      for (int q = 0; q < kSmallKW; ++q) p[q] = logit[((size_t)q * T + t) * 32 + e];
+  for (int p = 0; p < NP; ++p) {
+    tk[p] = p * TPP + (tid >> 5);
+    live[p] = tk[p] < NT && tk[p] < T && e < E;
+  }
+  // the kSmallKW partials in order, then the bias; every load is issued before the sums
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (live[p]) {
+      const int t = tk[p];
+      double q16[kSmallKW];
+#pragma unroll
+      for (int q = 0; q < kSmallKW; ++q) q16[q] = logit[((size_t)q * T + t) * 32 + e];
       const float b = br[e];
       double s = 0.0;
 #pragma unroll
-      for (int q = 0; q < kSmallKW; ++q) s += p[q];
+      for (int q = 0; q < kSmallKW; ++q) s += q16[q];
       const double v = s + (double)b;
-      lt[tl][e] = v;
+      lt[t][e] = v;
       if (out_logits) out_logits[(size_t)t * E + e] = (float)v;
     }
-    if (tid < 32 + NT) {
-      // threads 0..31: squared norms of the expert rows; 32..32+NT-1: of the token rows
-      const int r = tid < 32 ? tid : tid - 32;
-      const bool in = tid < 32 ? r < E : token0 + r < T;
-      float p[kSmallKW];
+  }
+  if (tid < 64) {
+    // threads 0..31: squared norms of the expert rows; 32..63: of the token rows
+    const int r = tid & 31;
+    const bool in = tid < 32 ? r < E : r < T;
+    float q16[kSmallKW];
 #pragma unroll
-      for (int q = 0; q < kSmallKW; ++q)
-        p[q] = !in ? 0.0f : (tid < 32 ? wsq[(size_t)q * 32 + r] : xsq[(size_t)q * T + token0 + r]);
-      float v = 0.0f;
+    for (int q = 0; q < kSmallKW; ++q)
+      q16[q] = !in ? 0.0f : (tid < 32 ? wsq[(size_t)q * 32 + r] : xsq[(size_t)q * T + r]);
+    float v = 0.0f;
 #pragma unroll
-      for (int q = 0; q < kSmallKW; ++q) v += p[q];
-      (tid < 32 ? wn2 : xn2)[r] = v;
-    }
+    for (int q = 0; q < kSmallKW; ++q) v += q16[q];
+    (tid < 32 ? wn2 : xn2)[r] = v;
   }
   __syncthreads();
   // rank among the live experts of the token
-  const double v0 = live ? lt[tl][e] : 0.0;
-  int rank = 0;
-  {
-    const double2* row = reinterpret_cast<const double2*>(&lt[t < T ? tl : 0][0]);
+  double v0[NP], v[NP];
+  int rank[NP];
+  bool sel[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int t = tk[p];
+    v0[p] = live[p] ? lt[t][e] : 0.0;
+    rank[p] = 0;
+    const double2* row = reinterpret_cast<const double2*>(&lt[t < T && t < NT ? t : 0][0]);
 #pragma unroll
     for (int j2 = 0; j2 < 16; ++j2) {
       const double2 w = row[j2];                          // one 16-byte read per two experts
       const int j = 2 * j2;
-      rank += (j < E && (w.x > v0 || (w.x == v0 && j < e))) ? 1 : 0;
-      rank += (j + 1 < E && (w.y > v0 || (w.y == v0 && j + 1 < e))) ? 1 : 0;
+      rank[p] += (j < E && (w.x > v0[p] || (w.x == v0[p] && j < e))) ? 1 : 0;
+      rank[p] += (j + 1 < E && (w.y > v0[p] || (w.y == v0[p] && j + 1 < e))) ? 1 : 0;
     }
+    sel[p] = live[p] && rank[p] < k;
+    if (sel[p] && rank[p] == k - 1) kth[t] = v0[p];
   }
-  bool sel = live && rank < k;
-  if (sel && rank == k - 1) kth[tl] = v0;
   __syncthreads();
   // band test: any other live expert within the band of the k-th score flags the token
   float wmax2 = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) wmax2 = fmaxf(wmax2, wn2[j]);             // zero past E
-  bool cand = false;
-  if (live) {
-    const double band = kBandRel * sqrt((double)xn2[tl] * (double)wmax2);
-    cand = sel || v0 >= kth[tl] - band;
+  bool cand[NP], flagged[NP];
+  uint32_t cm[NP];
+  bool any_flagged = false;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    cand[p] = false;
+    if (live[p]) {
+      const double band = kBandRel * sqrt((double)xn2[tk[p]] * (double)wmax2);
+      cand[p] = sel[p] || v0[p] >= kth[tk[p]] - band;
+    }
+    cm[p] = (uint32_t)(__ballot(cand[p]) >> hshift);
+    flagged[p] = live[p] && __popc(cm[p]) > k;
+    any_flagged = any_flagged || flagged[p];
+    v[p] = v0[p];
   }
-  const uint32_t cm = (uint32_t)(__ballot(cand) >> hshift);
-  const bool flagged = live && __popc(cm) > k;
   // flagged tokens: re-score every (token, candidate) pair exactly, the pairs dealt to the
   // workgroup's wavefronts in token-then-expert order (one wavefront per score), then rank again
   // among the candidates.  The whole section is skipped when no token is flagged.
-  double v = v0;
-  if (__syncthreads_or(flagged)) {
-    if (e == 0) fmask[tl] = flagged ? cm : 0u;
+  if (__syncthreads_or(any_flagged)) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (e == 0 && tk[p] < NT) fmask[tk[p]] = flagged[p] ? cm[p] : 0u;
     __syncthreads();
     const int wave = tid >> 6;
     int i = 0;
-    for (int ttl = 0; ttl < NT && token0 + ttl < T; ++ttl) {
-      uint32_t m = fmask[ttl];                           // uniform
+    for (int tt = 0; tt < NT && tt < T; ++tt) {
+      uint32_t m = fmask[tt];                            // uniform
       while (m) {
         const int j = __ffs(m) - 1;
         m &= m - 1;
         if (i % kWaves == wave) {
-          const double sc = score_f64(x + (size_t)(token0 + ttl) * D, wr + (size_t)j * D, (double)br[j], D, lane);
-          if (lane == 0) lt[ttl][j] = sc;
+          const double sc = score_f64(x + (size_t)tt * D, wr + (size_t)j * D, (double)br[j], D, lane);
+          if (lane == 0) lt[tt][j] = sc;
         }
         ++i;
       }
     }
     __syncthreads();
   }
-  if (flagged) {
-    v = cand ? lt[tl][e] : -INFINITY;
-    rank = 0;
+  uint32_t sm[NP];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const double w = lt[tl][j];
-      rank += (((cm >> j) & 1u) && (w > v || (w == v && j < e))) ? 1 : 0;
+  for (int p = 0; p < NP; ++p) {
+    const int t = tk[p];
+    if (flagged[p]) {
+      v[p] = cand[p] ? lt[t][e] : -INFINITY;
+      int r = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const double w = lt[t][j];
+        r += (((cm[p] >> j) & 1u) && (w > v[p] || (w == v[p] && j < e))) ? 1 : 0;
+      }
+      rank[p] = r;
+      sel[p] = cand[p] && r < k;
     }
-    sel = cand && rank < k;
+    if (sel[p] && rank[p] == 0) top[t] = v[p];
+    sm[p] = (uint32_t)(__ballot(sel[p]) >> hshift);
+    if (live[p] && e == 0) smask[t] = sm[p];
   }
-  if (sel && rank == 0) top[tl] = v;
-  const uint32_t sm = (uint32_t)(__ballot(sel) >> hshift);
-  if (live && e == 0) smask[tl] = sm;
   __syncthreads();
   // gates: softmax over the selected scores, exponentials of the gaps in fp32, summed in
   // ascending expert id; slots in ascending expert id
-  float g = 0.0f;
-  if (sel) {
-    g = expf((float)(v - top[tl]));
-    ex_l[tl][e] = g;
+  float g[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    g[p] = 0.0f;
+    if (sel[p]) {
+      g[p] = expf((float)(v[p] - top[tk[p]]));
+      ex_l[tk[p]][e] = g[p];
+    }
   }
   __syncthreads();
-  if (sel) {
-    float sum = 0.0f;
-    for (uint32_t m = sm; m; m &= m - 1) sum += ex_l[tl][__ffs(m) - 1];
-    const int slot = __popc(sm & ((1u << e) - 1u));
-    out_idx[(size_t)t * k + slot] = e;
-    out_w[(size_t)t * k + slot] = g / sum;
-  }
-  if constexpr (NT == 32) {
-    if (!perm) return;
-    // grouping: tokens before t that chose e, and the total per expert
-    int before = 0, total = 0;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int bit = j < T ? (int)((smask[j] >> e) & 1u) : 0;
-      total += bit;
-      before += j < t ? bit : 0;
+  for (int p = 0; p < NP; ++p) {
+    if (sel[p]) {
+      const int t = tk[p];
+      float sum = 0.0f;
+      for (uint32_t m = sm[p]; m; m &= m - 1) sum += ex_l[t][__ffs(m) - 1];
+      const int slot = __popc(sm[p] & ((1u << e) - 1u));
+      out_idx[(size_t)t * k + slot] = e;
+      out_w[(size_t)t * k + slot] = g[p] / sum;
     }
-    // exclusive scans over the 32 experts of this half-wavefront: segment offsets, first tiles
-    const int ntl = (total + bm - 1) / bm;
-    const int inc = half_scan(total), tinc = half_scan(ntl);
-    const int off = inc - total, tst = tinc - ntl;
-    const int used = __shfl(tinc, 31, 32);                 // tiles in use
-    const int n = T * k;
-    if (sel && off + before < n && tst + before / bm < slots) {   // always true; keeps stores in bounds
-      const int slot = __popc(sm & ((1u << e) - 1u));
+  }
+  if (!perm) return;
+  // grouping: the total per expert (the same in every pass: it depends on e only) and, per pass,
+  // the tokens before t that chose e
+  int total = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) total += j < T ? (int)((smask[j] >> e) & 1u) : 0;
+  // exclusive scans over the 32 experts of this half-wavefront: segment offsets, first tiles
+  const int ntl = (total + bm - 1) / bm;
+  const int inc = half_scan(total), tinc = half_scan(ntl);
+  const int off = inc - total, tst = tinc - ntl;
+  const int used = __shfl(tinc, 31, 32);                 // tiles in use
+  const int n = T * k;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int t = tk[p];
+    int before = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) before += j < T && j < t ? (int)((smask[j] >> e) & 1u) : 0;
+    if (sel[p] && off + before < n && tst + before / bm < slots) {   // always true; keeps stores in bounds
+      const int slot = __popc(sm[p] & ((1u << e) - 1u));
       const int a = t * k + slot, pos = off + before;
       perm[pos] = a;
       inv[a] = pos;
       tiles[(size_t)(tst + before / bm) * tile_ints(bm) + 4 + before % bm] = a;
     }
-    // totals, offsets and the headers of expert e's tiles from the first half-wavefront; the
-    // headers of the empty slots past the last tile from everyone
-    if (tid < 32 && e < E) {
-      counts[e] = total;
-      offsets[e] = off;
-      if (e == E - 1) offsets[E] = n;
-      for (int i = 0; i < ntl && tst + i < slots; ++i)
-        *reinterpret_cast<int4*>(tiles + (size_t)(tst + i) * tile_ints(bm)) =
-            make_int4(e, off + i * bm, min(bm, total - i * bm), used);
-    }
-    for (int sl = used + tid; sl < slots; sl += kThreads)
-      *reinterpret_cast<int4*>(tiles + (size_t)sl * tile_ints(bm)) = make_int4(-1, 0, 0, used);
   }
+  // totals, offsets and the headers of expert e's tiles from the first half-wavefront; the
+  // headers of the empty slots past the last tile from everyone
+  if (tid < 32 && e < E) {
+    counts[e] = total;
+    offsets[e] = off;
+    if (e == E - 1) offsets[E] = n;
+    for (int i = 0; i < ntl && tst + i < slots; ++i)
+      *reinterpret_cast<int4*>(tiles + (size_t)(tst + i) * tile_ints(bm)) =
+          make_int4(e, off + i * bm, min(bm, total - i * bm), used);
+  }
+  for (int sl = used + tid; sl < slots; sl += THREADS)
+    *reinterpret_cast<int4*>(tiles + (size_t)sl * tile_ints(bm)) = make_int4(-1, 0, 0, used);
 }
 
 }  // namespace moe
