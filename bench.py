@@ -358,6 +358,31 @@ def _time_steps(fn, copies, warmup: int, steps: int) -> float:
     return a.elapsed_time(b) / steps
 
 
+def _time_alternating(fa, fb, copies, warmup: int, steps: int, rounds: int = 8) -> tuple:
+    """Medians of ms per call of fa and of fb, timed in alternating stretches of steps // rounds calls
+    (so a drift of the clock affects both alike), after `warmup` untimed calls of each."""
+    import torch
+    stream = torch.cuda.current_stream()
+    L = len(copies)
+    for s in range(warmup):
+        fa(copies[s % L])
+        fb(copies[s % L])
+    n = max(1, steps // rounds)
+    ta, tb = [], []
+    for r in range(rounds):
+        for fn, out in ((fa, ta), (fb, tb)):
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for s in range(n):
+                fn(copies[s % L])
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / n)
+    med = lambda v: sorted(v)[len(v) // 2]
+    return med(ta), med(tb)
+
+
 def default_counts(ci: int):
     """(warm-up, timed steps) of a workload: about 0.2 s of warm-up so the clock has settled."""
     decode = synth_configs()[ci]["T"] <= 64
@@ -428,10 +453,15 @@ class Workload:
                     alg_flops_per_launch=int(gu_flops), fractions=fr)
         rec["gate_up_kernel"] = roof
         if block:
-            b_ms = _time_steps(lambda w: layer.block_forward(weights=w), copies, warmup, steps)
+            # the layer and the block timed in alternating stretches, medians of each
+            l_ms, b_ms = _time_alternating(lambda w: layer.forward(weights=w),
+                                           lambda w: layer.block_forward(weights=w), copies, warmup, 4 * steps)
             rec["block"] = {"what": "RMSNorm -> MoE layer -> residual add (moe_block_forward)",
                             "ms_per_step": round(b_ms, 5), "tokens_per_s": round(T / (b_ms * 1e-3), 1),
-                            "extra_ms_over_layer": round(b_ms - ms, 5)}
+                            "layer_ms_per_step_alternating": round(l_ms, 5),
+                            "extra_ms_over_layer": round(b_ms - l_ms, 5),
+                            "timing": "layer and block in 8 alternating stretches of 4 * steps / 8 calls each, "
+                                      "medians"}
         if act4:
             a_ms = _time_steps(lambda w: layer.forward_act4(weights=w), copies, warmup, steps)
             rec["act4"] = {"what": "MXFP4 activations into the expert GEMMs (moe_forward_act4; a lower-precision "

@@ -147,7 +147,8 @@ size_t moe_workspace_bytes(const moe_dims* dims, int32_t T);
  *   topk_w    out [T][top_k] fp32: softmax of the selected logits (same order)
  *   logits    out [T][n_experts] fp32 or NULL: router logits (rounded from float64)
  *   ws        device scratch of at least moe_route_workspace_bytes(dims, T)
- *             bytes, 256-byte aligned (float64 partial logits of the K slices)
+ *             bytes, 256-byte aligned (float64 partial logits: of groups of 256
+ *             K values for at most 32 tokens and 32 experts, of K slices beyond)
  * Logits are accumulated on the matrix cores (exact bf16 x split-fp32
  * products, 16-term fp32 partial sums, float64 accumulation); any expert
  * within 36 eps32 ||x_t|| max_e ||w_e|| of the k-th largest (twice the error

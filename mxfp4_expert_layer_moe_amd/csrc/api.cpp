@@ -105,7 +105,8 @@ size_t block_xn_bytes(const moe_dims* d, int32_t T) {
 // residual, the combine adds it to the output.
 moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const uint16_t* residual,
                         const float* w_router, const float* b_router, const moe_weights* wts, void* y,
-                        moe_dtype y_dtype, uint8_t* base, hipStream_t stream, int af = kActSplit6) {
+                        moe_dtype y_dtype, uint8_t* base, hipStream_t stream, int af = kActSplit6,
+                        const FrontNorm* fn = nullptr) {
   const WsLayout L = ws_layout(d, T, af);
   int32_t* idx = (int32_t*)(base + L.idx);
   float* w = (float*)(base + L.w);
@@ -118,11 +119,17 @@ moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const u
   uint8_t* hpack = base + L.hpack;
   _Float16* yperm = (_Float16*)(base + L.yperm);
   const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
+  if (fn && !(af == kActSplit6 && dense_decode(T, E, k, D))) {
+    // the normalisation as a launch of its own, into x
+    if (launch_rmsnorm(T, D, fn->raw, fn->gamma, (float)fn->eps, const_cast<uint16_t*>(x), stream)) return MOE_EHIP;
+    fn = nullptr;
+  }
   if (af == kActSplit6 && dense_decode(T, E, k, D)) {
-    // routing off the weight stream: logits, then the dense gate/up with the selection beside it,
-    // then the down projection of each expert's selected tokens (rows at t*k + j)
-    DenseSelection sel = {x, w_router, b_router, nullptr, nullptr, nullptr, idx, w, counts, offsets, perm, inv, tiles};
-    if (launch_route_partials(T, D, E, x, w_router, base + L.route, xpack, stream, &sel)) return MOE_EHIP;
+    // routing off the weight stream: the packed rows, then the dense gate/up with the scores and
+    // the selection beside it, then the down projection of each expert's selected tokens (rows at
+    // t*k + j)
+    DenseSelection sel = {x, w_router, b_router, idx, w, counts, offsets, perm, inv, tiles};
+    if (launch_front_pack(T, D, x, xpack, kActSplit6, stream, fn)) return MOE_EHIP;
     if (launch_gemm_dense_gate_up(T, D, I, E, k, d->swiglu_limit, xpack, wts->gu_codes, wts->gu_scales, hpack, &sel,
                                   stream))
       return MOE_EHIP;
@@ -134,7 +141,7 @@ moe_status forward_impl(const moe_dims* d, int32_t T, const uint16_t* x, const u
     return MOE_OK;
   }
   if (launch_route_front(T, D, E, k, x, w_router, b_router, idx, w, base + L.route, xpack, counts, offsets, perm,
-                         inv, tiles, stream, af))
+                         inv, tiles, stream, af, fn))
     return MOE_EHIP;
   if (launch_gemm(0, T, D, I, E, k, d->swiglu_limit, xpack, tiles, wts->gu_codes, wts->gu_scales, nullptr, hpack,
                   stream, af))
@@ -234,11 +241,12 @@ moe_status moe_route(const moe_dims* d, int32_t T, const void* x_bf16, const flo
   moe_status st = check_dims(d);
   if (st != MOE_OK) return st;
   if ((st = check_T(d, T)) != MOE_OK) return st;
-  if (!x_bf16 || !w_router || !b_router || !topk_idx || !topk_w || (T > 0 && !ws)) return MOE_EINVAL;
+  const size_t need = route_workspace_bytes(T, d->d_model, d->n_experts);
+  if (!x_bf16 || !w_router || !b_router || !topk_idx || !topk_w || (need > 0 && !ws)) return MOE_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(b_router, 4) || !aligned(topk_idx, 4) ||
       !aligned(topk_w, 4) || (logits && !aligned(logits, 4)) || !aligned(ws, kAlignWs))
     return MOE_EINVAL;
-  if (ws_bytes < route_workspace_bytes(T, d->d_model, d->n_experts)) return MOE_EWORKSPACE;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
   if (T == 0) return MOE_OK;
   return hip_status(launch_route(T, d->d_model, d->n_experts, d->top_k, (const uint16_t*)x_bf16, w_router,
                                  b_router, topk_idx, topk_w, logits, ws, stream));
@@ -405,10 +413,12 @@ moe_status moe_block_forward(const moe_dims* d, int32_t T, const void* x_bf16, c
   const size_t xn_bytes = block_xn_bytes(d, T);
   if (ws_bytes < xn_bytes + ws_layout(d, T).total) return MOE_EWORKSPACE;
   if (T == 0) return MOE_OK;
+  // the normalised rows go to the start of the workspace: written by the routing launch where
+  // it folds the RMSNorm in, else by a launch of their own
   uint16_t* xn = (uint16_t*)ws;
-  if (launch_rmsnorm(T, d->d_model, (const uint16_t*)x_bf16, gamma, eps, xn, stream)) return MOE_EHIP;
+  const FrontNorm fn = {(const uint16_t*)x_bf16, gamma, (double)eps};
   return forward_impl(d, T, xn, (const uint16_t*)x_bf16, w_router, b_router, wts, y, y_dtype,
-                      (uint8_t*)ws + xn_bytes, stream);
+                      (uint8_t*)ws + xn_bytes, stream, kActSplit6, &fn);
 }
 
 // ---- host-only ---------------------------------------------------------------

@@ -8,8 +8,9 @@
 // computes h = bf16(silu(clamp(g)) * clamp(u)) ("From GPT-2 to gpt-oss", section 3, Swish/SwiGLU;
 // clamp at swiglu_limit) for every (expert, token) pair, each expert's T tokens filling the rows of
 // one 32-row matrix tile, and writes packed h row e*T + t.  The first workgroup of the same launch
-// runs the selection of the top-k experts, their gates and the grouping by expert (select_small,
-// the code of the routed path's selection kernel), which only the next launch needs: the routed
+// scores the router and runs the selection of the top-k experts, their gates and the grouping by
+// expert (select_small, the code of the routed path's selection kernel), which only the next launch
+// needs: the routed
 // small-batch down projection (gemm.hip), reading h row e*T + t for each row of its tiles.
 //
 // Each row goes through exactly the instruction sequence of the routed small-batch kernel: per
@@ -49,9 +50,6 @@ struct DenseArgs {
   const uint16_t* x;
   const float* wr;
   const float* br;
-  const double* logit;
-  const float* xsq;
-  const float* wsq;
   int32_t* sel_idx;
   float* sel_w;
   int bm, slots;                    // the grouping's tile height and slot count
@@ -74,12 +72,14 @@ __global__ __launch_bounds__(kDenseThreads) void expert_gemm_dense_kernel(DenseA
   constexpr int NB = 2;                     // a SwiGLU pair of 32-column tiles per wavefront
   static_assert(P % 4 == 0, "prefetch depth covers whole scale groups");
   __shared__ __attribute__((aligned(16))) uint8_t sA[kDenseStageBytes];
-  static_assert(sizeof(SelectSmem) <= kDenseStageBytes, "the selection borrows the staging buffer");
+  using Scores = ScoreSmem<kDenseWaves>;
+  constexpr size_t kScoresAt = (sizeof(SelectSmem) + 15) / 16 * 16;
+  static_assert(kScoresAt + sizeof(Scores) <= kDenseStageBytes, "the selection borrows the staging buffer");
   if (blockIdx.x == 0) {
-    // the selection and the grouping of all tokens, beside the dense gate/up projection
-    select_small<kDenseThreads>(*reinterpret_cast<SelectSmem*>(sA), g.T, g.D, g.E, g.k, g.x, g.wr, g.br, g.logit,
-                                g.xsq, g.wsq, g.sel_idx, g.sel_w, nullptr, g.bm, g.slots, g.counts, g.offsets, g.perm,
-                                g.inv, g.tiles);
+    // the scores, the selection and the grouping of all tokens, beside the dense gate/up projection
+    select_small<kDenseThreads, true>(*reinterpret_cast<SelectSmem*>(sA), reinterpret_cast<Scores*>(sA + kScoresAt),
+                                nullptr, nullptr, g.T, g.D, g.E, g.k, g.x, g.wr, g.br, g.sel_idx, g.sel_w, nullptr,
+                                g.bm, g.slots, g.counts, g.offsets, g.perm, g.inv, g.tiles);
     return;
   }
   const int tid = threadIdx.x;
@@ -273,7 +273,7 @@ hipError_t launch_gemm_dense_gate_up(int T, int D, int I, int E, int k, float li
   g.scales_per_expert = w_scales_per_expert(2 * I, D);
   g.out = hpack;
   g.D = D;
-  g.x = sel->x; g.wr = sel->wr; g.br = sel->br; g.logit = sel->logit; g.xsq = sel->xsq; g.wsq = sel->wsq;
+  g.x = sel->x; g.wr = sel->wr; g.br = sel->br;
   g.sel_idx = sel->idx; g.sel_w = sel->w;
   const long long n = (long long)T * k;
   g.bm = tile_rows(n, E);

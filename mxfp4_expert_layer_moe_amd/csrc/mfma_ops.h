@@ -225,9 +225,16 @@ __device__ __forceinline__ void store_fp4_block(uint8_t* row, int b, const Fp4Bl
   chunk[32 + (b & 1)] = (uint8_t)q.scale;
 }
 
+// Store the 32 values of block b of activation row `row` (bf16 values held in fp32) in the packed
+// activation format: the hi/lo FP6 split (af = kActSplit6) or the MXFP4 quantization (af = kActFp4).
+__device__ __forceinline__ void pack_block_values(const float (&v)[32], int K, long long row, int b,
+                                                  uint8_t* __restrict__ packed, int af = kActSplit6) {
+  if (af == kActFp4) store_fp4_block(packed + (size_t)row * act4_row_bytes(K), b, quant_fp4x32(v));
+  else store_fp6_block(packed + (size_t)row * act_row_bytes(K), b, split_fp6x32(v));
+}
+
 // Pack block `blk` (= row * K/32 + b) of bf16 rows [rows][K] (16-byte aligned) in one lane:
-// four 16-byte loads, then the hi/lo FP6 split (af = kActSplit6) or the MXFP4 quantization
-// (af = kActFp4), the stores.  Lanes past the last block do nothing.
+// four 16-byte loads, then pack_block_values.  Lanes past the last block do nothing.
 __device__ __forceinline__ void pack_block_lane(const uint16_t* __restrict__ a, int K, long long nblocks,
                                                 long long blk, uint8_t* __restrict__ packed, int af = kActSplit6) {
   if (blk >= nblocks) return;
@@ -246,8 +253,7 @@ __device__ __forceinline__ void pack_block_lane(const uint16_t* __restrict__ a, 
       v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
   }
-  if (af == kActFp4) store_fp4_block(packed + (size_t)row * act4_row_bytes(K), b, quant_fp4x32(v));
-  else store_fp6_block(packed + (size_t)row * act_row_bytes(K), b, split_fp6x32(v));
+  pack_block_values(v, K, row, b, packed, af);
 }
 
 }  // namespace moe

@@ -132,10 +132,19 @@ hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const flo
 // The whole routing front end of a forward pass: logits (with the activation split of x
 // into xpack done by extra workgroups), selection and grouping; small batches fuse the
 // selection and the grouping into one workgroup.
+// The RMSNorm in front of the layer, folded into the first launch of the dense decode path: the
+// launch reads the raw rows, normalises them with the standalone RMSNorm's arithmetic and writes
+// the normalised rows to its x argument.
+struct FrontNorm {
+  const uint16_t* raw;
+  const float* gamma;
+  double eps;
+};
+
 hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
                               int32_t* idx, float* w, void* ws, uint8_t* xpack, int32_t* counts,
                               int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s,
-                              int af = kActSplit6);
+                              int af = kActSplit6, const FrontNorm* fn = nullptr);
 size_t route_workspace_bytes(int T, int D, int E);
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s);
@@ -169,15 +178,12 @@ __host__ inline bool dense_decode(int T, int E, int k, int D) {
   for (int t = 0; t < T; ++t) untouched *= 1.0 - (double)k / E;
   return untouched <= 0.15;
 }
-// router partials of a forward pass (launch_route_partials), which the dense launch selects from,
-// and where the selection and the grouping go
+// the router inputs of a forward pass, which the dense launch scores and selects from, and where
+// the selection and the grouping go
 struct DenseSelection {
   const uint16_t* x;
   const float* wr;
   const float* br;
-  const double* logit;
-  const float* xsq;
-  const float* wsq;
   int32_t* idx;
   float* w;
   int32_t* counts;
@@ -186,12 +192,12 @@ struct DenseSelection {
   int32_t* inv;
   int32_t* tiles;
 };
-// The router logits of a forward pass as K-partials, with the activation split of x into xpack in
-// the same launch (no selection).  Fills sel's logit, xsq and wsq.
-hipError_t launch_route_partials(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
-                                 hipStream_t s, DenseSelection* sel);
+// The first launch of the dense decode path: x split into xpack, one workgroup per row; with fn,
+// the normalised rows written to x and packed instead.
+hipError_t launch_front_pack(int T, int D, const uint16_t* x, uint8_t* xpack, int af, hipStream_t s,
+                             const FrontNorm* fn = nullptr);
 // the dense gate/up projection: packed x (T rows) -> packed h rows e*T + t for every expert e,
-// with the selection and the grouping of every token (sel) in the same launch
+// with the scores, the selection and the grouping of every token (sel) in the same launch
 hipError_t launch_gemm_dense_gate_up(int T, int D, int I, int E, int k, float limit, const uint8_t* xpack,
                                      const uint8_t* codes, const uint8_t* scales, void* hpack,
                                      const DenseSelection* sel, hipStream_t s);

@@ -7,23 +7,20 @@
 // A = 0.7 NN2 + 0.3 NN4; gpt-oss keeps 4 of 32 / 128).
 //
 // Kernels:
-//  route_logits (at most 32 tokens and 32 experts, i.e. decode): 16 workgroups of 16 wavefronts
-//     split the K loop of the (32-token, 32-expert) tile sixteen ways, so a decode step spreads
-//     over sixteen compute units; each wavefront issues the loads of four k-steps before their
-//     matrix instructions.  Logits run on the bf16 matrix cores: x is bf16 and the fp32 router
-//     weight is split exactly into three bf16 terms (truncation: hi + mid + lo == w), so every
-//     product is exact.  Each 16-wide k-step's three MFMAs start from zero and their small fp32
-//     result is added into a float64 accumulator, so the only fp32 roundings are those of
-//     16-term partial sums.  The 16 K-partials of a workgroup are summed in LDS in a fixed
-//     order and its float64 tile is written to the workspace, with the squared norms of the x
-//     rows and w rows.
-//  route_logits_wide (larger batches): the same arithmetic per k-step, one workgroup of 8
-//     wavefronts per (64-token block, 32-expert tile, K slice); the router chunk of each 64-wide
+//  route_groups (at most 32 tokens and 32 experts, i.e. decode): the scores of every (token,
+//     expert) pair on the bf16 matrix cores (x and the exact three-term bf16 split of the fp32
+//     router weight, k-step tiles added in float64) in groups of 16 k-steps, one workgroup per
+//     group, one k-step per wavefront, so a decode step spreads over about a dozen compute units;
+//     with the activation split of x for the gate/up GEMM in the same launch.
+//  route_select_small (the same batches): one workgroup adds the groups, ranks each pair among its
+//     token's scores, applies the band test, exact re-scoring and gate arithmetic below, and for
+//     the layer forward groups the assignments by expert.  The dense decode path runs the same code
+//     in the first workgroup of its gate/up launch, computing the groups itself (same arithmetic).
+//  front_pack (the dense decode path): one workgroup per token row splits the row into the packed
+//     activation format, normalising it first when the RMSNorm in front of the layer is folded in.
+//  route_logits_wide (larger batches): per k-step the arithmetic of small_scores, one workgroup of
+//     8 wavefronts per (64-token block, 32-expert tile, K slice); the router chunk of each 64-wide
 //     round is split once into an LDS ring shared by both 32-token tiles.
-//  route_select_small (with route_logits): one workgroup, one thread per (token, expert) pair;
-//     sums the partial tiles into an LDS logit table, ranks each pair among its token's scores,
-//     applies the same rules and arithmetic as route_select, and for the layer forward groups
-//     the assignments by expert in the same workgroup.
 //  route_select: one wavefront per token.  Sums the KW partial tiles in a
 //     fixed order (deterministic), adds the bias, takes the top-k by
 //     wave-wide arg-max (larger logit first, lower id on ties).  If any other
@@ -36,27 +33,20 @@
 //     selection at any input scale.  Gates are the softmax of the selected
 //     float64 scores, with the exponentials of their gaps taken in fp32.
 #include "mfma_ops.h"
+#include "norm_body.h"
 #include "select_body.h"
 
 namespace moe {
 
-constexpr int kRouteTokens = 32;
-
-__device__ inline uint32_t trunc_bf16_bits(float v) { return __float_as_uint(v) & 0xFFFF0000u; }
-
-// ---- work split and workspace layout (shared by the ABI layer) --------------------
-constexpr int kLogitWaves = 16;
-constexpr int kLogitBatch = 4;                 // k-steps whose loads are issued together
-
 static bool route_small(int T, int E) { return T <= 32 && E <= 32; }
 
+// ---- work split and workspace layout (shared by the ABI layer) --------------------
 // Larger batches: route_logits_wide_kernel, one workgroup per (64-token block, 32-expert tile)
 // and K slice.
 constexpr int kWideWaves = 8;                  // 2 token tiles x 4 k-step lanes
 constexpr int kWideTokens = 64;
 
 static int route_kw(int T, int E) {
-  if (route_small(T, E)) return kSmallKW;
   const int blocks = ((T + kWideTokens - 1) / kWideTokens) * ((E + 31) / 32);
   return blocks <= 128 ? 4 : (blocks <= 256 ? 2 : 1);     // about two workgroups per compute unit
 }
@@ -65,90 +55,31 @@ struct RouteWs {
   size_t logit, xsq, wsq, total;
 };
 
-static RouteWs route_ws_layout(int T, int E) {
+__host__ __device__ inline int score_groups(int D) { return (D / 16 + kGroupSteps - 1) / kGroupSteps; }
+
+// The larger batches: the K-partials of the scores.  The small batches: the group sums of
+// route_groups ([group][32][32] float64 in logit, [group][2][32] fp32 norms in xsq).
+static RouteWs route_ws_layout(int T, int D, int E) {
+  RouteWs L = {0, 0, 0, 0};
+  if (route_small(T, E)) {
+    const size_t G = (size_t)score_groups(D);
+    L.xsq = G * 1024 * 8;
+    L.total = L.xsq + (G * 64 * 4 + 255) / 256 * 256;
+    L.wsq = L.total;
+    return L;
+  }
   const int KW = route_kw(T, E);
   const size_t epad = (size_t)((E + 31) / 32) * 32;
-  RouteWs L;
-  L.logit = 0;
   L.xsq = ((size_t)KW * T * epad * 8 + 255) / 256 * 256;
   L.wsq = L.xsq + ((size_t)KW * T * 4 + 255) / 256 * 256;
   L.total = L.wsq + ((size_t)KW * epad * 4 + 255) / 256 * 256;
   return L;
 }
 
-size_t route_workspace_bytes(int T, int D, int E) {
-  (void)D;
-  return T > 0 ? route_ws_layout(T, E).total : 0;
-}
-
-// One wavefront's share of a (32-token, 32-expert) logit tile: the k-steps s_first, s_first +
-// s_stride, ... (16 K values each), BATCH of them loaded before their matrix instructions.
-// Lane l: token row / expert row l % 32, K half l / 32.  Returns the float64 tile partial in the
-// MFMA layout and the lane's partial squared norms of its x row (xs) and w row (sq).
-template <int BATCH>
-__device__ __forceinline__ void logit_steps(int T, int D, int E, const uint16_t* __restrict__ x,
-                                            const float* __restrict__ wr, int tok, int e, int half, int s_first,
-                                            int s_stride, double (&accd)[16], float& sq, float& xs) {
-  const int nsteps = D / 16;
-  const uint16_t* xa = x + (size_t)tok * D + 8 * half;
-  const float* wb = wr + (size_t)e * D + 8 * half;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) accd[r] = 0.0;
-  sq = 0.0f;
-  xs = 0.0f;
-  for (int s0 = s_first; s0 < nsteps; s0 += BATCH * s_stride) {
-    uint4 xu[BATCH];
-    float4 wa[BATCH], wc[BATCH];
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int s = s0 + b * s_stride;
-      xu[b] = make_uint4(0, 0, 0, 0);
-      wa[b] = make_float4(0.f, 0.f, 0.f, 0.f);
-      wc[b] = wa[b];
-      if (s < nsteps) {
-        if (tok < T) xu[b] = *reinterpret_cast<const uint4*>(xa + 16 * s);
-        if (e < E) {
-          wa[b] = *reinterpret_cast<const float4*>(wb + 16 * s);
-          wc[b] = *reinterpret_cast<const float4*>(wb + 16 * s + 4);
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      if (s0 + b * s_stride >= nsteps) break;             // uniform
-      const uint32_t uw[4] = {xu[b].x, xu[b].y, xu[b].z, xu[b].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(uw[i] << 16), hi = __uint_as_float(uw[i] & 0xFFFF0000u);
-        xs += lo * lo + hi * hi;
-      }
-      const v8bf a = __builtin_bit_cast(v8bf, xu[b]);
-      const float wv[8] = {wa[b].x, wa[b].y, wa[b].z, wa[b].w, wc[b].x, wc[b].y, wc[b].z, wc[b].w};
-      uint32_t hb[8], mb[8], lb[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sq += wv[i] * wv[i];
-        const uint32_t h = trunc_bf16_bits(wv[i]);
-        const float r1 = wv[i] - __uint_as_float(h);            // exact
-        const uint32_t m = trunc_bf16_bits(r1);
-        const float r2 = r1 - __uint_as_float(m);                // exact, <= 8 significant bits
-        hb[i] = h >> 16; mb[i] = m >> 16; lb[i] = __float_as_uint(r2) >> 16;
-      }
-      const uint4 hu = make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16));
-      const uint4 mu = make_uint4(mb[0] | (mb[1] << 16), mb[2] | (mb[3] << 16), mb[4] | (mb[5] << 16), mb[6] | (mb[7] << 16));
-      const uint4 lu = make_uint4(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16));
-      v16f t = {};
-      t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, lu), t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, mu), t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, hu), t, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) accd[r] += (double)t[r];
-    }
-  }
-}
+size_t route_workspace_bytes(int T, int D, int E) { return T > 0 ? route_ws_layout(T, D, E).total : 0; }
 
 // Exact split of n fp32 router weights into three bf16 terms by truncation (hi + mid + lo == w),
-// as in logit_steps, packed two per dword in element order.
+// as in score_step_tile, packed two per dword in element order.
 template <int N>
 __device__ __forceinline__ void split_terms(const float (&wv)[N], uint32_t (&hu)[N / 2], uint32_t (&mu)[N / 2],
                                             uint32_t (&lu)[N / 2]) {
@@ -169,77 +100,128 @@ __device__ __forceinline__ void split_terms(const float (&wv)[N], uint32_t (&hu)
   }
 }
 
-// Fixed-order sum of the 16 wavefronts' partial tiles: slot s = p_s + p_(s+8) is left in
-// red[s] (the caller adds slots 0..7 in order); the squared-norm partials go to rsq.
-__device__ __forceinline__ void reduce_partials(const double (&accd)[16], float sq, float xs,
-                                                double (&red)[8][32][33], float (&rsq)[kLogitWaves][2][32],
-                                                int wave, int half, int row) {
-  sq += __shfl_xor(sq, 32);
-  xs += __shfl_xor(xs, 32);
-  if (half == 0) {
-    rsq[wave][0][row] = xs;
-    rsq[wave][1][row] = sq;
-  }
-  if (wave < 8) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * half + (r & 3)][row] = accd[r];
-  }
-  __syncthreads();
-  if (wave >= 8) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave - 8][8 * (r >> 2) + 4 * half + (r & 3)][row] += accd[r];
-  }
-  __syncthreads();
-}
-
-// Workgroups past the logit tiles (when xpack is given) split x into the packed activation
-// format for the gate/up GEMM instead: one 32-value block per lane.
-__global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, int D, int E, int KW,
-                                                                         const uint16_t* __restrict__ x,
-                                                                         const float* __restrict__ wr,
-                                                                         double* __restrict__ logit,
-                                                                         float* __restrict__ xsq,
-                                                                         float* __restrict__ wsq,
-                                                                         int logit_wgs,
-                                                                         uint8_t* __restrict__ xpack, int af) {
-  __shared__ double red[8][32][33];          // K-partials: waves 0..7, then 8..15 added in place
-  __shared__ float rsq[kLogitWaves][2][32];  // partial ||x_t||^2 (0) and ||w_e||^2 (1)
-  if ((int)blockIdx.x >= logit_wgs) {        // activation split, one block per lane (no barriers)
-    const long long blk = (long long)(blockIdx.x - logit_wgs) * (kLogitWaves * 64) + threadIdx.x;
+// ---- the small batches' launches before the selection ---------------------------------
+// route_groups: workgroup g < ngroups (16 wavefronts) takes score group g of small_scores,
+// wavefront j the k-step 16g + j, and adds its tiles in the group's tree through LDS: p_j + p_(j+8)
+// in place, then the eight sums left to right; the norm terms the same way.  Writes the group sums
+// to gpart / gnorm.  Workgroups past the groups (when xpack is given) split x into the packed
+// activation format, one 32-value block per lane.
+__global__ __launch_bounds__(1024) void route_groups_kernel(int T, int D, int E, const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ wr, int ngroups,
+                                                            double* __restrict__ gpart, float* __restrict__ gnorm,
+                                                            uint8_t* __restrict__ xpack, int af) {
+  __shared__ double red[8][32][33];
+  __shared__ float rn[8][2][32];
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= ngroups) {                   // activation split (no barriers)
+    const long long blk = (long long)(blockIdx.x - ngroups) * 1024 + tid;
     pack_block_lane(x, D, (long long)T * (D / kBlock), blk, xpack, af);
     return;
   }
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nte = (E + 31) / 32;
-  const int kw = blockIdx.x % KW;
-  const int nt = (blockIdx.x / KW) % nte;
-  const int tt = blockIdx.x / (KW * nte);
-  const int epad = nte * 32;
-  const int kstride = kLogitWaves * KW;
-  const int row = lane & 31;
-  const int half = lane >> 5;
-  const int e = nt * 32 + row;
-  const int tok = tt * kRouteTokens + row;
-  double accd[16];
-  float sq, xs;
-  logit_steps<kLogitBatch>(T, D, E, x, wr, tok, e, half, kw * kLogitWaves + wave, kstride, accd, sq, xs);
-  reduce_partials(accd, sq, xs, red, rsq, wave, half, row);
-  double* lt = logit + ((size_t)kw * T + (size_t)tt * kRouteTokens) * epad + nt * 32;
-  for (int j = tid; j < 32 * 32; j += kLogitWaves * 64) {
-    const int m = j >> 5, c = j & 31;
-    double v = red[0][m][c];
+  const int j = tid >> 6;
+  const int s = blockIdx.x * kGroupSteps + j;
+  const int nsteps = D / 16;
+  const ScoreStep L = score_step_load(T, D, E, x, wr, s, nsteps, lane);
+  double p[16];
+  float xs, ws;
+  score_step_f64(L, s < nsteps, p, xs, ws);
+  const int col = lane & 31;
+  if (j < 8) {
 #pragma unroll
-    for (int s = 1; s < 8; ++s) v += red[s][m][c];
-    if (tt * kRouteTokens + m < T) lt[(size_t)m * epad + c] = v;
+    for (int r = 0; r < 16; ++r) red[j][score_row(r, lane)][col] = p[r];
+    if (lane < 32) {
+      rn[j][0][lane] = xs;
+      rn[j][1][lane] = ws;
+    }
   }
+  __syncthreads();
+  if (j >= 8) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[j - 8][score_row(r, lane)][col] += p[r];
+    if (lane < 32) {
+      rn[j - 8][0][lane] = __fadd_rn(rn[j - 8][0][lane], xs);
+      rn[j - 8][1][lane] = __fadd_rn(rn[j - 8][1][lane], ws);
+    }
+  }
+  __syncthreads();
+  const int i = tid >> 5, c = tid & 31;               // one element of the 32 x 32 tile per thread
+  double v = red[0][i][c];
+#pragma unroll
+  for (int q = 1; q < 8; ++q) v += red[q][i][c];
+  gpart[(size_t)blockIdx.x * 1024 + tid] = v;
   if (tid < 64) {
-    const int which = tid >> 5, r = tid & 31;
-    float v = 0.0f;
-    for (int w = 0; w < kLogitWaves; ++w) v += rsq[w][which][r];
-    if (which == 0 && nt == 0 && tt * kRouteTokens + r < T) xsq[(size_t)kw * T + tt * kRouteTokens + r] = v;
-    if (which == 1 && tt == 0) wsq[(size_t)kw * epad + nt * 32 + r] = v;
+    const int which = tid >> 5;                        // 0: x norms, 1: w norms
+    float n = rn[0][which][c];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) n = __fadd_rn(n, rn[q][which][c]);
+    gnorm[(size_t)blockIdx.x * 64 + tid] = n;
+  }
+}
+
+// front_pack (the dense decode path): one workgroup of kNormThreads per token row.  With gamma (the
+// RMSNorm in front of the layer folded in): r_t (row_rms_inv, the standalone RMSNorm's order), each
+// thread's normalised 8-value chunk to xn and to an LDS copy of the row, then thread i packs block
+// i of the normalised row (all of its 32 values in one lane); without, thread i packs block i of x.
+constexpr int kFrontMaxD = 8192;               // the LDS row copy (rows wider go without it)
+__global__ __launch_bounds__(kNormThreads) void front_pack_kernel(int D, const uint16_t* __restrict__ x,
+                                                                  const float* __restrict__ gamma, double eps,
+                                                                  uint16_t* __restrict__ xn,
+                                                                  uint8_t* __restrict__ xpack, int af) {
+  __shared__ double part[kNormThreads / 64];
+  __shared__ __align__(16) uint4 srow[kFrontMaxD / 8];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nb = D / kBlock, nc = D / 8;
+  auto pack = [&](int b, const uint4* src) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 q = src[i];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+    pack_block_values(v, D, row, b, xpack, af);
+  };
+  const uint16_t* xr = x + (size_t)row * D;
+  const uint4* x4 = reinterpret_cast<const uint4*>(xr);
+  if (!gamma) {
+    for (int b = tid; b < nb; b += kNormThreads) {
+      uint4 q[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) q[c] = x4[4 * b + c];
+      pack(b, q);
+    }
+    return;
+  }
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+  const float4 ga = tid < nc ? g4[2 * tid] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 gb = tid < nc ? g4[2 * tid + 1] : ga;
+  uint4 held;
+  const double r = row_rms_inv(xr, D, eps, part, held);
+  uint4* o4 = reinterpret_cast<uint4*>(xn + (size_t)row * D);
+  const bool staged = D <= kFrontMaxD;           // uniform
+  for (int c = tid; c < nc; c += kNormThreads) {
+    const uint4 q = c == tid ? chunk_rmsnorm(held, r, ga, gb) : chunk_rmsnorm(x4[c], r, gamma, c);
+    o4[c] = q;
+    if (staged) srow[c] = q;
+  }
+  if (staged) {
+    __syncthreads();
+    for (int b = tid; b < nb; b += kNormThreads) pack(b, srow + 4 * b);
+  } else {
+    __threadfence_block();                        // this workgroup's own xn stores, read back below
+    __syncthreads();
+    for (int b = tid; b < nb; b += kNormThreads) {
+      uint4 q[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) q[c] = o4[4 * b + c];
+      pack(b, q);
+    }
   }
 }
 
@@ -248,7 +230,7 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(int T, i
 // every thread loads one float4 of the round's 32 x 64 router chunk, splits it into the three
 // bf16 terms and stores them in an LDS ring of two rounds, so each router weight is split once
 // per 64 tokens and read from LDS by both token tiles; wavefront (tile q, lane group j) takes
-// k-step j of every round for tile q.  The arithmetic per k-step is that of logit_steps: three
+// k-step j of every round for tile q.  The arithmetic per k-step is that of logit_compute: three
 // bf16 MFMAs from zero, their fp32 result added into float64.  The four k-step lanes' partial
 // tiles are summed in LDS in a fixed order.  Loads run two rounds ahead.
 constexpr int kWideRowBytes = 128 + 16;        // one expert row of a round in bf16, padded
@@ -547,71 +529,83 @@ __global__ __launch_bounds__(256) void route_select_kernel(int T, int D, int E, 
 
 // ---- batches of at most 32 tokens and 32 experts --------------------------------------
 
-// At most 32 tokens and 32 experts: one workgroup selects for every token and (perm given)
-// groups the assignments.
+// At most 32 tokens and 32 experts: one workgroup adds the score groups of route_groups, selects
+// for every token and (perm given) groups the assignments.
 __global__ __launch_bounds__(1024) void route_select_small_kernel(
     int T, int D, int E, int k, const uint16_t* __restrict__ x, const float* __restrict__ wr,
-    const float* __restrict__ br, const double* __restrict__ logit, const float* __restrict__ xsq,
-    const float* __restrict__ wsq, int32_t* __restrict__ out_idx, float* __restrict__ out_w,
+    const float* __restrict__ br, int32_t* __restrict__ out_idx, float* __restrict__ out_w,
     float* __restrict__ out_logits, int bm, int slots, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ tiles) {
+    int32_t* __restrict__ tiles, const double* __restrict__ gpart, const float* __restrict__ gnorm) {
   __shared__ __align__(16) SelectSmem smem;
-  select_small<1024>(smem, T, D, E, k, x, wr, br, logit, xsq, wsq, out_idx, out_w, out_logits, bm, slots, counts,
-                     offsets, perm, inv, tiles);
+  select_small<1024, false>(smem, nullptr, gpart, gnorm, T, D, E, k, x, wr, br, out_idx, out_w, out_logits, bm, slots,
+                     counts, offsets, perm, inv, tiles);
 }
 
-static hipError_t launch_logits(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
-                                int af,
-                                hipStream_t s, double** logit, float** xsq, float** wsq, int* KW) {
+
+
+hipError_t launch_front_pack(int T, int D, const uint16_t* x, uint8_t* xpack, int af, hipStream_t s,
+                             const FrontNorm* fn) {
+  if (T == 0) return hipSuccess;
+  front_pack_kernel<<<dim3((unsigned)T), dim3(kNormThreads), 0, s>>>(
+      D, fn ? fn->raw : x, fn ? fn->gamma : nullptr, fn ? fn->eps : 0.0, fn ? const_cast<uint16_t*>(x) : nullptr,
+      xpack, af);
+  return hipGetLastError();
+}
+
+// Small batches: the score groups (and the packed rows when xpack is given) in one launch.
+static hipError_t launch_groups(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
+                                int af, hipStream_t s, const double** gpart, const float** gnorm) {
+  const RouteWs L = route_ws_layout(T, D, E);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  double* gp = reinterpret_cast<double*>(base + L.logit);
+  float* gn = reinterpret_cast<float*>(base + L.xsq);
+  const int ngroups = score_groups(D);
+  const long long pack_wgs = xpack ? ((long long)T * (D / kBlock) + 1023) / 1024 : 0;
+  route_groups_kernel<<<dim3((unsigned)(ngroups + pack_wgs)), dim3(1024), 0, s>>>(T, D, E, x, wr, ngroups, gp, gn,
+                                                                                  xpack, af);
+  *gpart = gp;
+  *gnorm = gn;
+  return hipGetLastError();
+}
+
+// Larger batches: the K-partial score tiles, with the activation split of x into xpack (when
+// given) in the same launch.
+static hipError_t launch_logits_wide(int T, int D, int E, const uint16_t* x, const float* wr, void* ws,
+                                     uint8_t* xpack, int af, hipStream_t s, double** logit, float** xsq,
+                                     float** wsq, int* KW) {
   *KW = route_kw(T, E);
-  const RouteWs L = route_ws_layout(T, E);
+  const RouteWs L = route_ws_layout(T, D, E);
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   *logit = reinterpret_cast<double*>(base + L.logit);
   *xsq = reinterpret_cast<float*>(base + L.xsq);
   *wsq = reinterpret_cast<float*>(base + L.wsq);
   const long long pack_blocks = xpack ? (long long)T * (D / kBlock) : 0;
   const int nte = (E + 31) / 32;
-  if (route_small(T, E)) {
-    const int logit_wgs = ((T + kRouteTokens - 1) / kRouteTokens) * nte * *KW;
-    const long long pack_wgs = (pack_blocks + kLogitWaves * 64 - 1) / (kLogitWaves * 64);
-    route_logits_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kLogitWaves * 64), 0, s>>>(
-        T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
-  } else {
-    const int logit_wgs = ((T + kWideTokens - 1) / kWideTokens) * nte * *KW;
-    const long long pack_wgs = (pack_blocks + kWideWaves * 64 - 1) / (kWideWaves * 64);
-    route_logits_wide_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kWideWaves * 64), 0, s>>>(
-        T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
-  }
+  const int logit_wgs = ((T + kWideTokens - 1) / kWideTokens) * nte * *KW;
+  const long long pack_wgs = (pack_blocks + kWideWaves * 64 - 1) / (kWideWaves * 64);
+  route_logits_wide_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kWideWaves * 64), 0, s>>>(
+      T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
   return hipGetLastError();
-}
-
-hipError_t launch_route_partials(int T, int D, int E, const uint16_t* x, const float* wr, void* ws, uint8_t* xpack,
-                                 hipStream_t s, DenseSelection* sel) {
-  double* logit;
-  float *xsq, *wsq;
-  int KW;
-  const hipError_t err = launch_logits(T, D, E, x, wr, ws, xpack, kActSplit6, s, &logit, &xsq, &wsq, &KW);
-  sel->logit = logit;
-  sel->xsq = xsq;
-  sel->wsq = wsq;
-  return err;
 }
 
 hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
                         int32_t* idx, float* w, float* logits, void* ws, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (route_small(T, E)) {
+    const double* gp;
+    const float* gn;
+    hipError_t err = launch_groups(T, D, E, x, wr, ws, nullptr, kActSplit6, s, &gp, &gn);
+    if (err != hipSuccess) return err;
+    route_select_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(T, D, E, k, x, wr, br, idx, w, logits, 0, 0, nullptr,
+                                                             nullptr, nullptr, nullptr, nullptr, gp, gn);
+    return hipGetLastError();
+  }
   double* logit;
   float *xsq, *wsq;
   int KW;
-  hipError_t err = launch_logits(T, D, E, x, wr, ws, nullptr, kActSplit6, s, &logit, &xsq, &wsq, &KW);
+  hipError_t err = launch_logits_wide(T, D, E, x, wr, ws, nullptr, kActSplit6, s, &logit, &xsq, &wsq, &KW);
   if (err != hipSuccess) return err;
-  if (route_small(T, E)) {
-    route_select_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(T, D, E, k, x, wr, br, logit, xsq, wsq, idx, w,
-                                                             logits, 0, 0, nullptr, nullptr, nullptr, nullptr,
-                                                             nullptr);
-    return hipGetLastError();
-  }
   route_select_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq, idx, w,
                                                               logits);
   return hipGetLastError();
@@ -620,20 +614,24 @@ hipError_t launch_route(int T, int D, int E, int k, const uint16_t* x, const flo
 hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, const float* wr, const float* br,
                               int32_t* idx, float* w, void* ws, uint8_t* xpack, int32_t* counts,
                               int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s,
-                              int af) {
+                              int af, const FrontNorm* fn) {
   if (T == 0) return hipSuccess;
+  hipError_t err;
+  if (fn) return hipErrorInvalidValue;             // the caller normalises first
+  if (route_small(T, E)) {
+    const double* gp;
+    const float* gn;
+    if ((err = launch_groups(T, D, E, x, wr, ws, xpack, af, s, &gp, &gn)) != hipSuccess) return err;
+    const long long n = (long long)T * k;
+    route_select_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(T, D, E, k, x, wr, br, idx, w, nullptr,
+                                                             tile_rows(n, E), (int)tile_slots(n, E), counts, offsets,
+                                                             perm, inv, tiles, gp, gn);
+    return hipGetLastError();
+  }
   double* logit;
   float *xsq, *wsq;
   int KW;
-  hipError_t err = launch_logits(T, D, E, x, wr, ws, xpack, af, s, &logit, &xsq, &wsq, &KW);
-  if (err != hipSuccess) return err;
-  if (route_small(T, E)) {
-    const long long n = (long long)T * k;
-    route_select_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(T, D, E, k, x, wr, br, logit, xsq, wsq, idx, w,
-                                                             nullptr, tile_rows(n, E), (int)tile_slots(n, E),
-                                                             counts, offsets, perm, inv, tiles);
-    return hipGetLastError();
-  }
+  if ((err = launch_logits_wide(T, D, E, x, wr, ws, xpack, af, s, &logit, &xsq, &wsq, &KW)) != hipSuccess) return err;
   route_select_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(T, D, E, k, KW, x, wr, br, logit, xsq, wsq, idx, w,
                                                               nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;

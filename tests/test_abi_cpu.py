@@ -95,16 +95,19 @@ def test_bad_dims_rejected(L, bad, status):
 def test_bad_arguments_rejected_before_launch(L):
     d = ctypes.byref(D)
     A = 1 << 20                                   # fake, aligned, never dereferenced
-    R = L.moe_route_workspace_bytes(d, 4)
+    # at most 32 tokens and 32 experts: the score groups, [ceil(d_model / 256)] x (8 KiB float64 tile +
+    # 256 B norms); larger batches: K-partial tiles
+    assert L.moe_route_workspace_bytes(d, 4) == 12 * 8192 + 12 * 256
+    R = L.moe_route_workspace_bytes(d, 64)
     assert R > 0 and L.moe_route_workspace_bytes(d, 0) == 0
-    assert L.moe_route(None, 4, A, A, A, A, A, None, A, R, None) == M.MOE_EINVAL
+    assert L.moe_route(None, 64, A, A, A, A, A, None, A, R, None) == M.MOE_EINVAL
     assert L.moe_route(d, -1, A, A, A, A, A, None, A, R, None) == M.MOE_EINVAL
     assert L.moe_route(d, 1 << 22, A, A, A, A, A, None, A, R, None) == M.MOE_EUNSUPPORTED   # T*k >= 2^24
-    assert L.moe_route(d, 4, None, A, A, A, A, None, A, R, None) == M.MOE_EINVAL
-    assert L.moe_route(d, 4, A + 2, A, A, A, A, None, A, R, None) == M.MOE_EINVAL          # misaligned x
-    assert L.moe_route(d, 4, A, A, A, A, A, None, None, R, None) == M.MOE_EINVAL           # no workspace
-    assert L.moe_route(d, 4, A, A, A, A, A, None, A + 16, R, None) == M.MOE_EINVAL         # misaligned ws
-    assert L.moe_route(d, 4, A, A, A, A, A, None, A, R - 1, None) == M.MOE_EWORKSPACE
+    assert L.moe_route(d, 64, None, A, A, A, A, None, A, R, None) == M.MOE_EINVAL
+    assert L.moe_route(d, 64, A + 2, A, A, A, A, None, A, R, None) == M.MOE_EINVAL          # misaligned x
+    assert L.moe_route(d, 64, A, A, A, A, A, None, None, R, None) == M.MOE_EINVAL           # no workspace
+    assert L.moe_route(d, 64, A, A, A, A, A, None, A + 16, R, None) == M.MOE_EINVAL         # misaligned ws
+    assert L.moe_route(d, 64, A, A, A, A, A, None, A, R - 1, None) == M.MOE_EWORKSPACE
     assert L.moe_route(d, 0, A, A, A, A, A, None, None, 0, None) == M.MOE_OK               # T = 0: no-op
     assert L.moe_permute(d, 4, A, A, A, None, A, A, None) == M.MOE_EINVAL
     assert L.moe_permute(d, 4, A, A, A, A, A, None, None) == M.MOE_EINVAL             # no tile table
