@@ -14,16 +14,18 @@
 //  - Each 64-wide k-tile of the tile's 128 activation rows (hi/lo FP6 chunks)
 //    is staged once in LDS and read by all four wavefronts. Each wavefront
 //    streams its own four weight tiles through a 4-deep register ring.
-//  - The LDS holds a ring of 4 staged k-tiles. k-tile kt+2 is written from
-//    registers while kt is computed, and kt+4 is loading into registers.
-//    There is one barrier per k-tile.
+//  - The LDS holds a ring of 8 staged k-tiles (128 KB). k-tile kt+3 is
+//    written from registers while kt is computed, and kt+5 is loading into
+//    registers. A barrier after every second k-tile publishes the two staged
+//    since the previous one.
 //  - Staged layout: the 128 rows' 112-byte chunks back to back.  The staging
 //    loads give consecutive lanes consecutive 16-byte pieces of a row (each load
 //    instruction reads about 9 whole gathered row chunks), and an operand read
 //    by 8 consecutive rows hits 8 different 16-byte bank groups (7r mod 8).
 //  - Work items (row tile, 512-column group) are dealt to the 8 XCDs in
 //    contiguous blocks, so the workgroups sharing an expert's weights share
-//    an L2.
+//    an L2; within the order, blocks of 4 row tiles go column group by column
+//    group, so the workgroups running together share weights and rows.
 //  - Gate/up epilogue: SwiGLU in registers, then a transpose of the h tile
 //    through LDS. Each lane then holds one 32-value block of an h row and
 //    splits it into hi/lo FP6 with the packed conversion instructions.
@@ -53,9 +55,10 @@ struct PrefillArgs {
 
 constexpr int kPWaveTiles = 4;                         // 32-column weight tiles per wavefront
 constexpr int kPGroupTiles = 4 * kPWaveTiles;          // per workgroup
-constexpr int kPSlots = 4;                             // staged k-tiles in the LDS ring
+constexpr int kPSlots = 8;                             // staged k-tiles in the LDS ring (slot = k-tile % 8)
 constexpr int kPSlotBytes = 1024 * 16;                 // 896 pieces + 128 dummy (4 unconditional per thread)
-constexpr int kPStageAhead = 2;                        // k-tile kt + 2 is written to LDS during k-tile kt
+constexpr int kPStageAhead = 3;                        // k-tile kt + 3 is written to LDS during k-tile kt
+constexpr int kPSlotBlock = 4;                         // row tiles per block of the work-item order
 constexpr int kPEpiStride = 68;                        // floats per row of the transposed h block
 constexpr int kPOutStride = 136;                       // halves per row of the transposed y block
 static_assert(kPSlots * kPSlotBytes >= 4 * 32 * kPEpiStride * 4, "h transposition fits the ring");
@@ -111,8 +114,17 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   const int local = blockIdx.x >> 3;
   const int item = (blockIdx.x & 7) * per + local;
   if (local >= per || item >= total) return;             // uniform per workgroup
-  const int slot = item / g.ngroups;
-  const int cgrp = item - slot * g.ngroups;
+  // item -> (row tile slot, column group): slots go in blocks of kPSlotBlock consecutive row tiles
+  // (one expert's, mostly), a block's items column group by column group with the row tile
+  // fastest, so the workgroups that run together on an XCD share each column group's weights
+  // kPSlotBlock ways and each row tile's activations about 32 / kPSlotBlock ways through its L2
+  const int full = used / kPSlotBlock;                   // whole blocks
+  const int in_full = full * kPSlotBlock * g.ngroups;
+  const int sb = item < in_full ? item / (kPSlotBlock * g.ngroups) : full;
+  const int nb = item < in_full ? kPSlotBlock : used - full * kPSlotBlock;
+  const int rem = item - sb * kPSlotBlock * g.ngroups;
+  const int cgrp = rem / nb;
+  const int slot = sb * kPSlotBlock + (rem - cgrp * nb);
   const int32_t* tile = g.tiles + (size_t)slot * tile_ints(kPrefillRows);
   // the header and the row ids in one round trip (a slot always holds 128 id entries)
   const int a_id = tile[4 + (tid & (kPrefillRows - 1))];
@@ -178,14 +190,15 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsS, lane * 4, sbase[cb] + grp * 256, 0);
   };
 
-  // ---- prologue: k-tiles 0, 1 staged; the next NA in registers; weight ring filled -------------
+  // ---- prologue: k-tiles 0 .. kPStageAhead-1 staged; the next NA in registers; weight ring -----
   // Every load index is clamped to the last k-tile, so no load or store depends on K: a k-tile
   // past the end is staged into a slot nobody reads.  Register set t % NA holds k-tile t.
   v4i abuf[NA][NPC];
-  load_a(0, abuf[0 % NA]);
-  store_a(0, abuf[0 % NA]);
-  load_a(min(1, KT - 1), abuf[1 % NA]);
-  store_a(1, abuf[1 % NA]);
+#pragma unroll
+  for (int t = 0; t < kPStageAhead; ++t) {
+    load_a(min(t, KT - 1), abuf[t % NA]);
+    store_a(t, abuf[t % NA]);
+  }
 #pragma unroll
   for (int t = kPStageAhead; t < kPStageAhead + NA; ++t) load_a(min(t, KT - 1), abuf[t % NA]);
   v4i bq[P][kPWaveTiles];
@@ -220,7 +233,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     uint32_t s;
   };
   auto read_ops = [&](const int kt, const int rb) __attribute__((always_inline)) {
-    const uint8_t* row = sA + (kt & 3) * kPSlotBytes + rb * kBlockBytes + r32 * CH;
+    const uint8_t* row = sA + (kt & (kPSlots - 1)) * kPSlotBytes + rb * kBlockBytes + r32 * CH;
     AOps o;
     if constexpr (F4) {                                   // the lane's block: 16 bytes and a scale byte
       const v4i q0 = *reinterpret_cast<const v4i*>(row + 16 * h);
@@ -278,7 +291,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
           acc[rb][cb] = mma_sel_a<1>(j & 3, a1, b_operand(bw[cb][1]), acc[rb][cb], cur.s, sqd[cb][1]);
         }
       }
-      if (rb == 0) store_a((kt + D) & 3, abuf[(j + D) % NA]);                  // publish kt + D
+      if (rb == 0) store_a((kt + D) & (kPSlots - 1), abuf[(j + D) % NA]);      // stage kt + D
       if (rb == 1) load_a(min(kt + D + NA, KT - 1), abuf[(j + D) % NA]);        // fetch kt + D + NA
       if (!F4 && rb == 2) {
 #pragma unroll
@@ -305,7 +318,11 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int cb = 0; cb < kPWaveTiles; ++cb) asm volatile("" : "+a"(acc[rb][cb]));
-    __syncthreads();
+    // A barrier after every second k-tile (odd kt) publishes the two k-tiles staged since the last
+    // one.  With k-tile kt + 3 staged during kt: the first operands of kt + 1, read at the end of
+    // kt, were staged during kt - 2, and one of kt - 2, kt - 1 ends with a barrier; the slot that
+    // kt + 3 takes last held kt - 5, which every wavefront finished before the last barrier.
+    if (j & 1) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int cb = 0; cb < (F4 ? 0 : kPWaveTiles); ++cb) {
