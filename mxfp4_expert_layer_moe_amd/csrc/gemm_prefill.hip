@@ -14,18 +14,18 @@
 //  - Each 64-wide k-tile of the tile's 128 activation rows (hi/lo FP6 chunks)
 //    is staged once in LDS and read by all four wavefronts. Each wavefront
 //    streams its own four weight tiles through a 4-deep register ring.
-//  - The LDS holds a ring of 8 staged k-tiles (128 KB). k-tile kt+3 is
-//    written from registers while kt is computed, and kt+5 is loading into
-//    registers. A barrier after every second k-tile publishes the two staged
-//    since the previous one.
+//  - The LDS holds a ring of staged k-tiles. In the gate/up stage (8 slots,
+//    128 KB) k-tile kt+3 is written from registers while kt is computed and
+//    kt+5 is loading into registers, and a barrier after every second k-tile
+//    publishes the two staged since the previous one; the down stage (4
+//    slots) writes kt+2 and has a barrier per k-tile.
 //  - Staged layout: the 128 rows' 112-byte chunks back to back.  The staging
 //    loads give consecutive lanes consecutive 16-byte pieces of a row (each load
 //    instruction reads about 9 whole gathered row chunks), and an operand read
 //    by 8 consecutive rows hits 8 different 16-byte bank groups (7r mod 8).
 //  - Work items (row tile, 512-column group) are dealt to the 8 XCDs in
 //    contiguous blocks, so the workgroups sharing an expert's weights share
-//    an L2; within the order, blocks of 4 row tiles go column group by column
-//    group, so the workgroups running together share weights and rows.
+//    an L2.
 //  - Gate/up epilogue: SwiGLU in registers, then a transpose of the h tile
 //    through LDS. Each lane then holds one 32-value block of an h row and
 //    splits it into hi/lo FP6 with the packed conversion instructions.
@@ -55,14 +55,21 @@ struct PrefillArgs {
 
 constexpr int kPWaveTiles = 4;                         // 32-column weight tiles per wavefront
 constexpr int kPGroupTiles = 4 * kPWaveTiles;          // per workgroup
-constexpr int kPSlots = 8;                             // staged k-tiles in the LDS ring (slot = k-tile % 8)
+constexpr int kPSlots = 8;                             // LDS ring slots of the gate/up stage (slot = k-tile % 8)
 constexpr int kPSlotBytes = 1024 * 16;                 // 896 pieces + 128 dummy (4 unconditional per thread)
-constexpr int kPStageAhead = 3;                        // k-tile kt + 3 is written to LDS during k-tile kt
-constexpr int kPSlotBlock = 4;                         // row tiles per block of the work-item order
+// The gate/up stage stages k-tile kt + 3 during kt into an 8-slot ring and publishes with a barrier
+// after every second k-tile; the down stage (fewer registers to spare) stages kt + 2 into 4 slots
+// and has a barrier per k-tile.
+template <int STAGE>
+constexpr int stage_ahead() { return STAGE == 0 ? 3 : 2; }
+template <int STAGE>
+constexpr int barrier_every() { return STAGE == 0 ? 2 : 1; }
+template <int STAGE>
+constexpr int ring_slots() { return STAGE == 0 ? kPSlots : 4; }
 constexpr int kPEpiStride = 68;                        // floats per row of the transposed h block
 constexpr int kPOutStride = 136;                       // halves per row of the transposed y block
-static_assert(kPSlots * kPSlotBytes >= 4 * 32 * kPEpiStride * 4, "h transposition fits the ring");
-static_assert(kPSlots * kPSlotBytes / 4 >= 32 * kPOutStride * 2, "y transposition fits a wavefront's quarter");
+static_assert(kPSlots * kPSlotBytes >= 4 * 32 * kPEpiStride * 4, "h transposition fits the gate/up ring");
+static_assert(4 * kPSlotBytes / 4 >= 32 * kPOutStride * 2, "y transposition fits a wavefront's quarter of the down ring");
 
 // Matrix-instruction pairing.  Each 64-wide k-tile holds two 32-value blocks b = 0, 1 of the
 // activation, each stored as hi + lo FP6 terms.  One MFMA per block: lanes 0-31 supply the hi term
@@ -97,7 +104,8 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   constexpr int NPC = F4 ? 2 : 4;                         // staged 16-byte pieces per thread per k-tile
   constexpr int kStagePieces = kPrefillRows * (CH / 16);  // 384 or 896 (the rest re-read a real one)
   constexpr int kBlockBytes = 32 * CH;                    // one 32-row block of a staged k-tile
-  __shared__ __attribute__((aligned(16))) uint8_t sA[kPSlots * kPSlotBytes];
+  constexpr int kSlots = ring_slots<STAGE>();
+  __shared__ __attribute__((aligned(16))) uint8_t sA[kSlots * kPSlotBytes];
   __shared__ int srow[kPrefillRows];
   __shared__ float sgate[kPrefillRows];
   __shared__ int sdst[kPrefillRows];                     // down: output row of each tile row
@@ -114,17 +122,8 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   const int local = blockIdx.x >> 3;
   const int item = (blockIdx.x & 7) * per + local;
   if (local >= per || item >= total) return;             // uniform per workgroup
-  // item -> (row tile slot, column group): slots go in blocks of kPSlotBlock consecutive row tiles
-  // (one expert's, mostly), a block's items column group by column group with the row tile
-  // fastest, so the workgroups that run together on an XCD share each column group's weights
-  // kPSlotBlock ways and each row tile's activations about 32 / kPSlotBlock ways through its L2
-  const int full = used / kPSlotBlock;                   // whole blocks
-  const int in_full = full * kPSlotBlock * g.ngroups;
-  const int sb = item < in_full ? item / (kPSlotBlock * g.ngroups) : full;
-  const int nb = item < in_full ? kPSlotBlock : used - full * kPSlotBlock;
-  const int rem = item - sb * kPSlotBlock * g.ngroups;
-  const int cgrp = rem / nb;
-  const int slot = sb * kPSlotBlock + (rem - cgrp * nb);
+  const int slot = item / g.ngroups;
+  const int cgrp = item - slot * g.ngroups;
   const int32_t* tile = g.tiles + (size_t)slot * tile_ints(kPrefillRows);
   // the header and the row ids in one round trip (a slot always holds 128 id entries)
   const int a_id = tile[4 + (tid & (kPrefillRows - 1))];
@@ -190,17 +189,18 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsS, lane * 4, sbase[cb] + grp * 256, 0);
   };
 
-  // ---- prologue: k-tiles 0 .. kPStageAhead-1 staged; the next NA in registers; weight ring -----
+  // ---- prologue: the first stage_ahead k-tiles staged; the next NA in registers; weight ring ----
+  constexpr int kAhead = stage_ahead<STAGE>();
   // Every load index is clamped to the last k-tile, so no load or store depends on K: a k-tile
   // past the end is staged into a slot nobody reads.  Register set t % NA holds k-tile t.
   v4i abuf[NA][NPC];
 #pragma unroll
-  for (int t = 0; t < kPStageAhead; ++t) {
+  for (int t = 0; t < kAhead; ++t) {
     load_a(min(t, KT - 1), abuf[t % NA]);
     store_a(t, abuf[t % NA]);
   }
 #pragma unroll
-  for (int t = kPStageAhead; t < kPStageAhead + NA; ++t) load_a(min(t, KT - 1), abuf[t % NA]);
+  for (int t = kAhead; t < kAhead + NA; ++t) load_a(min(t, KT - 1), abuf[t % NA]);
   v4i bq[P][kPWaveTiles];
   uint32_t sq[2][kPWaveTiles];
   uint32_t sqd[kPWaveTiles][2];                          // current scale group, per block
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     uint32_t s;
   };
   auto read_ops = [&](const int kt, const int rb) __attribute__((always_inline)) {
-    const uint8_t* row = sA + (kt & (kPSlots - 1)) * kPSlotBytes + rb * kBlockBytes + r32 * CH;
+    const uint8_t* row = sA + (kt & (kSlots - 1)) * kPSlotBytes + rb * kBlockBytes + r32 * CH;
     AOps o;
     if constexpr (F4) {                                   // the lane's block: 16 bytes and a scale byte
       const v4i q0 = *reinterpret_cast<const v4i*>(row + 16 * h);
@@ -250,9 +250,9 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   };
   // Software pipeline of one k-tile (kt, j = kt % 8, compile-time ring slots), in four phases of
   // eight matrix instructions (one row block each).  Other work rides in the phases' shadows:
-  //  - operands are read one row block ahead; the next k-tile's first block is read before this
-  //    k-tile's barrier (its slot was published before the previous barrier);
-  //  - phase 0 publishes staged k-tile kt + 2, phase 1 fetches k-tile kt + 2 + NA;
+  //  - operands are read one row block ahead; the next k-tile's first block is read at the end of
+  //    this k-tile (its slot was published by an earlier barrier);
+  //  - phase 0 stages k-tile kt + A, phase 1 fetches k-tile kt + A + NA (A = stage_ahead);
   //  - phase 2 splits the next k-tile's weight registers by block (and the next scale group);
   //  - phase 3 refills the weight ring slot just consumed.
   // A scheduling barrier between phases keeps each phase's work next to its matrix instructions.
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     }
   }
   auto step = [&](const int kt, const int j) __attribute__((always_inline)) {
-    constexpr int D = kPStageAhead;
+    constexpr int D = kAhead;
     v4i bwn[kPWaveTiles][2];
     uint32_t sqn[kPWaveTiles][2];
 #pragma unroll
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
           acc[rb][cb] = mma_sel_a<1>(j & 3, a1, b_operand(bw[cb][1]), acc[rb][cb], cur.s, sqd[cb][1]);
         }
       }
-      if (rb == 0) store_a((kt + D) & (kPSlots - 1), abuf[(j + D) % NA]);      // stage kt + D
+      if (rb == 0) store_a((kt + D) & (kSlots - 1), abuf[(j + D) % NA]);       // stage kt + D
       if (rb == 1) load_a(min(kt + D + NA, KT - 1), abuf[(j + D) % NA]);        // fetch kt + D + NA
       if (!F4 && rb == 2) {
 #pragma unroll
@@ -318,11 +318,14 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int cb = 0; cb < kPWaveTiles; ++cb) asm volatile("" : "+a"(acc[rb][cb]));
-    // A barrier after every second k-tile (odd kt) publishes the two k-tiles staged since the last
-    // one.  With k-tile kt + 3 staged during kt: the first operands of kt + 1, read at the end of
-    // kt, were staged during kt - 2, and one of kt - 2, kt - 1 ends with a barrier; the slot that
-    // kt + 3 takes last held kt - 5, which every wavefront finished before the last barrier.
-    if (j & 1) __syncthreads();
+    // A barrier after every B-th k-tile publishes the k-tiles staged since the last one (B =
+    // barrier_every, staging A = stage_ahead >= B + 1 ahead into 8 >= A + B slots).  The first
+    // operands of kt + 1, read at the end of kt, were staged during kt + 1 - A, and one of the B
+    // k-tiles before kt ends with a barrier; the slot kt + A takes last held kt + A - 8, which
+    // every wavefront finished before the last barrier.
+    constexpr int B = barrier_every<STAGE>();
+    static_assert(kAhead >= B + 1 && kSlots >= kAhead + B, "ring publishing order");
+    if (j % B == B - 1) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int cb = 0; cb < (F4 ? 0 : kPWaveTiles); ++cb) {
@@ -391,7 +394,7 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     __syncthreads();
     const int D = g.out_K;
     uint8_t* out = reinterpret_cast<uint8_t*>(g.out);
-    _Float16* ep = reinterpret_cast<_Float16*>(sA + wave * (kPSlots * kPSlotBytes / 4));
+    _Float16* ep = reinterpret_cast<_Float16*>(sA + wave * (kSlots * kPSlotBytes / 4));
     const int c0 = (cgrp * kPGroupTiles + wave * kPWaveTiles) * 32;   // first column of the wavefront
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
