@@ -34,18 +34,25 @@
  *    grouped by expert (ascending) and, within an expert, by token.
  *  - Calls that share no buffers may run concurrently on different streams.
  *
- * The step-by-step boundary (what differs from a plain bf16 interface)
- * --------------------------------------------------------------------
- *  - moe_permute also writes a row-tile table (expert, first grouped row, row
- *    count and the assignment id of every row of each tile); the expert GEMMs
- *    start from that table, not from perm and offsets.
- *  - The expert GEMMs take their activations already packed ("split MX6",
- *    below), not as bf16 rows: moe_pack_act packs x, and the gate/up stage
- *    writes h in the same packed format, which the down stage reads.  A packed
- *    row decodes to within 2^-8 of its 32-value block maximum of the bf16 row
- *    (hi + lo; the bf16 h the layer defines is rounded before it is packed).
- *  - The down stage writes y_perm in fp16, each row already multiplied by its
- *    gate; moe_combine sums a token's rows.
+ * The step-by-step boundary
+ * -------------------------
+ * moe_route -> moe_permute -> moe_expert_gemm_mxfp4 (GATE_UP, then DOWN) ->
+ * moe_combine computes what moe_forward computes, on bf16 rows: x [T][d_model],
+ * h [T*top_k][d_ff] in grouped order, y_perm [T*top_k][d_model] fp16 with each
+ * row already multiplied by its gate, and the grouping as perm and offsets.
+ * Scratch comes from ws.  The same steps also exist on the operands the kernels
+ * actually read, for callers that keep them between calls:
+ *  - moe_permute_tiles writes, besides the grouping, the row-tile table
+ *    (expert, first grouped row, row count and the assignment id of every row
+ *    of each tile) that the expert GEMMs start from;
+ *  - moe_expert_gemm_mxfp4_packed takes activations already packed ("split
+ *    MX6", below): moe_pack_act packs x, and its gate/up stage writes h in the
+ *    same packed format, which its down stage reads.  A packed row decodes to
+ *    within 2^-8 of its 32-value block maximum of the bf16 row (hi + lo; the
+ *    bf16 h the layer defines is rounded before it is packed).
+ * moe_expert_gemm_mxfp4 builds the tile table from perm and offsets and packs
+ * its input rows in ws, then runs the same kernels; its bf16 h is the value the
+ * packed gate/up stage splits, so packing it gives the packed stage's bytes.
  *
  * Activation pack format ("split MX6")
  * ------------------------------------
@@ -176,6 +183,17 @@ moe_status moe_route(const moe_dims* dims, int32_t T, const void* x_bf16, const 
  *   counts    out [n_experts]; offsets out [n_experts + 1] (exclusive prefix sum)
  *   perm      out [T*top_k]: assignment id at each grouped position
  *   inv       out [T*top_k]: inv[perm[p]] = p
+ *   ws        device scratch of at least moe_permute_workspace_bytes(dims, T)
+ *             bytes (moe_workspace_bytes(dims, T) is always enough), 256-byte
+ *             aligned; may be NULL when T == 0
+ */
+size_t moe_permute_workspace_bytes(const moe_dims* dims, int32_t T);
+moe_status moe_permute(const moe_dims* dims, int32_t T, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_permute that also hands back the row-tile table the expert GEMMs start
+ * from (same passages):
  *   tiles     out, moe_tile_table_bytes(dims, T) bytes, 16-byte aligned: the
  *             row-tile table: 8-row tiles when T*top_k <= 6*n_experts (48
  *             int32 per slot), else 128-row tiles (132 int32 per slot).  A
@@ -183,8 +201,8 @@ moe_status moe_route(const moe_dims* dims, int32_t T, const void* x_bf16, const 
  *             number of tiles in use, then the assignment id of each row.
  */
 size_t moe_tile_table_bytes(const moe_dims* dims, int32_t T);
-moe_status moe_permute(const moe_dims* dims, int32_t T, const int32_t* topk_idx, int32_t* counts,
-                       int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t stream);
+moe_status moe_permute_tiles(const moe_dims* dims, int32_t T, const int32_t* topk_idx, int32_t* counts,
+                             int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t stream);
 
 /*
  * Split bf16 rows into the packed hi/lo MX6 activation format above (the
@@ -202,9 +220,37 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
  * "Swish/SwiGLU", Figures 6-7: gate and up projections, silu(gate) * up, down
  * projection), its pre-activations clamped at swiglu_limit (7 in the "GPT-OSS
  * 20B" model card's raw config), its weights MXFP4 ("gpt-oss architecture
- * walk-through", section "Quantization").  This call takes the packed
- * activations and the row-tile table (see "The step-by-step boundary" above),
- * not bf16 rows with perm and offsets.
+ * walk-through", section "Quantization").  On bf16 rows with the grouping as
+ * perm and offsets (moe_permute):
+ *  MOE_STAGE_GATE_UP:
+ *    a         x [T][d_model] bf16; grouped position p reads token perm[p] / top_k
+ *    out       h [T*top_k][d_ff] bf16, row p = grouped position p, the bf16
+ *              round of silu(clamp(g)) * clamp(u) (g, u accumulated in fp32 over
+ *              the hi/lo split of x)
+ *    topk_w    unused (may be NULL)
+ *  MOE_STAGE_DOWN:
+ *    a         h [T*top_k][d_ff] bf16 in grouped order (the GATE_UP output)
+ *    topk_w    [T][top_k] fp32 gates; row p is scaled by topk_w[perm[p]]
+ *    out       y_perm [T*top_k][d_model] fp16 (round to nearest even), row p =
+ *              gate-weighted expert output; its magnitude must stay below the
+ *              fp16 maximum (65504)
+ *  codes/scales  prepacked weights of the stage (moe_mxfp4_prepack)
+ *  perm, offsets  moe_permute's outputs for the same T
+ *  ws        device scratch of at least moe_expert_gemm_workspace_bytes(dims, T,
+ *            stage) bytes (moe_workspace_bytes(dims, T) is always enough),
+ *            256-byte aligned: the row-tile table built from perm and offsets,
+ *            then the packed input rows; may be NULL when T == 0
+ *  Experts with no token have no tile (their weights are not read).
+ */
+size_t moe_expert_gemm_workspace_bytes(const moe_dims* dims, int32_t T, moe_stage stage);
+moe_status moe_expert_gemm_mxfp4(const moe_dims* dims, int32_t T, moe_stage stage, const void* a,
+                                 const int32_t* perm, const int32_t* offsets, const uint8_t* codes,
+                                 const uint8_t* scales, const float* topk_w, void* out, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
+ * The same GEMM on the packed activations and the row-tile table (see "The
+ * step-by-step boundary" above; same passages):
  *  MOE_STAGE_GATE_UP:
  *    a_packed  packed x, T rows of d_model (moe_pack_act output); the row of
  *              grouped position p is token perm[p] / top_k
@@ -219,12 +265,12 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
  *    out       y_perm [T*top_k][d_model] fp16 (round to nearest even), row p =
  *              gate-weighted expert output; its magnitude must stay below the fp16
  *              maximum (65504)
- *  tiles is moe_permute's row-tile table for the same T.  Experts with no token
- *  have no tile (their weights are not read).
+ *  tiles is moe_permute_tiles's row-tile table for the same T.  Experts with no
+ *  token have no tile (their weights are not read).
  */
-moe_status moe_expert_gemm_mxfp4(const moe_dims* dims, int32_t T, moe_stage stage, const void* a_packed,
-                                 const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
-                                 const float* topk_w, void* out, hipStream_t stream);
+moe_status moe_expert_gemm_mxfp4_packed(const moe_dims* dims, int32_t T, moe_stage stage, const void* a_packed,
+                                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
+                                        const float* topk_w, void* out, hipStream_t stream);
 
 /*
  * Weighted combine: y[t] = sum over the token's slots j (ascending expert id)
@@ -319,7 +365,7 @@ moe_status moe_forward_noalloc(const moe_dims* dims, int32_t T, const void* x_bf
  * is not the W4A16 layer of moe_forward: it is a different, lower-precision
  * contract.
  *   moe_pack_act4:               bf16 rows -> MXFP4 rows
- *   moe_expert_gemm_mxfp4_act4:  as moe_expert_gemm_mxfp4 with MXFP4 activations
+ *   moe_expert_gemm_mxfp4_act4:  as moe_expert_gemm_mxfp4_packed with MXFP4 activations
  *                                (stage GATE_UP writes h in the MXFP4 format)
  *   moe_forward_act4:            the whole layer; ws of moe_workspace_bytes_act4
  */

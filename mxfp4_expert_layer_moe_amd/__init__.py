@@ -23,6 +23,8 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN = 0, 1
 # Symbols the header declares (checked by the CPU tests).
 EXPORTS = ("moe_status_str", "moe_act_pack_bytes", "moe_prepacked_codes_bytes", "moe_prepacked_scales_bytes",
            "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes", "moe_route", "moe_permute",
+           "moe_permute_workspace_bytes", "moe_permute_tiles", "moe_expert_gemm_workspace_bytes",
+           "moe_expert_gemm_mxfp4_packed",
            "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine", "moe_forward", "moe_mxfp4_quantize",
            "moe_mxfp4_prepack", "moe_combine_residual", "moe_rmsnorm", "moe_block_workspace_bytes",
            "moe_block_forward", "moe_act4_pack_bytes", "moe_pack_act4", "moe_expert_gemm_mxfp4_act4",
@@ -66,13 +68,17 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, ctypes.c_int]
         for name in ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_table_bytes",
-                     "moe_block_workspace_bytes", "moe_workspace_bytes_act4"):
+                     "moe_block_workspace_bytes", "moe_workspace_bytes_act4", "moe_permute_workspace_bytes"):
             getattr(L, name).restype = sz
             getattr(L, name).argtypes = [dp, i32]
         L.moe_route.argtypes = [dp, i32, vp, f32p, f32p, i32p, f32p, f32p, vp, sz, vp]
-        L.moe_permute.argtypes = [dp, i32, i32p, i32p, i32p, i32p, i32p, i32p, vp]
+        L.moe_expert_gemm_workspace_bytes.restype = sz
+        L.moe_expert_gemm_workspace_bytes.argtypes = [dp, i32, ctypes.c_int]
+        L.moe_permute.argtypes = [dp, i32, i32p, i32p, i32p, i32p, i32p, vp, sz, vp]
+        L.moe_permute_tiles.argtypes = [dp, i32, i32p, i32p, i32p, i32p, i32p, i32p, vp]
         L.moe_pack_act.argtypes = [i32, i32, vp, vp, vp]
-        L.moe_expert_gemm_mxfp4.argtypes = [dp, i32, ctypes.c_int, vp, i32p, vp, vp, f32p, vp, vp]
+        L.moe_expert_gemm_mxfp4.argtypes = [dp, i32, ctypes.c_int, vp, i32p, i32p, vp, vp, f32p, vp, vp, sz, vp]
+        L.moe_expert_gemm_mxfp4_packed.argtypes = [dp, i32, ctypes.c_int, vp, i32p, vp, vp, f32p, vp, vp]
         L.moe_combine.argtypes = [dp, i32, f32p, i32p, vp, ctypes.c_int, vp]
         L.moe_forward.argtypes = [dp, i32, vp, f32p, f32p, ctypes.POINTER(moe_weights), vp, ctypes.c_int, vp, sz, vp]
         L.moe_combine_residual.argtypes = [dp, i32, vp, i32p, vp, vp, ctypes.c_int, vp]
@@ -88,7 +94,8 @@ def lib() -> ctypes.CDLL:
                                         vp, ctypes.c_int, vp, sz, vp]
         L.moe_mxfp4_quantize.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
         L.moe_mxfp4_prepack.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp]
-        for name in ("moe_route", "moe_permute", "moe_pack_act", "moe_expert_gemm_mxfp4", "moe_combine",
+        for name in ("moe_route", "moe_permute", "moe_permute_tiles", "moe_pack_act", "moe_expert_gemm_mxfp4",
+                     "moe_expert_gemm_mxfp4_packed", "moe_combine",
                      "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_prepack", "moe_combine_residual",
                      "moe_rmsnorm", "moe_block_forward", "moe_pack_act4", "moe_expert_gemm_mxfp4_act4",
                      "moe_forward_act4", "moe_forward_noalloc"):
@@ -171,18 +178,38 @@ def moe_tile_table_bytes(d: moe_dims, T: int) -> int:
     return lib().moe_tile_table_bytes(ctypes.byref(d), T)
 
 
-def moe_permute(d, T, topk_idx, counts, offsets, perm, inv, tiles, stream=None):
+def moe_permute_workspace_bytes(d: moe_dims, T: int) -> int:
+    return lib().moe_permute_workspace_bytes(ctypes.byref(d), T)
+
+
+def moe_permute(d, T, topk_idx, counts, offsets, perm, inv, ws, ws_bytes, stream=None):
     _check(lib().moe_permute(ctypes.byref(d), T, _p(topk_idx), _p(counts), _p(offsets), _p(perm), _p(inv),
-                             _p(tiles), _s(stream)), "moe_permute")
+                             _p(ws), ws_bytes, _s(stream)), "moe_permute")
+
+
+def moe_permute_tiles(d, T, topk_idx, counts, offsets, perm, inv, tiles, stream=None):
+    _check(lib().moe_permute_tiles(ctypes.byref(d), T, _p(topk_idx), _p(counts), _p(offsets), _p(perm), _p(inv),
+                                   _p(tiles), _s(stream)), "moe_permute_tiles")
 
 
 def moe_pack_act(K, rows, a, a_packed, stream=None):
     _check(lib().moe_pack_act(K, rows, _p(a), _p(a_packed), _s(stream)), "moe_pack_act")
 
 
-def moe_expert_gemm_mxfp4(d, T, stage, a_packed, tiles, codes, scales, topk_w, out, stream=None):
-    _check(lib().moe_expert_gemm_mxfp4(ctypes.byref(d), T, stage, _p(a_packed), _p(tiles), _p(codes),
-                                       _p(scales), _p(topk_w), _p(out), _s(stream)), "moe_expert_gemm_mxfp4")
+def moe_expert_gemm_workspace_bytes(d: moe_dims, T: int, stage: int) -> int:
+    return lib().moe_expert_gemm_workspace_bytes(ctypes.byref(d), T, stage)
+
+
+def moe_expert_gemm_mxfp4(d, T, stage, a, perm, offsets, codes, scales, topk_w, out, ws, ws_bytes, stream=None):
+    _check(lib().moe_expert_gemm_mxfp4(ctypes.byref(d), T, stage, _p(a), _p(perm), _p(offsets), _p(codes),
+                                       _p(scales), _p(topk_w), _p(out), _p(ws), ws_bytes, _s(stream)),
+           "moe_expert_gemm_mxfp4")
+
+
+def moe_expert_gemm_mxfp4_packed(d, T, stage, a_packed, tiles, codes, scales, topk_w, out, stream=None):
+    _check(lib().moe_expert_gemm_mxfp4_packed(ctypes.byref(d), T, stage, _p(a_packed), _p(tiles), _p(codes),
+                                              _p(scales), _p(topk_w), _p(out), _s(stream)),
+           "moe_expert_gemm_mxfp4_packed")
 
 
 def moe_combine(d, T, y_perm, inv, y, y_dtype, stream=None):

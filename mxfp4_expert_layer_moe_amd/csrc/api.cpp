@@ -257,8 +257,8 @@ size_t moe_tile_table_bytes(const moe_dims* d, int32_t T) {
   return tile_table_bytes(d, T);
 }
 
-moe_status moe_permute(const moe_dims* d, int32_t T, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
-                       int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t stream) {
+moe_status moe_permute_tiles(const moe_dims* d, int32_t T, const int32_t* topk_idx, int32_t* counts,
+                             int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t stream) {
   moe_status st = check_dims(d);
   if (st != MOE_OK) return st;
   if ((st = check_T(d, T)) != MOE_OK) return st;
@@ -309,10 +309,69 @@ static moe_status expert_gemm(const moe_dims* d, int32_t T, moe_stage stage, con
                                 out, stream, af));
 }
 
-moe_status moe_expert_gemm_mxfp4(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed,
-                                 const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
-                                 const float* topk_w, void* out, hipStream_t stream) {
+moe_status moe_expert_gemm_mxfp4_packed(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed,
+                                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales,
+                                        const float* topk_w, void* out, hipStream_t stream) {
   return expert_gemm(d, T, stage, a_packed, tiles, codes, scales, topk_w, out, stream, kActSplit6);
+}
+
+// ---- the plain boundary: bf16 rows, perm and offsets, scratch from ws -----------------------
+
+size_t moe_permute_workspace_bytes(const moe_dims* d, int32_t T) {
+  if (check_dims(d) != MOE_OK || check_T(d, T) != MOE_OK) return 0;
+  return tile_table_bytes(d, T);
+}
+
+moe_status moe_permute(const moe_dims* d, int32_t T, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (!topk_idx || !counts || !offsets || !perm || !inv) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!ws || !aligned(ws, kAlignWs)) return MOE_EINVAL;
+  if (ws_bytes < tile_table_bytes(d, T)) return MOE_EWORKSPACE;
+  return moe_permute_tiles(d, T, topk_idx, counts, offsets, perm, inv, (int32_t*)ws, stream);
+}
+
+// the plain expert GEMM's scratch: the row-tile table, then the packed activation rows
+static size_t gemm_ws_packed_at(const moe_dims* d, int32_t T) { return round_up(tile_table_bytes(d, T), kAlignWs); }
+static size_t gemm_ws_bytes(const moe_dims* d, int32_t T, moe_stage stage) {
+  if (T == 0) return 0;
+  const size_t rows = stage == MOE_STAGE_GATE_UP ? (size_t)T : (size_t)T * d->top_k;
+  const int K = stage == MOE_STAGE_GATE_UP ? d->d_model : d->d_ff;
+  return gemm_ws_packed_at(d, T) + rows * act_row_bytes(K);
+}
+
+size_t moe_expert_gemm_workspace_bytes(const moe_dims* d, int32_t T, moe_stage stage) {
+  if (check_dims(d) != MOE_OK || check_T(d, T) != MOE_OK) return 0;
+  if (stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN) return 0;
+  return gemm_ws_bytes(d, T, stage);
+}
+
+moe_status moe_expert_gemm_mxfp4(const moe_dims* d, int32_t T, moe_stage stage, const void* a, const int32_t* perm,
+                                 const int32_t* offsets, const uint8_t* codes, const uint8_t* scales,
+                                 const float* topk_w, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(d, T)) != MOE_OK) return st;
+  if (stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN) return MOE_EINVAL;
+  if (!a || !perm || !offsets || !codes || !scales || !out) return MOE_EINVAL;
+  if (stage == MOE_STAGE_DOWN && !topk_w) return MOE_EINVAL;
+  if (!aligned(a, 16) || !aligned(perm, 4) || !aligned(offsets, 4) || !aligned(codes, 16) || !aligned(scales, 4) ||
+      !aligned(out, 16) || (topk_w && !aligned(topk_w, 4)))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!ws || !aligned(ws, kAlignWs)) return MOE_EINVAL;
+  if (ws_bytes < gemm_ws_bytes(d, T, stage)) return MOE_EWORKSPACE;
+  const int D = d->d_model, I = d->d_ff, E = d->n_experts, k = d->top_k;
+  int32_t* tiles = (int32_t*)ws;
+  uint8_t* packed = (uint8_t*)ws + gemm_ws_packed_at(d, T);
+  if (launch_tiles_from_groups(T, E, k, offsets, perm, tiles, stream)) return MOE_EHIP;
+  const int s = stage == MOE_STAGE_GATE_UP ? 0 : 1;
+  if (launch_pack(s == 0 ? D : I, s == 0 ? T : T * k, (const uint16_t*)a, packed, stream)) return MOE_EHIP;
+  return hip_status(launch_gemm(s, T, D, I, E, k, d->swiglu_limit, packed, tiles, codes, scales, topk_w, out, stream,
+                                kActSplit6, /*out_assign=*/0, /*dense_rows=*/0, /*h_bf16=*/s == 0));
 }
 
 moe_status moe_expert_gemm_mxfp4_act4(const moe_dims* d, int32_t T, moe_stage stage, const void* a_packed4,

@@ -33,6 +33,7 @@ struct GemmArgs {
   int T, k, E, K, KT, KG, units, out_K;
   int out_assign;                                       // down: rows to their assignment index
   int dense_rows;                                       // down: packed h row e*T + t (dense decode path)
+  int h_bf16;                                           // gate/up: h as bf16 rows instead of packed
   float limit;
   const uint8_t* a_packed;
   const int32_t* tiles;
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs g) {
         v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
       }
       if constexpr (AF == kActFp4) store_fp4_block(out + (size_t)(p0 + lane) * orb, u, quant_fp4x32(v));
+      else if (g.h_bf16) store_bf16_block(reinterpret_cast<uint16_t*>(g.out) + (size_t)(p0 + lane) * I, u, v);
       else store_fp6_block(out + (size_t)(p0 + lane) * orb, u, split_fp6x32(v));
     }
   } else {
@@ -324,12 +326,14 @@ constexpr int kDownP = 8;       // and k-tiles in flight
 
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
-                       void* out, hipStream_t s, int af, int out_assign, int dense_rows) {
+                       void* out, hipStream_t s, int af, int out_assign, int dense_rows, int h_bf16) {
   if (T == 0) return hipSuccess;
+  if (h_bf16 && (stage != 0 || af != kActSplit6)) return hipErrorInvalidValue;
   GemmArgs g;
   g.T = T; g.k = k; g.E = E; g.limit = limit;
   g.out_assign = stage == 1 && out_assign;
   g.dense_rows = stage == 1 && dense_rows;
+  g.h_bf16 = h_bf16;
   g.a_packed = a_packed; g.tiles = tiles; g.codes = codes; g.scales = scales;
   g.topk_w = topk_w; g.out = out;
   const int N = stage == 0 ? 2 * I : D;
@@ -345,7 +349,7 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   if (tile_rows(n_assign, E) != 8) {
     if (g.dense_rows) return hipErrorInvalidValue;     // the dense decode path uses 8-row tiles only
     return launch_gemm_prefill(stage, T, D, I, E, k, limit, a_packed, tiles, codes, scales, topk_w, out, s, af,
-                               out_assign);
+                               out_assign, h_bf16);
   }
   // decode-sized batches (8-row tiles whose activations fit LDS whole)
   const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));

@@ -42,6 +42,7 @@ namespace moe {
 struct PrefillArgs {
   int k, KT, KG, nt, ngroups, out_K;
   int out_assign;                                        // down: rows to their assignment index
+  int h_bf16;                                            // gate/up: h as bf16 rows instead of packed
   float limit;
   const uint8_t* a_packed;
   uint32_t a_bytes, arb;
@@ -381,8 +382,12 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
         const Fp4Block q4 = quant_fp4x32(v);
         if (m < nrows && 2 * ublk < g.nt) store_fp4_block(out + (size_t)(p0 + m) * orb, ublk, q4);
       } else {
-        const Fp6Split sp = split_fp6x32(v);
-        if (m < nrows && 2 * ublk < g.nt) store_fp6_block(out + (size_t)(p0 + m) * orb, ublk, sp);
+        if (g.h_bf16) {
+          if (m < nrows && 2 * ublk < g.nt) store_bf16_block(reinterpret_cast<uint16_t*>(g.out) + (size_t)(p0 + m) * I, ublk, v);
+        } else {
+          const Fp6Split sp = split_fp6x32(v);
+          if (m < nrows && 2 * ublk < g.nt) store_fp6_block(out + (size_t)(p0 + m) * orb, ublk, sp);
+        }
       }
     }
   } else {
@@ -435,9 +440,10 @@ constexpr int kPP = 4;          // weight k-tiles in flight per wavefront
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
                                const uint8_t* scales, const float* topk_w, void* out, hipStream_t s, int af,
-                               int out_assign) {
+                               int out_assign, int h_bf16) {
   PrefillArgs g;
   g.out_assign = stage == 1 && out_assign;
+  g.h_bf16 = stage == 0 && h_bf16;
   const int K = stage == 0 ? D : I;
   const int N = stage == 0 ? 2 * I : D;
   g.k = k;

@@ -225,6 +225,19 @@ __device__ __forceinline__ void store_fp4_block(uint8_t* row, int b, const Fp4Bl
   chunk[32 + (b & 1)] = (uint8_t)q.scale;
 }
 
+// Store block b (32 values, each already a bf16 value held in fp32) of a bf16 row: 64 bytes.
+__device__ __forceinline__ void store_bf16_block(uint16_t* row, int b, const float (&v)[32]) {
+  uint4* dst = reinterpret_cast<uint4*>(row + (size_t)b * kBlock);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (__float_as_uint(v[8 * q + 2 * j]) >> 16) | (__float_as_uint(v[8 * q + 2 * j + 1]) & 0xFFFF0000u);
+    dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Store the 32 values of block b of activation row `row` (bf16 values held in fp32) in the packed
 // activation format: the hi/lo FP6 split (af = kActSplit6) or the MXFP4 quantization (af = kActFp4).
 __device__ __forceinline__ void pack_block_values(const float (&v)[32], int K, long long row, int b,

@@ -148,18 +148,24 @@ hipError_t launch_route_front(int T, int D, int E, int k, const uint16_t* x, con
 size_t route_workspace_bytes(int T, int D, int E);
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int32_t* tiles, hipStream_t s);
+// The row-tile table of a grouping given as offsets [E + 1] and perm (the grouped assignment ids),
+// the same table launch_permute writes (without the grouping's scratch after it).
+hipError_t launch_tiles_from_groups(int T, int E, int k, const int32_t* offsets, const int32_t* perm,
+                                    int32_t* tiles, hipStream_t s);
 hipError_t launch_pack(int K, int rows, const uint16_t* a, uint8_t* packed, hipStream_t s, int af = kActSplit6);
-// out_assign (down stage only): row p of the output goes to the row of its assignment perm[p]
+// out_assign (down stage only): row p of the output goes to the row of its assignment perm[p];
+// h_bf16 (gate/up stage, split activations only): h written as bf16 rows of d_ff, not packed
 // = t*k + j instead of row p, so the combine reads a token's rows without the inverse permutation.
 // dense_rows (down stage only, 8-row tiles): the activation of tile row p is packed h row e*T + t
 // (the dense decode path's gate/up output) instead of row p.
 hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit, const uint8_t* a_packed,
                        const int32_t* tiles, const uint8_t* codes, const uint8_t* scales, const float* topk_w,
-                       void* out, hipStream_t s, int af = kActSplit6, int out_assign = 0, int dense_rows = 0);
+                       void* out, hipStream_t s, int af = kActSplit6, int out_assign = 0, int dense_rows = 0,
+                       int h_bf16 = 0);
 hipError_t launch_gemm_prefill(int stage, int T, int D, int I, int E, int k, float limit,
                                const uint8_t* a_packed, const int32_t* tiles, const uint8_t* codes,
                                const uint8_t* scales, const float* topk_w, void* out, hipStream_t s,
-                               int af = kActSplit6, int out_assign = 0);
+                               int af = kActSplit6, int out_assign = 0, int h_bf16 = 0);
 // inv null: the rows are in assignment order (row t*k + j), as the down stage writes with out_assign
 hipError_t launch_combine(int T, int D, int k, const _Float16* y_perm, const int32_t* inv, const uint16_t* residual,
                           void* y, int y_bf16, hipStream_t s);

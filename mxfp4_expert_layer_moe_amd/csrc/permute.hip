@@ -195,4 +195,71 @@ hipError_t launch_permute(int T, int E, int k, const int32_t* idx, int32_t* coun
   return hipGetLastError();
 }
 
+// ---- the row-tile table from a grouping given as offsets and perm ----------------------------
+// Every workgroup takes the tile counts per expert, ceil((offsets[e+1] - offsets[e]) / bm), and
+// their exclusive scan (the first slot of each expert) in LDS; workgroup 0 writes the slot
+// headers, and every workgroup writes the assignment ids of its share of the grouped positions
+// (grouped position p of expert e is row (p - offsets[e]) % bm of tile (p - offsets[e]) / bm).
+// The result equals the table launch_permute writes for the same grouping.
+constexpr int kTileFromThreads = 256;              // one thread per expert (E <= 256)
+__global__ __launch_bounds__(kTileFromThreads) void tiles_from_groups_kernel(int E, int bm, int slots,
+                                                                             const int32_t* __restrict__ offsets,
+                                                                             const int32_t* __restrict__ perm,
+                                                                             int32_t* __restrict__ tiles) {
+  __shared__ int soff[kTileFromThreads + 1];
+  __shared__ int sfirst[kTileFromThreads];
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += kTileFromThreads) soff[e] = offsets[e];
+  __syncthreads();
+  const int cnt = tid < E ? soff[tid + 1] - soff[tid] : 0;
+  const int ntl = (cnt + bm - 1) / bm;
+  // inclusive scan of ntl over the experts (Hillis-Steele in LDS)
+  sfirst[tid] = ntl;
+  __syncthreads();
+  for (int d = 1; d < kTileFromThreads; d <<= 1) {
+    const int v = tid >= d ? sfirst[tid - d] : 0;
+    __syncthreads();
+    sfirst[tid] += v;
+    __syncthreads();
+  }
+  const int used = sfirst[kTileFromThreads - 1];
+  const int first = sfirst[tid] - ntl;              // exclusive
+  __syncthreads();
+  sfirst[tid] = first;
+  __syncthreads();
+  const int ints = tile_ints(bm);
+  if (blockIdx.x == 0) {
+    for (int i = 0; i < ntl && first + i < slots; ++i)
+      *reinterpret_cast<int4*>(tiles + (size_t)(first + i) * ints) =
+          make_int4(tid, soff[tid] + i * bm, min(bm, cnt - i * bm), used);
+    for (int sl = used + tid; sl < slots; sl += kTileFromThreads)
+      *reinterpret_cast<int4*>(tiles + (size_t)sl * ints) = make_int4(-1, 0, 0, used);
+  }
+  const int n = soff[E];
+  for (int p = blockIdx.x * kTileFromThreads + tid; p < n; p += gridDim.x * kTileFromThreads) {
+    int lo = 0, hi = E;                               // the last e with soff[e] <= p
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (soff[mid] <= p) lo = mid;
+      else hi = mid;
+    }
+    const int q = p - soff[lo];
+    const int slot = sfirst[lo] + q / bm;
+    if (slot < slots) tiles[(size_t)slot * ints + 4 + q % bm] = perm[p];
+  }
+}
+
+hipError_t launch_tiles_from_groups(int T, int E, int k, const int32_t* offsets, const int32_t* perm,
+                                    int32_t* tiles, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (E > kTileFromThreads) return hipErrorInvalidValue;
+  const long long n = (long long)T * k;
+  const int bm = tile_rows(n, E);
+  const long long slots = tile_slots(n, E);
+  const long long wgs = (n + kTileFromThreads - 1) / kTileFromThreads;
+  tiles_from_groups_kernel<<<dim3((unsigned)(wgs < 1024 ? wgs : 1024)), dim3(kTileFromThreads), 0, s>>>(
+      E, bm, (int)slots, offsets, perm, tiles);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -11,9 +11,10 @@ import torch
 
 from . import (MOE_BF16, MOE_FP32, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, dims, moe_act4_pack_bytes, moe_act_pack_bytes,
                moe_block_forward, moe_block_workspace_bytes, moe_combine, moe_combine_residual,
-               moe_expert_gemm_mxfp4, moe_expert_gemm_mxfp4_act4, moe_forward, moe_forward_act4, moe_mxfp4_prepack,
-               moe_pack_act, moe_pack_act4, moe_permute, moe_rmsnorm, moe_route, moe_route_workspace_bytes,
-               moe_tile_table_bytes, moe_weights, moe_workspace_bytes, moe_workspace_bytes_act4)
+               moe_expert_gemm_mxfp4, moe_expert_gemm_mxfp4_act4, moe_expert_gemm_mxfp4_packed, moe_forward,
+               moe_forward_act4, moe_mxfp4_prepack, moe_pack_act, moe_pack_act4, moe_permute, moe_permute_tiles,
+               moe_rmsnorm, moe_route, moe_route_workspace_bytes, moe_tile_table_bytes, moe_weights,
+               moe_workspace_bytes, moe_workspace_bytes_act4)
 
 
 def _u8(a: np.ndarray, device) -> torch.Tensor:
@@ -92,21 +93,21 @@ class DeviceLayer:
                   self.topk_w, self.logits if logits else None, self.route_ws, None, stream)
 
     def permute(self, stream=None):
-        moe_permute(self.dims, self.T, self.topk_idx, self.counts, self.offsets, self.perm, self.inv, self.tiles,
-                    stream)
+        moe_permute_tiles(self.dims, self.T, self.topk_idx, self.counts, self.offsets, self.perm, self.inv,
+                          self.tiles, stream)
 
     def pack_x(self, stream=None, x=None):
         moe_pack_act(self.D, self.T, self.x if x is None else x, self.x_packed, stream)
 
     def gate_up(self, weights: DeviceWeights | None = None, stream=None):
         w = weights or self.weights
-        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_GATE_UP, self.x_packed, self.tiles, w.gu_codes,
-                              w.gu_scales, None, self.h_packed, stream)
+        moe_expert_gemm_mxfp4_packed(self.dims, self.T, MOE_STAGE_GATE_UP, self.x_packed, self.tiles, w.gu_codes,
+                                     w.gu_scales, None, self.h_packed, stream)
 
     def down(self, weights: DeviceWeights | None = None, stream=None):
         w = weights or self.weights
-        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_DOWN, self.h_packed, self.tiles, w.dn_codes,
-                              w.dn_scales, self.topk_w, self.y_perm, stream)
+        moe_expert_gemm_mxfp4_packed(self.dims, self.T, MOE_STAGE_DOWN, self.h_packed, self.tiles, w.dn_codes,
+                                     w.dn_scales, self.topk_w, self.y_perm, stream)
 
     def combine(self, bf16=False, stream=None, residual=None):
         y, dt = (self.y16, MOE_BF16) if bf16 else (self.y32, MOE_FP32)
@@ -114,6 +115,21 @@ class DeviceLayer:
             moe_combine(self.dims, self.T, self.y_perm, self.inv, y, dt, stream)
         else:
             moe_combine_residual(self.dims, self.T, self.y_perm, self.inv, residual, y, dt, stream)
+
+    # ---- the plain boundary: bf16 rows, perm and offsets, scratch from the workspace ----------
+    def permute_plain(self, stream=None):
+        moe_permute(self.dims, self.T, self.topk_idx, self.counts, self.offsets, self.perm, self.inv, self.ws,
+                    self.ws.numel(), stream)
+
+    def gate_up_plain(self, h_bf16, weights: DeviceWeights | None = None, stream=None, x=None):
+        w = weights or self.weights
+        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_GATE_UP, self.x if x is None else x, self.perm,
+                              self.offsets, w.gu_codes, w.gu_scales, None, h_bf16, self.ws, self.ws.numel(), stream)
+
+    def down_plain(self, h_bf16, weights: DeviceWeights | None = None, stream=None):
+        w = weights or self.weights
+        moe_expert_gemm_mxfp4(self.dims, self.T, MOE_STAGE_DOWN, h_bf16, self.perm, self.offsets, w.dn_codes,
+                              w.dn_scales, self.topk_w, self.y_perm, self.ws, self.ws.numel(), stream)
 
     def steps(self, bf16=False, stream=None):
         self.route(stream=stream)

@@ -109,10 +109,18 @@ def test_bad_arguments_rejected_before_launch(L):
     assert L.moe_route(d, 64, A, A, A, A, A, None, A + 16, R, None) == M.MOE_EINVAL         # misaligned ws
     assert L.moe_route(d, 64, A, A, A, A, A, None, A, R - 1, None) == M.MOE_EWORKSPACE
     assert L.moe_route(d, 0, A, A, A, A, A, None, None, 0, None) == M.MOE_OK               # T = 0: no-op
-    assert L.moe_permute(d, 4, A, A, A, None, A, A, None) == M.MOE_EINVAL
-    assert L.moe_permute(d, 4, A, A, A, A, A, None, None) == M.MOE_EINVAL             # no tile table
-    assert L.moe_permute(d, 4, A, A, A, A, A, A + 4, None) == M.MOE_EINVAL            # misaligned tiles
-    assert L.moe_permute(d, 0, A, A, A, A, A, A, None) == M.MOE_OK
+    assert L.moe_permute_tiles(d, 4, A, A, A, None, A, A, None) == M.MOE_EINVAL
+    assert L.moe_permute_tiles(d, 4, A, A, A, A, A, None, None) == M.MOE_EINVAL       # no tile table
+    assert L.moe_permute_tiles(d, 4, A, A, A, A, A, A + 4, None) == M.MOE_EINVAL      # misaligned tiles
+    assert L.moe_permute_tiles(d, 0, A, A, A, A, A, A, None) == M.MOE_OK
+    # the plain form: scratch instead of the tile table
+    P = L.moe_permute_workspace_bytes(d, 4)
+    assert P == L.moe_tile_table_bytes(d, 4) and P <= L.moe_workspace_bytes(d, 4)
+    assert L.moe_permute(d, 4, A, A, A, None, A, A, P, None) == M.MOE_EINVAL
+    assert L.moe_permute(d, 4, A, A, A, A, A, None, P, None) == M.MOE_EINVAL              # no workspace
+    assert L.moe_permute(d, 4, A, A, A, A, A, A + 16, P, None) == M.MOE_EINVAL            # misaligned workspace
+    assert L.moe_permute(d, 4, A, A, A, A, A, A, P - 1, None) == M.MOE_EWORKSPACE
+    assert L.moe_permute(d, 0, A, A, A, A, A, None, 0, None) == M.MOE_OK
     # tile table: 8-row tiles (48-int slots) up to 6 assignments per expert on average, 128-row
     # tiles (132-int slots) beyond
     # followed by the grouping's scratch: [G][E] counts (G = ceil(n / 1024)) and E + 1 tile starts,
@@ -128,11 +136,26 @@ def test_bad_arguments_rejected_before_launch(L):
     assert L.moe_pack_act(96, 4, A, A, None) == M.MOE_EUNSUPPORTED
     assert L.moe_pack_act(64, 4, A, A + 8, None) == M.MOE_EINVAL
     assert L.moe_pack_act(64, 0, A, A, None) == M.MOE_OK
-    assert L.moe_expert_gemm_mxfp4(d, 4, 7, A, A, A, A, A, A, None) == M.MOE_EINVAL
-    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, None, A, None) == M.MOE_EINVAL
-    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_GATE_UP, A, A, A + 4, A, None, A, None) == M.MOE_EINVAL
-    assert L.moe_expert_gemm_mxfp4(d, 4, M.MOE_STAGE_GATE_UP, A, A + 8, A, A, None, A, None) == M.MOE_EINVAL
-    assert L.moe_expert_gemm_mxfp4(d, 0, M.MOE_STAGE_GATE_UP, A, A, A, A, None, A, None) == M.MOE_OK
+    assert L.moe_expert_gemm_mxfp4_packed(d, 4, 7, A, A, A, A, A, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4_packed(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4_packed(d, 4, M.MOE_STAGE_GATE_UP, A, A, A + 4, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4_packed(d, 4, M.MOE_STAGE_GATE_UP, A, A + 8, A, A, None, A, None) == M.MOE_EINVAL
+    assert L.moe_expert_gemm_mxfp4_packed(d, 0, M.MOE_STAGE_GATE_UP, A, A, A, A, None, A, None) == M.MOE_OK
+    # the plain form: bf16 rows, perm and offsets, scratch = the tile table + the packed rows
+    for st, rows, K in ((M.MOE_STAGE_GATE_UP, 4, 2880), (M.MOE_STAGE_DOWN, 16, 2880)):
+        G = L.moe_expert_gemm_workspace_bytes(d, 4, st)
+        assert G == -(-L.moe_tile_table_bytes(d, 4) // 256) * 256 + L.moe_act_pack_bytes(K, rows)
+        assert G <= L.moe_workspace_bytes(d, 4)
+    G = L.moe_expert_gemm_workspace_bytes(d, 4, M.MOE_STAGE_DOWN)
+    assert L.moe_expert_gemm_workspace_bytes(d, 4, 7) == 0
+    gemm = L.moe_expert_gemm_mxfp4
+    assert gemm(d, 4, 7, A, A, A, A, A, A, A, A, G, None) == M.MOE_EINVAL
+    assert gemm(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, A, None, A, A, G, None) == M.MOE_EINVAL   # no gates
+    assert gemm(d, 4, M.MOE_STAGE_DOWN, A, None, A, A, A, A, A, A, G, None) == M.MOE_EINVAL   # no perm
+    assert gemm(d, 4, M.MOE_STAGE_DOWN, A + 2, A, A, A, A, A, A, A, G, None) == M.MOE_EINVAL  # misaligned rows
+    assert gemm(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, A, A, A, None, G, None) == M.MOE_EINVAL   # no workspace
+    assert gemm(d, 4, M.MOE_STAGE_DOWN, A, A, A, A, A, A, A, A, G - 1, None) == M.MOE_EWORKSPACE
+    assert gemm(d, 0, M.MOE_STAGE_GATE_UP, A, A, A, A, A, None, A, None, 0, None) == M.MOE_OK
     assert L.moe_combine(d, 4, A, A, A, 5, None) == M.MOE_EINVAL
     assert L.moe_combine(d, 4, A, A, A + 4, M.MOE_FP32, None) == M.MOE_EINVAL
     # the inverse permutation is required: only the whole-layer path reads rows without it

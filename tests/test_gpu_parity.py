@@ -167,10 +167,10 @@ def test_identity_activation_probe_down_gemm_is_exact():
     counts, offsets = torch.empty(1, **i32), torch.empty(2, **i32)
     perm, inv = torch.empty(I, **i32), torch.empty(I, **i32)
     tiles = torch.empty(M.moe_tile_table_bytes(d, I) // 4, **i32)
-    M.moe_permute(d, I, idx, counts, offsets, perm, inv, tiles)
+    M.moe_permute_tiles(d, I, idx, counts, offsets, perm, inv, tiles)
     w = torch.ones(I, dtype=torch.float32, device=dev)
     y = torch.empty((I, D), dtype=torch.float16, device=dev)
-    M.moe_expert_gemm_mxfp4(d, I, M.MOE_STAGE_DOWN, hp, tiles, torch.from_numpy(dc).to(dev),
+    M.moe_expert_gemm_mxfp4_packed(d, I, M.MOE_STAGE_DOWN, hp, tiles, torch.from_numpy(dc).to(dev),
                             torch.from_numpy(ds).to(dev), w, y)
     torch.cuda.synchronize()
     from tests import actpack
@@ -235,7 +235,7 @@ def test_maximum_batch_full_shape():
 
 
 def test_invalid_expert_ids_get_no_row():
-    """moe_permute with expert ids outside [0, E) (a caller error): those assignments are left out
+    """moe_permute_tiles with expert ids outside [0, E) (a caller error): those assignments are left out
     of counts, perm and the tiles, their inv entry is -1, and moe_combine skips them."""
     import mxfp4_expert_layer_moe_amd as M
     T, E, k, D = 40, 6, 2, 64
@@ -251,7 +251,7 @@ def test_invalid_expert_ids_get_no_row():
     counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
     perm, inv = torch.full((n,), 12345, **i32), torch.full((n,), 12345, **i32)
     tiles = torch.empty(M.moe_tile_table_bytes(d, T) // 4, **i32)
-    M.moe_permute(d, T, torch.from_numpy(idx).to(dev), counts, offsets, perm, inv, tiles)
+    M.moe_permute_tiles(d, T, torch.from_numpy(idx).to(dev), counts, offsets, perm, inv, tiles)
     yp = torch.from_numpy(rng.standard_normal((n, D)).astype(np.float16)).to(dev)
     y = torch.empty((T, D), dtype=torch.float32, device=dev)
     M.moe_combine(d, T, yp, inv, y, M.MOE_FP32)
