@@ -73,27 +73,12 @@ static_assert(kPSlots * kPSlotBytes >= 4 * 32 * kPEpiStride * 4, "h transpositio
 static_assert(4 * kPSlotBytes / 4 >= 32 * kPOutStride * 2, "y transposition fits a wavefront's quarter of the down ring");
 
 // Matrix-instruction pairing.  Each 64-wide k-tile holds two 32-value blocks b = 0, 1 of the
-// activation, each stored as hi + lo FP6 terms.  One MFMA per block: lanes 0-31 supply the hi term
-// and lanes 32-63 the lo term of block b as the instruction's two K halves, and the weight operand
-// holds block b in both halves, so the instruction sums (hi + lo) * w over the block.  A lane half's
-// two 24-byte terms are the 48 contiguous bytes at 48h of the row chunk: read as twelve dwords,
-// block 0's operand is dwords 0-5 and block 1's dwords 6-11 (register sub-ranges, no copies).
+// activation, each stored as hi + lo FP6 terms.  Two MFMAs per weight tile, one per term: lane half
+// b supplies block b's hi term to the first and its lo term to the second, as the instruction's K
+// halves, so the weight operand and its scales are used as loaded (lane half b: block b).  The
+// lane's two 24-byte terms sit at 24b and 48 + 24b of the row chunk: read as twelve dwords, the hi
+// operand is dwords 0-5 and the lo operand dwords 6-11 (register sub-ranges, no copies).
 typedef int v16i __attribute__((ext_vector_type(16)));
-
-// both halves of the weight register: [block 0 | block 0] and [block 1 | block 1]
-__device__ __forceinline__ void split_halves(const v4i x, v4i& b0, v4i& b1) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x[d], (unsigned)x[d], false, false);
-    b0[d] = (int)r[0];
-    b1[d] = (int)r[1];
-  }
-}
-__device__ __forceinline__ void split_halves(const uint32_t x, uint32_t& s0, uint32_t& s1) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  s0 = r[0];
-  s1 = r[1];
-}
 
 // NA: activation k-tiles in flight in registers (k-tile t is fetched NA k-tiles before it is
 // written to LDS); P: weight k-tiles in flight per wavefront.  Both divide 8.
@@ -204,7 +189,6 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   for (int t = kAhead; t < kAhead + NA; ++t) load_a(min(t, KT - 1), abuf[t % NA]);
   v4i bq[P][kPWaveTiles];
   uint32_t sq[2][kPWaveTiles];
-  uint32_t sqd[kPWaveTiles][2];                          // current scale group, per block
 #pragma unroll
   for (int j = 0; j < P; ++j)
 #pragma unroll
@@ -224,10 +208,11 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
 
   const int r32 = lane & 31;
   const int h = lane >> 5;
-  // A operands of (k-tile kt, row block rb) from the staged slot kt % 4
-  // block b's term of this lane half (h = 0: hi, 1: lo) sits at bytes [48h + 24b, 48h + 24b + 24)
-  // of the row chunk; the scale bytes are [hi0, hi1, lo0, lo1] at 96, so the half's two scales are
-  // the 16 bits at 96 + 2h (byte b for block b, chosen by the instruction's A-scale byte select).
+  // A operands of (k-tile kt, row block rb) from the staged ring slot
+  // this lane half's block h has its hi term at bytes [24h, 24h + 24) of the row chunk and its lo
+  // term at [48 + 24h, 72 + 24h); the scale bytes are [hi0, hi1, lo0, lo1] at 96, so the scale
+  // dword shifted right by 8h holds the block's hi scale in byte 0 and its lo scale in byte 2
+  // (chosen by the instruction's A-scale byte select).
   // Loads only: nothing waits for them until the operands are used a phase later.
   struct AOps {
     v16i q;
@@ -242,11 +227,16 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
       o.s = row[32 + h];
       return o;
     }
-    const v4i q0 = *reinterpret_cast<const v4i*>(row + 48 * h);
-    const v4i q1 = *reinterpret_cast<const v4i*>(row + 48 * h + 16);
-    const v4i q2 = *reinterpret_cast<const v4i*>(row + 48 * h + 32);
-    o.q = v16i{q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w, q2.x, q2.y, q2.z, q2.w, 0, 0, 0, 0};
-    o.s = *reinterpret_cast<const uint16_t*>(row + 96 + 2 * h);
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const uint8_t* hi = row + 24 * h;
+    const v2i q0 = *reinterpret_cast<const v2i*>(hi);
+    const v2i q1 = *reinterpret_cast<const v2i*>(hi + 8);
+    const v2i q2 = *reinterpret_cast<const v2i*>(hi + 16);
+    const v2i q3 = *reinterpret_cast<const v2i*>(hi + 48);
+    const v2i q4 = *reinterpret_cast<const v2i*>(hi + 56);
+    const v2i q5 = *reinterpret_cast<const v2i*>(hi + 64);
+    o.q = v16i{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y, q4.x, q4.y, q5.x, q5.y, 0, 0, 0, 0};
+    o.s = *reinterpret_cast<const uint32_t*>(row + 96) >> (8 * h);
     return o;
   };
   // Software pipeline of one k-tile (kt, j = kt % 8, compile-time ring slots), in four phases of
@@ -254,22 +244,11 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
   //  - operands are read one row block ahead; the next k-tile's first block is read at the end of
   //    this k-tile (its slot was published by an earlier barrier);
   //  - phase 0 stages k-tile kt + A, phase 1 fetches k-tile kt + A + NA (A = stage_ahead);
-  //  - phase 2 splits the next k-tile's weight registers by block (and the next scale group);
   //  - phase 3 refills the weight ring slot just consumed.
   // A scheduling barrier between phases keeps each phase's work next to its matrix instructions.
   AOps nxt = read_ops(0, 0);
-  v4i bw[kPWaveTiles][2];
-  if constexpr (!F4) {
-#pragma unroll
-    for (int cb = 0; cb < kPWaveTiles; ++cb) {
-      split_halves(bq[0][cb], bw[cb][0], bw[cb][1]);
-      split_halves(sq[0][cb], sqd[cb][0], sqd[cb][1]);
-    }
-  }
   auto step = [&](const int kt, const int j) __attribute__((always_inline)) {
     constexpr int D = kAhead;
-    v4i bwn[kPWaveTiles][2];
-    uint32_t sqn[kPWaveTiles][2];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       AOps cur;
@@ -284,24 +263,18 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
         for (int cb = 0; cb < kPWaveTiles; ++cb)
           acc[rb][cb] = mma4_sel(j & 3, a, b_operand(bq[j % P][cb]), acc[rb][cb], cur.s, sq[(j >> 2) & 1][cb]);
       } else {
-        const v8i a0 = __builtin_shufflevector(cur.q, cur.q, 0, 1, 2, 3, 4, 5, 6, 7);
-        const v8i a1 = __builtin_shufflevector(cur.q, cur.q, 6, 7, 8, 9, 10, 11, 12, 13);
+        const v8i ahi = __builtin_shufflevector(cur.q, cur.q, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v8i alo = __builtin_shufflevector(cur.q, cur.q, 6, 7, 8, 9, 10, 11, 12, 13);
 #pragma unroll
         for (int cb = 0; cb < kPWaveTiles; ++cb) {
-          acc[rb][cb] = mma_sel_a<0>(j & 3, a0, b_operand(bw[cb][0]), acc[rb][cb], cur.s, sqd[cb][0]);
-          acc[rb][cb] = mma_sel_a<1>(j & 3, a1, b_operand(bw[cb][1]), acc[rb][cb], cur.s, sqd[cb][1]);
+          const v8i b = b_operand(bq[j % P][cb]);
+          const uint32_t sb = sq[(j >> 2) & 1][cb];
+          acc[rb][cb] = mma_sel_a<0>(j & 3, ahi, b, acc[rb][cb], cur.s, sb);
+          acc[rb][cb] = mma_sel_a<2>(j & 3, alo, b, acc[rb][cb], cur.s, sb);
         }
       }
       if (rb == 0) store_a((kt + D) & (kSlots - 1), abuf[(j + D) % NA]);       // stage kt + D
       if (rb == 1) load_a(min(kt + D + NA, KT - 1), abuf[(j + D) % NA]);        // fetch kt + D + NA
-      if (!F4 && rb == 2) {
-#pragma unroll
-        for (int cb = 0; cb < kPWaveTiles; ++cb) {
-          split_halves(bq[(j + 1) % P][cb], bwn[cb][0], bwn[cb][1]);
-          // the next k-tile opens a scale group: its dwords (loaded a group ago) by block
-          if ((j & 3) == 3) split_halves(sq[((j >> 2) + 1) & 1][cb], sqn[cb][0], sqn[cb][1]);
-        }
-      }
       if (rb == 3) {
 #pragma unroll
         for (int cb = 0; cb < kPWaveTiles; ++cb) bq[j % P][cb] = load_b(cb, min(kt + P, KT - 1));
@@ -328,15 +301,6 @@ __global__ __launch_bounds__(256) void expert_gemm_prefill_kernel(PrefillArgs g)
     static_assert(kAhead >= B + 1 && kSlots >= kAhead + B, "ring publishing order");
     if (j % B == B - 1) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int cb = 0; cb < (F4 ? 0 : kPWaveTiles); ++cb) {
-      bw[cb][0] = bwn[cb][0];
-      bw[cb][1] = bwn[cb][1];
-      if ((j & 3) == 3) {
-        sqd[cb][0] = sqn[cb][0];
-        sqd[cb][1] = sqn[cb][1];
-      }
-    }
   };
   if constexpr (KTC > 0) {
 #pragma unroll
