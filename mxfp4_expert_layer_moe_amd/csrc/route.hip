@@ -237,44 +237,55 @@ constexpr int kWideRowBytes = 128 + 16;        // one expert row of a round in b
 constexpr int kWidePlane = 32 * kWideRowBytes; // one term of a round
 constexpr int kWideBuf = 3 * kWidePlane;
 
-__global__ __launch_bounds__(kWideWaves * 64) void route_logits_wide_kernel(
+template <int TQ>
+__global__ __launch_bounds__(TQ * 256) void route_logits_wide_kernel(
     int T, int D, int E, int KW, const uint16_t* __restrict__ x, const float* __restrict__ wr,
     double* __restrict__ logit, float* __restrict__ xsq, float* __restrict__ wsq, int logit_wgs,
     uint8_t* __restrict__ xpack, int af) {
-  constexpr int kRedBytes = 4 * 2 * 32 * 33 * 8;                 // [k-step lane][tile][token][expert]
+  constexpr int kThreads = TQ * 256;                             // TQ token tiles x 4 k-step lanes
+  constexpr int kTokens = TQ * 32;
+  constexpr int kPer = 2048 / kThreads;                          // router values per thread and round
+  constexpr int kRowThreads = 64 / kPer;                         // threads per expert row of a round
+  constexpr int kRedBytes = 4 * TQ * 32 * 33 * 8;                // [k-step lane][tile][token][expert]
   static_assert(2 * kWideBuf <= kRedBytes, "the ring fits the reduction area");
   __shared__ __align__(16) uint8_t smem[kRedBytes];
-  __shared__ float rsx[4][2][32];                               // partial ||x_t||^2
+  __shared__ float rsx[4][TQ][32];                               // partial ||x_t||^2
   if ((int)blockIdx.x >= logit_wgs) {                           // activation split, one block per lane
-    const long long blk = (long long)(blockIdx.x - logit_wgs) * (kWideWaves * 64) + threadIdx.x;
+    const long long blk = (long long)(blockIdx.x - logit_wgs) * kThreads + threadIdx.x;
     pack_block_lane(x, D, (long long)T * (D / kBlock), blk, xpack, af);
     return;
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int tq = wave & 1, kq = wave >> 1;
+  const int tq = wave % TQ, kq = wave / TQ;
   const int nte = (E + 31) / 32;
   const int kw = blockIdx.x % KW;
   const int nt = (blockIdx.x / KW) % nte;
   const int tb = blockIdx.x / (KW * nte);
   const int epad = nte * 32;
   const int row = lane & 31, half = lane >> 5;
-  const int tok = tb * kWideTokens + tq * 32 + row;
+  const int tok = tb * kTokens + tq * 32 + row;
   const int rounds = D / 64;
   const int r0 = rounds * kw / KW, r1 = rounds * (kw + 1) / KW;
-  // this thread's float4 of every router chunk, and its x row (clamped; masked at the end)
-  const int wrow = tid >> 4, wc4 = tid & 15;
+  // the token norms are stored by the first expert tile's workgroups only (the 64-token form
+  // computes them everywhere: the branch costs it more than the arithmetic)
+  const bool norms = TQ == 2 || nt == 0;
+  // this thread's kPer values of every router chunk, and its x row (clamped; masked at the end)
+  const int wrow = tid / kRowThreads, wc = tid % kRowThreads;
   const bool wlive = nt * 32 + wrow < E;
-  const float* wsrc = wr + (size_t)min(nt * 32 + wrow, E - 1) * D + 4 * wc4;
+  const float* wsrc = wr + (size_t)min(nt * 32 + wrow, E - 1) * D + kPer * wc;
   const uint16_t* xa = x + (size_t)min(tok, T - 1) * D + 16 * kq + 8 * half;
+  typedef float vw __attribute__((ext_vector_type(kPer)));
   auto load_w = [&](const int r) {
-    return wlive && r < r1 ? *reinterpret_cast<const float4*>(wsrc + 64 * r) : make_float4(0.f, 0.f, 0.f, 0.f);
+    vw v = {};
+    if (wlive && r < r1) v = *reinterpret_cast<const vw*>(wsrc + 64 * r);
+    return v;
   };
   auto load_x = [&](const int r) {
     return r < r1 ? *reinterpret_cast<const uint4*>(xa + 64 * r) : make_uint4(0, 0, 0, 0);
   };
-  float4 wq[2] = {load_w(r0), load_w(r0 + 1)};
+  vw wq[2] = {load_w(r0), load_w(r0 + 1)};
   uint4 xq[2] = {load_x(r0), load_x(r0 + 1)};
   double accd[16];
 #pragma unroll
@@ -283,15 +294,23 @@ __global__ __launch_bounds__(kWideWaves * 64) void route_logits_wide_kernel(
   auto round = [&](const int r, const int slot) __attribute__((always_inline)) {
     uint8_t* buf = smem + slot * kWideBuf;
     {
-      const float wv[4] = {wq[slot].x, wq[slot].y, wq[slot].z, wq[slot].w};
-      uint32_t hu[2], mu[2], lu[2];
-      split_terms<4>(wv, hu, mu, lu);
+      float wv[kPer];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sq += wv[i] * wv[i];
-      uint8_t* dst = buf + wrow * kWideRowBytes + wc4 * 8;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(hu[0], hu[1]);
-      *reinterpret_cast<uint2*>(dst + kWidePlane) = make_uint2(mu[0], mu[1]);
-      *reinterpret_cast<uint2*>(dst + 2 * kWidePlane) = make_uint2(lu[0], lu[1]);
+      for (int i = 0; i < kPer; ++i) wv[i] = wq[slot][i];
+      uint32_t hu[kPer / 2], mu[kPer / 2], lu[kPer / 2];
+      split_terms<kPer>(wv, hu, mu, lu);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) sq += wv[i] * wv[i];
+      uint8_t* dst = buf + wrow * kWideRowBytes + wc * (2 * kPer);
+      if constexpr (kPer == 4) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(hu[0], hu[1]);
+        *reinterpret_cast<uint2*>(dst + kWidePlane) = make_uint2(mu[0], mu[1]);
+        *reinterpret_cast<uint2*>(dst + 2 * kWidePlane) = make_uint2(lu[0], lu[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = hu[0];
+        *reinterpret_cast<uint32_t*>(dst + kWidePlane) = mu[0];
+        *reinterpret_cast<uint32_t*>(dst + 2 * kWidePlane) = lu[0];
+      }
     }
     const uint4 xu = xq[slot];
     wq[slot] = load_w(r + 2);
@@ -301,11 +320,13 @@ __global__ __launch_bounds__(kWideWaves * 64) void route_logits_wide_kernel(
     const uint4 hb = *reinterpret_cast<const uint4*>(bb);
     const uint4 mb = *reinterpret_cast<const uint4*>(bb + kWidePlane);
     const uint4 lb = *reinterpret_cast<const uint4*>(bb + 2 * kWidePlane);
-    const uint32_t uw[4] = {xu.x, xu.y, xu.z, xu.w};
+    if (norms) {
+      const uint32_t uw[4] = {xu.x, xu.y, xu.z, xu.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = __uint_as_float(uw[i] << 16), hi = __uint_as_float(uw[i] & 0xFFFF0000u);
-      xs += lo * lo + hi * hi;
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(uw[i] << 16), hi = __uint_as_float(uw[i] & 0xFFFF0000u);
+        xs += lo * lo + hi * hi;
+      }
     }
     const v8bf a = __builtin_bit_cast(v8bf, xu);
     v16f t = {};
@@ -324,26 +345,29 @@ __global__ __launch_bounds__(kWideWaves * 64) void route_logits_wide_kernel(
   }
   if (r < r1) round(r, 0);
   __syncthreads();                                              // the ring is free
-  double (*red)[2][32][33] = reinterpret_cast<double (*)[2][32][33]>(smem);
+  double (*red)[TQ][32][33] = reinterpret_cast<double (*)[TQ][32][33]>(smem);
 #pragma unroll
   for (int i = 0; i < 16; ++i) red[kq][tq][8 * (i >> 2) + 4 * half + (i & 3)][row] = accd[i];
-  xs += __shfl_xor(xs, 32);
-  if (half == 0) rsx[kq][tq][row] = xs;
-  // the router rows' squared norms over this K slice: 16 threads per row, summed in a fixed order
+  if (norms) {
+    xs += __shfl_xor(xs, 32);
+    if (half == 0) rsx[kq][tq][row] = xs;
+  }
+  // the router rows' squared norms over this K slice: kRowThreads threads per row, summed in a
+  // fixed order
 #pragma unroll
-  for (int d = 8; d >= 1; d >>= 1) sq += __shfl_xor(sq, d);
-  if (tb == 0 && wc4 == 0) wsq[(size_t)kw * epad + nt * 32 + wrow] = sq;
+  for (int d = kRowThreads / 2; d >= 1; d >>= 1) sq += __shfl_xor(sq, d);
+  if (tb == 0 && wc == 0) wsq[(size_t)kw * epad + nt * 32 + wrow] = sq;
   __syncthreads();
-  for (int j = tid; j < 2 * 32 * 32; j += kWideWaves * 64) {
+  for (int j = tid; j < TQ * 32 * 32; j += kThreads) {
     const int q = j >> 10, m = (j >> 5) & 31, c = j & 31;
     const double v = ((red[0][q][m][c] + red[1][q][m][c]) + red[2][q][m][c]) + red[3][q][m][c];
-    const int tj = tb * kWideTokens + q * 32 + m;
+    const int tj = tb * kTokens + q * 32 + m;
     if (tj < T) logit[((size_t)kw * T + tj) * epad + nt * 32 + c] = v;
   }
-  if (nt == 0 && tid < 64) {
+  if (nt == 0 && tid < TQ * 32) {
     const int q = tid >> 5, m = tid & 31;
     const float v = ((rsx[0][q][m] + rsx[1][q][m]) + rsx[2][q][m]) + rsx[3][q][m];
-    const int tj = tb * kWideTokens + q * 32 + m;
+    const int tj = tb * kTokens + q * 32 + m;
     if (tj < T) xsq[(size_t)kw * T + tj] = v;
   }
 }
@@ -582,9 +606,18 @@ static hipError_t launch_logits_wide(int T, int D, int E, const uint16_t* x, con
   *wsq = reinterpret_cast<float*>(base + L.wsq);
   const long long pack_blocks = xpack ? (long long)T * (D / kBlock) : 0;
   const int nte = (E + 31) / 32;
+  // 128-token workgroups (16 wavefronts, one per compute unit) once they fill the chip, so each
+  // router weight is split once per 128 tokens; 64-token workgroups of 8 wavefronts before that
+  if (*KW == 1 && ((T + 127) / 128) * nte >= 256) {
+    const int logit_wgs = ((T + 127) / 128) * nte;
+    const long long pack_wgs = (pack_blocks + 1023) / 1024;
+    route_logits_wide_kernel<4><<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(1024), 0, s>>>(
+        T, D, E, 1, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
+    return hipGetLastError();
+  }
   const int logit_wgs = ((T + kWideTokens - 1) / kWideTokens) * nte * *KW;
   const long long pack_wgs = (pack_blocks + kWideWaves * 64 - 1) / (kWideWaves * 64);
-  route_logits_wide_kernel<<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kWideWaves * 64), 0, s>>>(
+  route_logits_wide_kernel<2><<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(kWideWaves * 64), 0, s>>>(
       T, D, E, *KW, x, wr, *logit, *xsq, *wsq, logit_wgs, xpack, af);
   return hipGetLastError();
 }
