@@ -235,7 +235,11 @@ moe_status moe_pack_act(int32_t K, int32_t rows, const void* a_bf16, void* a_pac
  *              gate-weighted expert output; its magnitude must stay below the
  *              fp16 maximum (65504)
  *  codes/scales  prepacked weights of the stage (moe_mxfp4_prepack)
- *  perm, offsets  moe_permute's outputs for the same T
+ *  perm, offsets  moe_permute's outputs for the same T: offsets[0] = 0 <= ... <=
+ *            offsets[E] = T*top_k and perm a permutation of [0, T*top_k)
+ *            grouping the assignments by expert.  These are read on the device
+ *            and not checked: other values can make the kernels read outside a
+ *            and topk_w.
  *  ws        device scratch of at least moe_expert_gemm_workspace_bytes(dims, T,
  *            stage) bytes (moe_workspace_bytes(dims, T) is always enough),
  *            256-byte aligned: the row-tile table built from perm and offsets,
