@@ -44,7 +44,9 @@ struct GemmArgs {
   size_t codes_per_expert, scales_per_expert;
 };
 
-constexpr int kAStageBytes = 40 * 1024;     // LDS for staged activation rows: 8 rows of K = 2880 fit whole
+// LDS for staged activation rows: 8 rows of K = 2880 fit whole, and with the row ids the workgroup
+// takes 40960 bytes, so four workgroups share a compute unit's 160 KB
+constexpr int kAStageBytes = 40 * 1024 - 32;
 
 __device__ inline v8i a_operand_lds(const uint8_t* p) {      // 24 bytes, 8-byte aligned
   const uint2* q = reinterpret_cast<const uint2*>(p);
@@ -354,7 +356,7 @@ hipError_t launch_gemm(int stage, int T, int D, int I, int E, int k, float limit
   // decode-sized batches (8-row tiles whose activations fit LDS whole)
   const dim3 grid((g.units + 3) / 4, (unsigned)tile_slots(n_assign, E));
   // the model's K = 2880 (45 k-tiles): fully unrolled k-loop
-  const bool k45 = g.KT == 45 && 8 * stage_stride(45) <= kAStageBytes;   // 40384 <= 40960
+  const bool k45 = g.KT == 45 && 8 * stage_stride(45) <= kAStageBytes;   // 40384 <= 40928
   if (af == kActFp4) {
     if (stage == 0) {
       if (k45) expert_gemm_kernel<0, kGateUpP, 8, 45, 1, 1, 2, kActFp4><<<grid, dim3(256), 0, s>>>(g);

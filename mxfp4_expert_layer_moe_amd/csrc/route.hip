@@ -607,8 +607,10 @@ static hipError_t launch_logits_wide(int T, int D, int E, const uint16_t* x, con
   const long long pack_blocks = xpack ? (long long)T * (D / kBlock) : 0;
   const int nte = (E + 31) / 32;
   // 128-token workgroups (16 wavefronts, one per compute unit) once they fill the chip, so each
-  // router weight is split once per 128 tokens; 64-token workgroups of 8 wavefronts before that
-  if (*KW == 1 && ((T + 127) / 128) * nte >= 256) {
+  // router weight is split once per 128 tokens; 64-token workgroups of 8 wavefronts before that.
+  // Not with the activation split in the same launch: its workgroups would take the 137 KB of LDS
+  // too, one per compute unit, and wait behind the logit workgroups.
+  if (!xpack && *KW == 1 && ((T + 127) / 128) * nte >= 256) {
     const int logit_wgs = ((T + 127) / 128) * nte;
     const long long pack_wgs = (pack_blocks + 1023) / 1024;
     route_logits_wide_kernel<4><<<dim3((unsigned)(logit_wgs + pack_wgs)), dim3(1024), 0, s>>>(
