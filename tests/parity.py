@@ -237,3 +237,19 @@ def compare(inp, g: dict, o: dict, check_h: bool = True) -> dict:
     assert dy.max() <= TOL_Y * rms_y, stats
     assert np.array_equal(g["y16"], rne_bf16_bits(g["y32"]))
     return stats
+
+
+def record_stats(case: str, stats: dict) -> None:
+    """Append a case's error statistics as one JSON line to parity_stats.jsonl in the directory named
+    by MOE_PARITY_STATS_DIR (nothing is written when it is unset)."""
+    import json
+    import os
+    d = os.environ.get("MOE_PARITY_STATS_DIR")
+    if not d:
+        return
+    try:
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "parity_stats.jsonl"), "a") as f:
+            f.write(json.dumps(dict(case=case, **stats)) + "\n")
+    except OSError:
+        pass

@@ -9,7 +9,6 @@ fraction below 1e-3 of the elements); y within 2e-2 x RMS(y) of the act4 oracle;
 output equal to RNE(fp32); moe_forward_act4 equal to the step calls and deterministic.
 """
 import json
-import os
 import time
 
 import numpy as np
@@ -22,7 +21,6 @@ from tests import actpack, parity
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-RESULTS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -36,12 +34,7 @@ def gpu():
 
 def _record(name, stats):
     print(f"[act4] {name}: " + json.dumps(stats), flush=True)
-    try:
-        os.makedirs(RESULTS, exist_ok=True)
-        with open(os.path.join(RESULTS, "parity_stats.jsonl"), "a") as f:
-            f.write(json.dumps(dict(case="act4_" + name, **stats)) + "\n")
-    except OSError:
-        pass
+    parity.record_stats("act4_" + name, stats)
 
 
 def _u16(t):

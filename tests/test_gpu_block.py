@@ -8,7 +8,6 @@ equal to the step-by-step sequence bit for bit.
 """
 import dataclasses
 import json
-import os
 import time
 
 import numpy as np
@@ -21,7 +20,6 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-RESULTS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,12 +33,7 @@ def gpu():
 
 def _record(name, stats):
     print(f"[block] {name}: " + json.dumps(stats), flush=True)
-    try:
-        os.makedirs(RESULTS, exist_ok=True)
-        with open(os.path.join(RESULTS, "parity_stats.jsonl"), "a") as f:
-            f.write(json.dumps(dict(case="block_" + name, **stats)) + "\n")
-    except OSError:
-        pass
+    parity.record_stats("block_" + name, stats)
 
 
 def _u16(t):

@@ -12,7 +12,6 @@ output to equal the step-by-step calls bit for bit.
 """
 import dataclasses
 import json
-import os
 import sys
 import time
 
@@ -26,7 +25,6 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-RESULTS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -40,12 +38,7 @@ def gpu():
 
 def _record(name, stats):
     print(f"[parity] {name}: " + json.dumps(stats), flush=True)
-    try:
-        os.makedirs(RESULTS, exist_ok=True)
-        with open(os.path.join(RESULTS, "parity_stats.jsonl"), "a") as f:
-            f.write(json.dumps(dict(case=name, **stats)) + "\n")
-    except OSError:
-        pass
+    parity.record_stats(name, stats)
 
 
 def _layer(inp):

@@ -10,7 +10,6 @@ whole plain sequence holds every oracle bar of the layer tests (tests/parity.py)
 through its packed form.
 """
 import json
-import os
 import time
 
 import numpy as np
@@ -22,7 +21,6 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-RESULTS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -104,12 +102,7 @@ def _plain_check(name, inp, tokens=None):
     stats = parity.compare(inp, g, o)
     stats["seconds"] = round(time.time() - t0, 1)
     print(f"[plain] {name}: " + json.dumps(stats), flush=True)
-    try:
-        os.makedirs(RESULTS, exist_ok=True)
-        with open(os.path.join(RESULTS, "parity_stats.jsonl"), "a") as f:
-            f.write(json.dumps(dict(case="plain_" + name, **stats)) + "\n")
-    except OSError:
-        pass
+    parity.record_stats("plain_" + name, stats)
 
 
 CASES = {
