@@ -77,6 +77,9 @@ def parse():
     p.add_argument("--pmc-report", nargs=2, metavar=("PMC_DIR", "OUT_TXT"),
                    help="summarise a rocprofv3 --pmc --kernel-trace run (per-kernel counters, clock, MFMA rate)")
     p.add_argument("--command", default="", help="the command that made the profile (for the reports)")
+    p.add_argument("--probe-json", default=None,
+                   help="with --stats-report: the ceiling probes' JSON record of the same run, checked "
+                        "against the trace")
     p.add_argument("--no-block", action="store_true", help="skip the timing of the pre-norm block forward")
     p.add_argument("--no-act4", action="store_true", help="skip the timing of the MXFP4-activation variant")
     return p.parse_args()
@@ -202,9 +205,38 @@ def stats_report(args):
         lines.append(f"{r['Name'][:72]:<72} {int(r['Calls']):>7} {float(r['AverageNs']) / 1e3:>9.2f} "
                      f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
                      f"{float(r['Percentage']):>6.2f}")
+    if args.probe_json:
+        lines += probe_crosscheck(rows, json.load(open(args.probe_json)))
     with open(args.stats_report[1], "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def probe_crosscheck(rows: list, rec: dict) -> list:
+    """The ceiling probes' own rates (HIP events around five back-to-back launches) beside the
+    work per launch divided by the kernel trace's mean duration of the same run's probe kernels."""
+    kern = {"fp6xfp4": "mfma_scaled_probe<2, 4>", "fp4xfp4": "mfma_scaled_probe<4, 4>",
+            "fp8xfp4": "mfma_scaled_probe<0, 4>", "bf16": "mfma_bf16_probe",
+            "read_nt": "stream_read_probe<1>", "read": "stream_read_probe<0>"}
+    work = rec["work_per_launch"]
+    out = ["", "# probe rates: events (the probe's own timing) vs work per launch / trace mean duration",
+           f"{'probe':<10} {'events':>12} {'trace':>12} {'unit':>8}"]
+    for name, k in kern.items():
+        r = next((r for r in rows if k in r["Name"]), None)
+        if r is None:
+            continue
+        secs = float(r["AverageNs"]) * 1e-9
+        if name.startswith("read"):
+            ev = rec["stream_read_nt_GB_per_s" if name == "read_nt" else "stream_read_GB_per_s"]
+            tr = work["stream_read_bytes"] / secs / 1e9
+            unit = "GB/s"
+        else:
+            ev = rec[f"mfma_{name}_TFLOP_per_s"]
+            tr = work[f"mfma_{name}_flop"] / secs / 1e12
+            unit = "TFLOP/s"
+        out.append(f"{name:<10} {ev:>12.1f} {tr:>12.1f} {unit:>8}")
+    out.append("# probe record: " + json.dumps(rec))
+    return out
 
 
 def pmc_summary(d: str) -> list:

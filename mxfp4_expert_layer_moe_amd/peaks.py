@@ -79,3 +79,27 @@ def measure_all() -> dict:
     out["stream_read_nt_GB_per_s"] = round(stream_read_rate(nontemporal=True) / 1e9, 1)
     out["stream_read_GB_per_s"] = round(stream_read_rate(nontemporal=False) / 1e9, 1)
     return out
+
+
+def main(argv: list | None = None) -> int:
+    """`python -m mxfp4_expert_layer_moe_amd.peaks [OUT_JSON]`: every probe once, as one JSON object
+    with the work per launch beside each rate, so a kernel trace of the same run (average launch
+    duration x rate = work per launch) can be checked against it."""
+    import json
+    import sys
+    argv = sys.argv[1:] if argv is None else argv
+    rec = measure_all()
+    rec["work_per_launch"] = {f"mfma_{NAMES[f]}_flop": lib().moe_peak_mfma_flops(f, 2048, 2000)
+                              for f in (FP6_FP4, FP4_FP4, FP8_FP4, BF16)}
+    rec["work_per_launch"]["stream_read_bytes"] = 2048 << 20
+    rec["launches_per_probe"] = 6            # one warm launch, then five timed back to back
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if argv:
+        with open(argv[0], "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

@@ -147,3 +147,16 @@ def test_pmc_summary_means_per_dispatch_and_derives_the_matrix_rate(tmp_path):
     assert abs(r["mean_us"] - 2.0) < 1e-9                                  # (1 + 3) us / 2
     assert abs(r["mfma_f6f4_TFLOP_per_s"] - 2000.0 * 512 / 2e-6 * 1e-12) < 1e-9
     assert r["mfma_busy_cycles_per_simd"] == 3072.0 / 1024
+
+
+def test_probe_crosscheck_divides_the_work_per_launch_by_the_trace_mean():
+    rows = [dict(Name="void (anonymous namespace)::mfma_scaled_probe<2, 4>(int, float*)", AverageNs="2000000"),
+            dict(Name="void (anonymous namespace)::stream_read_probe<1>(unsigned char const*)", AverageNs="500000")]
+    rec = {"mfma_fp6xfp4_TFLOP_per_s": 6000.0, "stream_read_nt_GB_per_s": 4000.0,
+           "work_per_launch": {"mfma_fp6xfp4_flop": 1.0e13, "stream_read_bytes": 2.0e9}}
+    out = bench.probe_crosscheck(rows, rec)
+    fp6 = next(l for l in out if l.startswith("fp6xfp4")).split()
+    assert float(fp6[1]) == 6000.0 and float(fp6[2]) == 5000.0      # 1e13 flop / 2 ms = 5 PF
+    nt = next(l for l in out if l.startswith("read_nt")).split()
+    assert float(nt[1]) == 4000.0 and float(nt[2]) == 4000.0        # 2e9 B / 0.5 ms = 4 TB/s
+    assert not any(l.startswith("bf16") for l in out)               # probes missing from the trace are left out
