@@ -13,9 +13,10 @@
 // The arithmetic (float64 throughout, one bf16 rounding, and the order in which
 // a row's squares are summed) lives in norm_body.h, shared with the routing
 // front end that folds the normalisation into its own launch for small
-// batches, so both give the same bits.  Here: one workgroup of 512 threads per
-// row, one 8-value chunk per thread.  Memory-bound: reads 2D + 4D bytes, writes
-// 2D bytes per row.
+// batches, so both give the same bits.  Memory-bound: reads 2D + 4D bytes,
+// writes 2D bytes per row.  Rows up to 4096 wide: one wavefront per row, four
+// rows per workgroup, every chunk of the row in flight at once and no barrier;
+// wider rows: one workgroup of 512 threads per row.
 #include "norm_body.h"
 
 namespace moe {
@@ -41,10 +42,55 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(int D, const uint
   for (int c = tid + kNormThreads; c < nc; c += kNormThreads) out[c] = chunk_rmsnorm(x4[c], r, gamma, c);
 }
 
+// One wavefront per row (D / 8 <= kNormRowChunks chunks), with row_rms_inv's sum, term for term.
+// There, thread 64 w + l of the 512 sums the chunks 64 w + l, 64 w + l + 512, ... in order; each
+// wavefront w adds its 64 sums by a butterfly; the eight wavefront sums are added in order w = 0..7.
+// Here lane l keeps the eight sums of w = 0..7 side by side (with at most 512 chunks each holds one
+// chunk or none: 0.0 + s = s exactly), runs the same butterfly on each and adds them in the same
+// order, so r_t has the same bits.  The row's chunks stay in registers for the scaling pass.
+constexpr int kNormRowChunks = 512;
+constexpr int kNormRowHold = kNormRowChunks / 64;       // chunks per lane
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int D, const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ gamma, double eps,
+                                                           uint16_t* __restrict__ xn) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;                                  // uniform per wavefront; no barrier follows
+  const int nc = D / 8;
+  const uint4* x4 = reinterpret_cast<const uint4*>(x + (size_t)row * D);
+  uint4 held[kNormRowHold];
+#pragma unroll
+  for (int w = 0; w < kNormRowHold; ++w) {
+    const int c = lane + 64 * w;
+    held[w] = c < nc ? x4[c] : make_uint4(0, 0, 0, 0);
+  }
+  double part[kNormRowHold];
+#pragma unroll
+  for (int w = 0; w < kNormRowHold; ++w) part[w] = lane + 64 * w < nc ? chunk_sum_sq(held[w]) : 0.0;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1)
+#pragma unroll
+    for (int w = 0; w < kNormRowHold; ++w) part[w] += __shfl_xor(part[w], d);
+  double ss = part[0];
+#pragma unroll
+  for (int w = 1; w < kNormRowHold; ++w) ss += part[w];
+  const double r = 1.0 / sqrt(ss / (double)D + eps);
+  uint4* out = reinterpret_cast<uint4*>(xn + (size_t)row * D);
+#pragma unroll
+  for (int w = 0; w < kNormRowHold; ++w) {
+    const int c = lane + 64 * w;
+    if (c < nc) out[c] = chunk_rmsnorm(held[w], r, gamma, c);
+  }
+}
+static_assert(kNormRowChunks == kNormThreads, "the row kernel mirrors row_rms_inv's 512 partial sums");
+
 hipError_t launch_rmsnorm(int T, int D, const uint16_t* x, const float* gamma, float eps, uint16_t* xn,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
-  rmsnorm_kernel<<<dim3((unsigned)T), dim3(kNormThreads), 0, s>>>(D, x, gamma, (double)eps, xn);
+  if (D / 8 <= kNormRowChunks)
+    rmsnorm_rows_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s>>>(T, D, x, gamma, (double)eps, xn);
+  else
+    rmsnorm_kernel<<<dim3((unsigned)T), dim3(kNormThreads), 0, s>>>(D, x, gamma, (double)eps, xn);
   return hipGetLastError();
 }
 

@@ -15,22 +15,21 @@
 
 namespace moe {
 
-// float64 -> bf16 bits, round to nearest, ties to even, directly from the float64 value.
+// float64 -> bf16 bits, round to nearest, ties to even, with no branch.  With 2^e <= |v| < 2^(e+1),
+// the bf16 spacing at v is 2^p, p = max(e, -126) - 7 (below 2^-126 the bf16 subnormals, 2^-133).
+// Adding c = 1.5 * 2^(p+52) puts v + c in a binade whose float64 spacing is 2^p, so (v + c) - c is v
+// rounded to a multiple of 2^p, ties to even (c / 2^p is even, so the tie goes the same way for
+// either sign); the sign is copied back so that a value rounding to zero keeps it.  The result has
+// at most 8 significant bits: its float32 conversion is exact (the launch preserves float32
+// denormals), float32 overflow gives infinity as bf16 does, and the bf16 bits are the float32's
+// upper half.  e is capped at 128: anything at or above 2^128 becomes infinity either way.
+// Contraction is off: v must be the float64 value it is given, not a product fused into v + c.
 __device__ inline uint32_t f64_to_bf16_rne(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
-  const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
-  const int e = (int)(a >> 52) - 1023;                  // exponent before rounding
-  if (e < -126) {
-    // below the normal range: multiples of 2^-133 (bf16 subnormal spacing), rounded with rint
-    const double q = rint(fabs(v) * 0x1p133);          // exact scaling, then nearest even integer
-    return sign | (uint32_t)q;                          // q <= 128; 128 is the smallest normal
-  }
-  // keep 7 stored mantissa bits: the last kept bit is bit 45 of the float64 pattern
-  const uint64_t r = (a + 0x00000FFFFFFFFFFFull + ((a >> 45) & 1u)) & ~0x00001FFFFFFFFFFFull;
-  const int er = (int)(r >> 52) - 1023;                // a carry may raise the exponent
-  if (er > 127) return sign | 0x7F80u;                  // overflow: infinity
-  return sign | ((uint32_t)(er + 127) << 7) | (uint32_t)((r >> 45) & 0x7Fu);
+#pragma clang fp contract(off)
+  const int e = min(max(__builtin_amdgcn_frexp_exp(v) - 1, -126), 128);
+  const double c = __builtin_amdgcn_ldexp(1.5, e + 45);
+  const double r = __builtin_copysign((v + c) - c, v);
+  return __float_as_uint((float)r) >> 16;
 }
 
 // sum of the squares of one 8-value bf16 chunk, in element order
