@@ -118,3 +118,23 @@ def test_block_full_size_workload(cfg, n_tokens):
     tokens = None if n_tokens is None else np.sort(np.random.default_rng(200 + cfg).choice(inp.T, n_tokens,
                                                                                          replace=False))
     _block_check(f"config{cfg}", inp, tokens)
+
+
+@pytest.mark.parametrize("D,T", [(4096, 33), (4160, 5), (8192, 3)])
+def test_rmsnorm_rows_at_and_past_the_one_wavefront_width(D, T):
+    """moe_rmsnorm alone at d_model 4096 (the widest row one wavefront normalises), 4160 (the first
+    width past it, normalised by a 512-thread workgroup per row) and 8192: bit-exact against the
+    oracle."""
+    import mxfp4_expert_layer_moe_amd as M
+    inp = synth.make_inputs(dict(T=T, D=D, E=4, k=2, I=64, seed=70 + D % 97), experts=False)
+    print(f"[block] rmsnorm T={T} D={D}", flush=True)
+    d = M.dims(D, 64, 4, 2)
+    x = torch.from_numpy(inp.x_bf16.view(np.int16)).to("cuda").view(torch.bfloat16)
+    gamma = torch.from_numpy(np.ascontiguousarray(inp.norm_weight, dtype=np.float32)).to("cuda")
+    xn = torch.empty_like(x)
+    M.moe_rmsnorm(d, T, x, gamma, inp.norm_eps, xn)
+    torch.cuda.synchronize()
+    want = oracle.f64_to_bf16_bits(oracle.rms_norm(synth.bf16_bits_to_f32(inp.x_bf16).astype(np.float64),
+                                                   inp.norm_weight, inp.norm_eps))
+    got = _u16(xn)
+    assert int((got != want).sum()) == 0
