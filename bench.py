@@ -99,6 +99,10 @@ GU_KERNEL = {"decode": ("void moe::expert_gemm_kernel<0,", ", 0>(moe::GemmArgs)"
              "prefill": ("void moe::expert_gemm_prefill_kernel<0,", ", 0>(moe::PrefillArgs)")}
 KERNEL_LABEL = {"decode": "expert_gemm_kernel<0> (gate/up + SwiGLU, 8-row tiles)",
                 "prefill": "expert_gemm_prefill_kernel<0> (gate/up + SwiGLU, 128-row tiles)"}
+DN_KERNEL = {"decode": ("void moe::expert_gemm_kernel<1,", ", 0>(moe::GemmArgs)"),
+             "prefill": ("void moe::expert_gemm_prefill_kernel<1,", ", 0>(moe::PrefillArgs)")}
+DN_LABEL = {"decode": "expert_gemm_kernel<1> (down, gate-scaled, 8-row tiles)",
+            "prefill": "expert_gemm_prefill_kernel<1> (down, gate-scaled, 128-row tiles)"}
 
 
 def gemm_kind(cfg: dict) -> str:
@@ -147,7 +151,8 @@ def _per_dispatch(rows, counter: str):
 
 
 def traffic_record(fetch_dir: str, write_dir: str, copy_mib: int, config: int, command: str = "") -> dict:
-    """Gate/up kernel HBM bytes per launch, each counter scaled by what it reads for a plain copy.
+    """Gate/up kernel HBM bytes per launch, each counter scaled by what it reads for a plain copy;
+    the down kernel's from the same runs under "down".
 
     FETCH_SIZE and WRITE_SIZE are in KiB per dispatch (summed over the rows rocprofv3 writes for
     one dispatch).  The last three copyBuffer dispatches of each run are the --copy-mib
@@ -155,7 +160,6 @@ def traffic_record(fetch_dir: str, write_dir: str, copy_mib: int, config: int, c
     """
     cfg = dict(__import__("synth").CONFIGS[config])
     kind = gemm_kind(cfg)
-    prefix, suffix = GU_KERNEL[kind]
     known = copy_mib * 2 ** 20
     if known <= 0:
         raise SystemExit("--traffic-report needs the --copy-mib the runs used")
@@ -163,23 +167,34 @@ def traffic_record(fetch_dir: str, write_dir: str, copy_mib: int, config: int, c
            "kernel": KERNEL_LABEL[kind],
            "kernel_source_sha256_16": gemm_source_hash(kind),
            "command": command}
-    total = 0.0
+    down = {"kernel": DN_LABEL[kind]}
+    total = {"gu": 0.0, "dn": 0.0}
     for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         per = _per_dispatch(_counter_rows(d), counter)
-        gu = [v for n, v in per.values() if n.startswith(prefix) and n.endswith(suffix)]
         cp = [v for n, v in per.values() if n.startswith(COPY_KERNEL)][-3:]
-        if not gu or len(cp) < 3:
-            raise SystemExit(f"{d}: {len(gu)} gate/up dispatches, {len(cp)} calibration copies")
-        kib = sum(gu) / len(gu)
+        sel = {tag: [v for n, v in per.values() if n.startswith(pre) and n.endswith(suf)]
+               for tag, (pre, suf) in (("gu", GU_KERNEL[kind]), ("dn", DN_KERNEL[kind]))}
+        if not sel["gu"] or len(cp) < 3:
+            raise SystemExit(f"{d}: {len(sel['gu'])} gate/up dispatches, {len(cp)} calibration copies")
         factor = known / (sum(cp) / len(cp) * 1024.0)
+        kib = sum(sel["gu"]) / len(sel["gu"])
         rec[f"{key}_kib_per_launch_raw"] = round(kib, 1)
-        rec[f"{key}_gate_up_dispatches"] = len(gu)
+        rec[f"{key}_gate_up_dispatches"] = len(sel["gu"])
         rec[f"{key}_copy_kib_raw"] = [round(v, 1) for v in cp]
         rec[f"{key}_copy_scale"] = round(factor, 5)
         rec[f"{key}_bytes_per_launch"] = int(kib * 1024.0 * factor)
-        total += kib * 1024.0 * factor
+        total["gu"] += kib * 1024.0 * factor
+        if sel["dn"]:
+            kd = sum(sel["dn"]) / len(sel["dn"])
+            down[f"{key}_kib_per_launch_raw"] = round(kd, 1)
+            down[f"{key}_dispatches"] = len(sel["dn"])
+            down[f"{key}_bytes_per_launch"] = int(kd * 1024.0 * factor)
+            total["dn"] += kd * 1024.0 * factor
     rec["copy_bytes_each_way"] = known
-    rec["hbm_bytes_per_launch"] = int(total)
+    rec["hbm_bytes_per_launch"] = int(total["gu"])
+    if "fetch_bytes_per_launch" in down and "write_bytes_per_launch" in down:
+        down["hbm_bytes_per_launch"] = int(total["dn"])
+        rec["down"] = down
     return rec
 
 

@@ -17,6 +17,8 @@ GU_ACT4 = "void moe::expert_gemm_kernel<0, 8, 8, 45, 1, 1, 2, 1>(moe::GemmArgs)"
 DOWN = "void moe::expert_gemm_kernel<1, 8, 8, 45, 2, 1, 1, 0>(moe::GemmArgs)"
 PF_BF16 = "void moe::expert_gemm_prefill_kernel<0, 45, 2, 4, 0>(moe::PrefillArgs)"
 PF_ACT4 = "void moe::expert_gemm_prefill_kernel<0, 45, 2, 4, 1>(moe::PrefillArgs)"
+PF_DOWN = "void moe::expert_gemm_prefill_kernel<1, 45, 2, 4, 0>(moe::PrefillArgs)"
+PF_DOWN_ACT4 = "void moe::expert_gemm_prefill_kernel<1, 45, 2, 4, 1>(moe::PrefillArgs)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -160,3 +162,22 @@ def test_probe_crosscheck_divides_the_work_per_launch_by_the_trace_mean():
     nt = next(l for l in out if l.startswith("read_nt")).split()
     assert float(nt[1]) == 4000.0 and float(nt[2]) == 4000.0        # 2e9 B / 0.5 ms = 4 TB/s
     assert not any(l.startswith("bf16") for l in out)               # probes missing from the trace are left out
+
+
+def test_traffic_record_carries_the_down_kernel_of_the_same_runs(tmp_path):
+    mib = 16
+    kib = mib * 1024
+    _write_counters(tmp_path / "f", "FETCH_SIZE",
+                    [(2, PF_BF16, 500.0), (3, PF_DOWN, 200.0), (4, PF_DOWN_ACT4, 9e9), (5, PF_DOWN, 400.0),
+                     (6, COPY, kib / 2), (7, COPY, kib / 2), (8, COPY, kib / 2)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE",
+                    [(2, PF_BF16, 10.0), (3, PF_DOWN, 50.0), (5, PF_DOWN, 70.0), (6, COPY, kib), (7, COPY, kib),
+                     (8, COPY, kib)])
+    rec = bench.traffic_record(str(tmp_path / "f"), str(tmp_path / "w"), mib, 2, "cmd")
+    dn = rec["down"]
+    assert dn["kernel"].startswith("expert_gemm_prefill_kernel<1>")
+    assert dn["fetch_dispatches"] == 2 and dn["write_dispatches"] == 2       # the act4 down kernel is not it
+    assert dn["fetch_bytes_per_launch"] == 300 * 1024 * 2                    # mean of 200 and 400 KiB, x 2
+    assert dn["write_bytes_per_launch"] == 60 * 1024
+    assert dn["hbm_bytes_per_launch"] == 300 * 1024 * 2 + 60 * 1024
+    assert rec["hbm_bytes_per_launch"] == 500 * 1024 * 2 + 10 * 1024         # the gate/up record is unchanged
