@@ -130,7 +130,9 @@ typedef struct {
 const char* moe_status_str(moe_status s);
 
 /* Bytes of `rows` packed activation rows of length K (0 if K % 64 != 0): the split-MX6
- * encoding above of the bf16 activations that enter the expert projections. */
+ * encoding above of the bf16 activations that enter the expert projections (the scaled
+ * matrix instruction that reads the MXFP4 weights of "gpt-oss architecture walk-through",
+ * section "Quantization", takes MX operands only). */
 size_t moe_act_pack_bytes(int32_t K, int32_t rows);
 
 /* Bytes of the prepacked codes / scales of all experts for one stage: 4 bits per weight plus
@@ -140,8 +142,10 @@ size_t moe_prepacked_codes_bytes(const moe_dims* dims, moe_stage stage);
 size_t moe_prepacked_scales_bytes(const moe_dims* dims, moe_stage stage);
 
 /* Workspace bytes moe_forward needs for T tokens (0 on invalid dims or an unsupported T): the
- * scratch of the whole layer defined at the top of this file (routing results, the grouping,
- * packed x and h, y_perm, the router's float64 partials), 256-byte aligned regions. */
+ * scratch of the whole layer defined at the top of this file ("gpt-oss architecture
+ * walk-through", sections "Mixture of Experts" and "Quantization"; "From GPT-2 to gpt-oss",
+ * section 3): routing results, the grouping, packed x and h, y_perm, the router's float64
+ * partials, in 256-byte aligned regions. */
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t T);
 
 /*
@@ -193,7 +197,9 @@ moe_status moe_permute(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
 
 /*
  * moe_permute that also hands back the row-tile table the expert GEMMs start
- * from (same passages):
+ * from (the grouping of "From GPT-2 to gpt-oss", section 4 "Mixture of Experts":
+ * only the selected experts run for a token, so each expert's GEMM takes the
+ * rows routed to it):
  *   tiles     out, moe_tile_table_bytes(dims, T) bytes, 16-byte aligned: the
  *             row-tile table: 8-row tiles when T*top_k <= 6*n_experts (48
  *             int32 per slot), else 128-row tiles (132 int32 per slot).  A
@@ -254,7 +260,10 @@ moe_status moe_expert_gemm_mxfp4(const moe_dims* dims, int32_t T, moe_stage stag
 
 /*
  * The same GEMM on the packed activations and the row-tile table (see "The
- * step-by-step boundary" above; same passages):
+ * step-by-step boundary" above): the SwiGLU expert of "From GPT-2 to gpt-oss",
+ * section 3 "Swish/SwiGLU" (Figures 6-7), clamped at swiglu_limit (the "GPT-OSS
+ * 20B" model card's raw config), on the MXFP4 weights of "gpt-oss architecture
+ * walk-through", section "Quantization":
  *  MOE_STAGE_GATE_UP:
  *    a_packed  packed x, T rows of d_model (moe_pack_act output); the row of
  *              grouped position p is token perm[p] / top_k
@@ -384,7 +393,10 @@ moe_status moe_forward_act4(const moe_dims* dims, int32_t T, const void* x_bf16,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * The MoE half of a pre-norm transformer block: y = x + MoE(RMSNorm(x)), i.e.
+ * The MoE half of a pre-norm transformer block ("From GPT-2 to gpt-oss", section 7
+ * "RMSNorm replaces LayerNorm", Figures 11-12, for the normalisation; "gpt-oss
+ * architecture walk-through", section "Transformer Blocks", for its place in the
+ * block, [N x 2880] in and out): y = x + MoE(RMSNorm(x)), i.e.
  * moe_rmsnorm -> the moe_forward steps on the normalised rows ->
  * moe_combine_residual with x.  The bits equal those of that sequence of step
  * calls.  ws: at least moe_block_workspace_bytes(dims, T) bytes, 256-byte
